@@ -1,0 +1,187 @@
+"""ctypes wrapper over ``maxsim_oracle.c`` (test infrastructure only).
+
+Arrays cross as numpy arrays; fp16 / bf16 tensors cross as their raw uint16
+bit patterns so the C side decodes them exactly.  Every function mirrors one
+C entry point; the passages of the paper each follows are cited in the C file.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+F16 = 0
+BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "maxsim_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# Tests that plant mistakes in a copy of the oracle point this at the mutant.
+_LIB_OVERRIDE = os.environ.get("MAXSIM_ORACLE_LIB")
+_lib = None
+
+
+def lib_path():
+    return _LIB
+
+
+def build(force=True):
+    """Compile the oracle with gcc: -O2, OpenMP, no FMA contraction, no fast-math."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB):
+                build()
+            lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_f64.restype = ctypes.c_double
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.oracle_fwd_padded.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P]
+        lib.oracle_fwd_varlen.argtypes = [P, P, P, I, I, I, I, I, P, P, P]
+        lib.oracle_fwd_i8.argtypes = [P, P, P, P, P, I, I, I, I, P, P]
+        lib.oracle_sim_at.argtypes = [P, P, P, I, I, I, I, I, P, P]
+        lib.oracle_csr_build.argtypes = [P, I, I, I, I, P, P]
+        lib.oracle_bwd.argtypes = [P, P, I, P, P, I, I, I, I, I, P, P]
+        for name in ("oracle_fwd_padded", "oracle_fwd_varlen", "oracle_fwd_i8", "oracle_sim_at",
+                     "oracle_csr_build", "oracle_bwd", "oracle_num_threads"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _bits16(a):
+    """fp16 arrays -> their uint16 bits; uint16 arrays (bf16 bits) pass through."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError("expected float16 or uint16 (bf16 bits), got %s" % a.dtype)
+    return a
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError("oracle %s rejected its arguments (rc=%d)" % (what, rc))
+
+
+def f16_to_f64(bits):
+    lib = _load()
+    return np.array([lib.oracle_f16_to_f64(int(b)) for b in np.asarray(bits).ravel()])
+
+
+def bf16_to_f64(bits):
+    lib = _load()
+    return np.array([lib.oracle_bf16_to_f64(int(b)) for b in np.asarray(bits).ravel()])
+
+
+def fwd_padded(Q, D, dtype, d_lens=None, want_rowmax=False):
+    """Q [Nq, Lq, d], D [B, Ld, d] -> (scores fp64 [Nq, B], argmax int32 [Nq, B, Lq][, rowmax])."""
+    Qb, Db = _bits16(Q), _bits16(D)
+    Nq, Lq, d = Qb.shape
+    B, Ld, d2 = Db.shape
+    assert d == d2
+    lens = None if d_lens is None else np.ascontiguousarray(d_lens, dtype=np.int32)
+    scores = np.empty((Nq, B), np.float64)
+    amax = np.empty((Nq, B, Lq), np.int32)
+    rowmax = np.empty((Nq, B, Lq), np.float64) if want_rowmax else None
+    rc = _load().oracle_fwd_padded(_p(Qb), _p(Db), _p(lens), dtype, Nq, Lq, B, Ld, d,
+                                   _p(scores), _p(amax), _p(rowmax))
+    _check(rc, "fwd_padded")
+    return (scores, amax, rowmax) if want_rowmax else (scores, amax)
+
+
+def fwd_varlen(Q, D_packed, cu_seqlens, dtype, want_rowmax=False):
+    """Q [Nq, Lq, d], D_packed [T, d], cu_seqlens [B+1] -> (scores, argmax[, rowmax])."""
+    Qb, Db = _bits16(Q), _bits16(D_packed)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    Nq, Lq, d = Qb.shape
+    B = cu.shape[0] - 1
+    assert Db.shape[1] == d and Db.shape[0] >= cu[-1]
+    scores = np.empty((Nq, B), np.float64)
+    amax = np.empty((Nq, B, Lq), np.int32)
+    rowmax = np.empty((Nq, B, Lq), np.float64) if want_rowmax else None
+    rc = _load().oracle_fwd_varlen(_p(Qb), _p(Db), _p(cu), dtype, Nq, Lq, B, d,
+                                   _p(scores), _p(amax), _p(rowmax))
+    _check(rc, "fwd_varlen")
+    return (scores, amax, rowmax) if want_rowmax else (scores, amax)
+
+
+def fwd_i8(Q, q_scale, D_packed, d_scale, cu_seqlens):
+    """INT8 x INT8 forward -> (scores fp32 [Nq, B], argmax int32 [Nq, B, Lq])."""
+    Q = np.ascontiguousarray(Q, dtype=np.int8)
+    D_packed = np.ascontiguousarray(D_packed, dtype=np.int8)
+    qs = np.ascontiguousarray(q_scale, dtype=np.float32)
+    ds = np.ascontiguousarray(d_scale, dtype=np.float32)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    Nq, Lq, d = Q.shape
+    B = cu.shape[0] - 1
+    assert qs.shape == (Nq, Lq) and ds.shape[0] >= cu[-1] and D_packed.shape[1] == d
+    scores = np.empty((Nq, B), np.float32)
+    amax = np.empty((Nq, B, Lq), np.int32)
+    rc = _load().oracle_fwd_i8(_p(Q), _p(qs), _p(D_packed), _p(ds), _p(cu), Nq, Lq, B, d,
+                               _p(scores), _p(amax))
+    _check(rc, "fwd_i8")
+    return scores, amax
+
+
+def sim_at(Q, D_packed, cu_seqlens, dtype, sel):
+    """fp64 <Q[q,i], D[b, sel[q,b,i]]> for every (q, b, i); -inf where sel is out of range."""
+    Qb, Db = _bits16(Q), _bits16(D_packed)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    Nq, Lq, d = Qb.shape
+    B = cu.shape[0] - 1
+    assert sel.shape == (Nq, B, Lq)
+    out = np.empty((Nq, B, Lq), np.float64)
+    _check(_load().oracle_sim_at(_p(Qb), _p(Db), _p(cu), dtype, Nq, Lq, B, d, _p(sel), _p(out)),
+           "sim_at")
+    return out
+
+
+def csr_build(argmax, Ld):
+    """argmax [Nq, B, Lq] -> (row_ptr int32 [B*Ld+1], col_idx int32 [Nq*B*Lq])."""
+    A = np.ascontiguousarray(argmax, dtype=np.int32)
+    Nq, B, Lq = A.shape
+    row_ptr = np.empty(B * Ld + 1, np.int32)
+    col_idx = np.empty(Nq * B * Lq, np.int32)
+    _check(_load().oracle_csr_build(_p(A), Nq, B, Lq, Ld, _p(row_ptr), _p(col_idx)), "csr_build")
+    return row_ptr, col_idx
+
+
+def bwd(Q, D, dtype, argmax, g):
+    """Closed-form gradients -> (dQ fp64 [Nq, Lq, d], dD fp64 [B, Ld, d])."""
+    Qb, Db = _bits16(Q), _bits16(D)
+    A = np.ascontiguousarray(argmax, dtype=np.int32)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    Nq, Lq, d = Qb.shape
+    B, Ld, _ = Db.shape
+    assert A.shape == (Nq, B, Lq) and g.shape == (Nq, B)
+    dQ = np.empty((Nq, Lq, d), np.float64)
+    dD = np.empty((B, Ld, d), np.float64)
+    _check(_load().oracle_bwd(_p(Qb), _p(Db), dtype, _p(A), _p(g), Nq, Lq, B, Ld, d, _p(dQ), _p(dD)),
+           "bwd")
+    return dQ, dD
+
+
+def num_threads():
+    return int(_load().oracle_num_threads())

@@ -1,0 +1,163 @@
+"""Pins for the oracle's backward and inverse-grid CSR map (CPU only).
+
+CSR: exact against numpy's bincount / cumsum / stable argsort plus its
+structural invariants.  Gradients: the hand-worked case, a dense one-hot
+formulation with numpy matmul, exact finite differences on a dyadic grid
+(the score is piecewise linear), Euler's relation for degree-1 homogeneous
+functions, and a mass identity.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from late_interaction_retrieval_amd import inputs
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "maxsim_hand.json")
+
+
+def decoded(a):
+    if a.dtype == np.float16:
+        return a.astype(np.float64)
+    return inputs.bf16_bits_to_f32(a).astype(np.float64)
+
+
+def numpy_csr(A, Ld):
+    Nq, B, Lq = A.shape
+    b_of_s = np.broadcast_to(np.arange(B)[None, :, None], A.shape)
+    dst = (b_of_s * Ld + A).ravel()
+    cnt = np.bincount(dst, minlength=B * Ld)
+    row_ptr = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+    col_idx = np.argsort(dst, kind="stable").astype(np.int32)
+    return row_ptr, col_idx, dst
+
+
+def test_golden_hand_case():
+    g = json.load(open(GOLD))
+    f, bw = g["fwd_padded"], g["bwd"]
+    Q = np.array(f["Q"], np.float16)
+    D = np.array(f["D"], np.float16)
+    A = np.array(f["argmax"], np.int32)
+    gg = np.array(bw["g"], np.float32)
+    dQ, dD = oracle.bwd(Q, D, oracle.F16, A, gg)
+    assert np.array_equal(dQ, np.array(bw["dQ"]))
+    assert np.array_equal(dD, np.array(bw["dD"]))
+    rp, ci = oracle.csr_build(A, 3)
+    assert np.array_equal(rp, np.array(bw["row_ptr"]))
+    assert np.array_equal(ci, np.array(bw["col_idx"]))
+
+
+@pytest.mark.parametrize("shape,Ld,hot", [((3, 4, 5), 6, False), ((8, 16, 64), 64, False),
+                                          ((8, 16, 64), 64, True), ((1, 1, 1), 1, False)])
+def test_csr_matches_numpy(shape, Ld, hot):
+    rng = np.random.default_rng(sum(shape) + Ld)
+    A = rng.integers(0, Ld, size=shape).astype(np.int32)
+    if hot:  # a few hot tokens take most of the selections
+        A = np.where(rng.random(shape) < 0.7, rng.integers(0, 3, size=shape), A).astype(np.int32)
+    rp, ci = oracle.csr_build(A, Ld)
+    rp_np, ci_np, dst = numpy_csr(A, Ld)
+    assert np.array_equal(rp, rp_np)
+    assert np.array_equal(ci, ci_np)
+    # invariants: non-decreasing, total, every source once, source lands in its row
+    Nq, B, Lq = shape
+    assert rp[0] == 0 and rp[-1] == A.size and np.all(np.diff(rp) >= 0)
+    assert np.array_equal(np.sort(ci), np.arange(A.size))
+    row_of_k = np.repeat(np.arange(B * Ld), np.diff(rp))
+    assert np.array_equal(dst[ci], row_of_k)
+    # each document segment holds exactly Nq * Lq sources, offset known in closed form
+    assert np.array_equal(rp[np.arange(B) * Ld], np.arange(B) * Nq * Lq)
+    # stable: ascending source id within every row
+    for r in range(B * Ld):
+        seg = ci[rp[r]:rp[r + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+def test_csr_rejects_out_of_range():
+    A = np.zeros((1, 2, 3), np.int32)
+    A[0, 1, 2] = 5
+    with pytest.raises(ValueError):
+        oracle.csr_build(A, 5)
+
+
+def _random_case(seed, dtn, Nq=3, Lq=6, B=4, Ld=7, d=16):
+    Q = inputs.random_rows(seed, Nq * Lq, d, dtn).reshape(Nq, Lq, d)
+    D = inputs.random_rows(seed + 1, B * Ld, d, dtn).reshape(B, Ld, d)
+    g = np.random.default_rng(seed).standard_normal((Nq, B)).astype(np.float32)
+    return Q, D, g
+
+
+@pytest.mark.parametrize("dtn,dt", [(inputs.F16, oracle.F16), (inputs.BF16, oracle.BF16)])
+def test_one_hot_dense_formulation(dtn, dt):
+    Q, D, g = _random_case(41, dtn)
+    _, A = oracle.fwd_padded(Q, D, dt)
+    dQ, dD = oracle.bwd(Q, D, dt, A, g)
+    Qd, Dd = decoded(Q), decoded(D)
+    Nq, B, Lq = A.shape
+    Ld = D.shape[1]
+    dQ_ref = np.zeros_like(dQ)
+    dD_ref = np.zeros_like(dD)
+    for q in range(Nq):
+        for b in range(B):
+            P = np.zeros((Lq, Ld))
+            P[np.arange(Lq), A[q, b]] = 1.0
+            dQ_ref[q] += g[q, b] * (P @ Dd[b])
+            dD_ref[b] += g[q, b] * (P.T @ Qd[q])
+    np.testing.assert_allclose(dQ, dQ_ref, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dD, dD_ref, rtol=1e-13, atol=1e-14)
+    # rows no query token selected are exactly zero
+    chosen = np.zeros((B, Ld), bool)
+    for b in range(B):
+        chosen[b, np.unique(A[:, b, :])] = True
+    assert np.all(dD[~chosen] == 0.0)
+
+
+def _loss(Q, D, g, dt):
+    s, a = oracle.fwd_padded(Q, D, dt)
+    return float((g.astype(np.float64) * s).sum()), a
+
+
+def test_finite_differences_exact_on_dyadic_grid():
+    """L = sum g * score is piecewise linear; away from argmax changes a finite
+    difference on a dyadic grid equals the oracle gradient exactly."""
+    rng = np.random.default_rng(42)
+    Nq, Lq, B, Ld, d = 2, 3, 3, 5, 8
+    Qf = rng.integers(-32, 33, size=(Nq, Lq, d)) / 32.0
+    Df = rng.integers(-32, 33, size=(B, Ld, d)) / 32.0
+    g = (rng.integers(-8, 9, size=(Nq, B)) / 8.0).astype(np.float32)
+    Q, D = Qf.astype(np.float16), Df.astype(np.float16)
+    L0, A0 = _loss(Q, D, g, oracle.F16)
+    dQ, dD = oracle.bwd(Q, D, oracle.F16, A0, g)
+    h = 1.0 / 32.0
+    checked = 0
+    for idx in [(0, 0, 0), (0, 2, 5), (1, 1, 7), (1, 0, 3)]:
+        Q2 = Qf.copy()
+        Q2[idx] += h
+        L1, A1 = _loss(Q2.astype(np.float16), D, g, oracle.F16)
+        if np.array_equal(A1, A0):
+            assert (L1 - L0) / h == dQ[idx]
+            checked += 1
+    for idx in [(0, 0, 0), (1, 4, 2), (2, 3, 6), (2, 1, 1)]:
+        D2 = Df.copy()
+        D2[idx] += h
+        L1, A1 = _loss(Q, D2.astype(np.float16), g, oracle.F16)
+        if np.array_equal(A1, A0):
+            assert (L1 - L0) / h == dD[idx]
+            checked += 1
+    assert checked >= 5
+
+
+@pytest.mark.parametrize("dtn,dt", [(inputs.F16, oracle.F16), (inputs.BF16, oracle.BF16)])
+def test_euler_homogeneity_and_mass(dtn, dt):
+    """score is degree-1 homogeneous in Q and in D, so <dQ, Q> = sum g*score = <dD, D>;
+    and sum_t dD[b, t] = sum_q g[q, b] sum_i Q[q, i]."""
+    Q, D, g = _random_case(43, dtn, Nq=4, Lq=9, B=5, Ld=11, d=32)
+    s, A = oracle.fwd_padded(Q, D, dt)
+    dQ, dD = oracle.bwd(Q, D, dt, A, g)
+    Qd, Dd = decoded(Q), decoded(D)
+    gs = float((g.astype(np.float64) * s).sum())
+    assert float((dQ * Qd).sum()) == pytest.approx(gs, rel=1e-12, abs=1e-12)
+    assert float((dD * Dd).sum()) == pytest.approx(gs, rel=1e-12, abs=1e-12)
+    mass = np.einsum("qb,qk->bk", g.astype(np.float64), Qd.sum(axis=1))
+    np.testing.assert_allclose(dD.sum(axis=1), mass, rtol=1e-12, atol=1e-12)

@@ -1,0 +1,50 @@
+"""The oracle's pins are strong enough to catch plausible mistakes.
+
+Each case plants one mistake in a copy of ``oracle/maxsim_oracle.c`` (a
+dropped term, a wrong sign, index or operand, a wrong tie rule), compiles the
+copy with gcc, and runs the pin tests against it: at least one must fail.
+Everything happens on the CPU; the real oracle is untouched.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "maxsim_oracle.c")
+PINS = ["tests/test_oracle_fwd.py", "tests/test_oracle_i8.py", "tests/test_oracle_bwd.py"]
+
+MUTANTS = {
+    "tie_takes_last_index": ("            if (s > m) {\n                m = s;\n                arg = j;",
+                             "            if (s >= m) {\n                m = s;\n                arg = j;"),
+    "sum_sign": ("        score += m;", "        score -= m;"),
+    "mask_dropped": ("        len[b] = d_lens ? d_lens[b] : Ld;", "        len[b] = Ld;"),
+    "f16_exponent_bias": ("ldexp((double)(1024 + frac), expo - 25)", "ldexp((double)(1024 + frac), expo - 24)"),
+    "bf16_fraction_width": ("ldexp((double)(128 + frac), expo - 134)", "ldexp((double)(128 + frac), expo - 133)"),
+    "i8_tie_takes_last": ("                    if (s > m) {", "                    if (s >= m) {"),
+    "i8_query_scale_dropped": ("float v = m * q_scale[(int64_t)q * Lq + i];", "float v = m;"),
+    "i8_doc_scale_of_wrong_token": ("float s = (float)dot * d_scale[first + j];",
+                                    "float s = (float)dot * d_scale[first];"),
+    "csr_cursor_not_advanced": ("        cursor[dst] += 1;\n", "\n"),
+    "csr_wrong_doc_stride": ("        cnt[b * Ld + t] += 1;", "        cnt[t * B + b] += 1;"),
+    "dD_wrong_operand": ("ddr[k] += gqb * decode(qrow[k], dtype);", "ddr[k] += gqb * decode(drow[k], dtype);"),
+    "dQ_transposed_upstream": ("double gqb = (double)g[(int64_t)q * B + b];",
+                               "double gqb = (double)g[(int64_t)b * Nq + q];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site for %s not unique" % name
+    mut_c = tmp_path / "mutant.c"
+    mut_c.write_text(src.replace(old, new))
+    mut_so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+                    str(mut_c), "-o", str(mut_so), "-lm"], check=True)
+    env = dict(os.environ, MAXSIM_ORACLE_LIB=str(mut_so), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] + PINS,
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1, "mutant %s survived the pins:\n%s" % (name, r.stdout[-2000:])
