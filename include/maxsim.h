@@ -1,0 +1,146 @@
+/*
+ * maxsim.h -- C ABI of the MI355X (gfx950) fused late-interaction MaxSim
+ * library, libmaxsim.so.
+ *
+ * The operation is MaxSim from "Flash-MaxSim: IO-Aware Fused Kernels for
+ * Late-Interaction Scoring" (arXiv 2605.29517), Section 1, Eq. (1):
+ *
+ *     score(Q, D) = sum_i max_j <Q_i, D_j>
+ *
+ * computed for every (query, document) pair of Nq queries and B documents
+ * (the all-pairs regime of Section 3.1) without materialising the
+ * [Nq, B, Lq, Ld] similarity tensor, plus the training backward of
+ * Section 4.2 and the INT8 and padding-free variants of Section 4.3.
+ *
+ * Conventions shared by every entry point:
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or synchronises; each call only enqueues work on
+ *     `stream` (a hipStream_t passed as void*, NULL = the null stream) and
+ *     returns.  Outputs are fully overwritten.
+ *   - Tensors are dense, row-major, contiguous.  The embedding width d must be
+ *     128 (MAXSIM_ERR_UNSUPPORTED otherwise).  Q, D and D_packed must be
+ *     16-byte aligned, every other buffer 4-byte aligned (MAXSIM_ERR_ALIGN).
+ *   - Arguments are validated on the host before any HIP call, so every
+ *     MAXSIM_ERR_* other than MAXSIM_ERR_HIP is returned without touching the
+ *     device.  MAXSIM_ERR_HIP reports a failed launch (hipGetLastError).
+ *   - Device-side data are not validated; instead every kernel clamps what it
+ *     reads so that no access leaves the buffers described by the sizes:
+ *     a document length outside [0, Ld] (padded) is clamped to that range, a
+ *     cu_seqlens range outside [0, T) is clamped to it, and an argmax entry
+ *     outside [0, Ld) given to the backward is clamped into [0, Ld) (the
+ *     gradients are then unspecified, but no access leaves the buffers).
+ *   - Query-token count Lq is limited to 1 <= Lq <= 1024.
+ *   - A document with no valid token scores -inf and every argmax entry of
+ *     it is -1 (the running maximum starts at -inf, Section 4.1).
+ *   - Argmax indices are local to the document ([0, length)) and, where
+ *     several tokens attain the maximum, point at one of them (the INT8 path
+ *     always at the first).
+ */
+#ifndef MAXSIM_H
+#define MAXSIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MAXSIM_OK = 0,
+    MAXSIM_ERR_NULL = 1,        /* a required pointer is NULL */
+    MAXSIM_ERR_SHAPE = 2,       /* a size is negative / zero where not allowed, or overflows */
+    MAXSIM_ERR_UNSUPPORTED = 3, /* d != 128, Lq > 1024, unknown dtype, shape beyond a kernel limit */
+    MAXSIM_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
+    MAXSIM_ERR_WORKSPACE = 5,   /* workspace smaller than maxsim_bwd_workspace_bytes() */
+    MAXSIM_ERR_HIP = 6          /* the HIP runtime rejected a launch */
+} maxsim_status;
+
+typedef enum { MAXSIM_F16 = 0, MAXSIM_BF16 = 1 } maxsim_dtype;
+
+/*
+ * Fused forward, padded documents (Section 4.1, Algorithm 2; masking of
+ * invalid positions to -inf before the row maximum, "Online-Max Recurrence").
+ *   Q       [Nq, Lq, d]  fp16 or bf16 (dtype)
+ *   D       [B, Ld, d]   same dtype; document b is D[b, :d_lens[b], :]
+ *   d_lens  [B] int32 valid lengths, or NULL for "all Ld tokens valid"
+ *   scores  [Nq, B] fp32 out: score of query q against document b
+ *   argmax  [Nq, B, Lq] int32 out, or NULL to skip it: for each query token
+ *           the document token attaining its maximum (Section 4.2, the
+ *           saved argmax of "Runtime Inverse-Grid Construction")
+ * Arithmetic: products of fp16/bf16 inputs accumulated in fp32 (MFMA), fp32
+ * running maximum, fp32 sum over query tokens (Section 4.1 "Numerical
+ * Fidelity").  Requires Nq >= 0, B >= 0, 1 <= Lq <= 1024, Ld >= 1.
+ */
+int maxsim_fwd(const void* Q, const void* D, const int32_t* d_lens, int32_t Nq, int32_t Lq,
+               int32_t B, int32_t Ld, int32_t d, int32_t dtype, float* scores, int32_t* argmax,
+               void* stream);
+
+/*
+ * Fused forward, padding-free documents (Section 4.3 "Padding-Free
+ * Variable-Length"): only the real tokens are read and scored.
+ *   D_packed    [T, d] the documents' tokens back to back
+ *   cu_seqlens  [B+1] int32, cu_seqlens[0] = 0, non-decreasing; document b is
+ *               rows [cu_seqlens[b], cu_seqlens[b+1]) of D_packed
+ *   max_Ld      an upper bound of the document lengths (>= 1)
+ * Other arguments and outputs as maxsim_fwd; argmax is local to the document.
+ */
+int maxsim_fwd_varlen(const void* Q, const void* D_packed, const int32_t* cu_seqlens, int32_t Nq,
+                      int32_t Lq, int32_t B, int64_t T, int32_t max_Ld, int32_t d, int32_t dtype,
+                      float* scores, int32_t* argmax, void* stream);
+
+/*
+ * INT8 x INT8 forward over padding-free documents (Section 4.3 "INT8xINT8
+ * Quantization": per-token symmetric scales, dequantisation fused into the
+ * kernel).  The page leaves the arithmetic open; this library computes,
+ * exactly and bit-reproducibly:
+ *     dot_ij = sum_k Q[q,i,k] * D[j,k]                 (int32, exact)
+ *     s_ij   = fl32((float)dot_ij * d_scale[j])
+ *     m_i    = max_j s_ij           argmax_i = first j attaining m_i
+ *     v_i    = fl32(m_i * q_scale[q,i])
+ *     score  = fp32 sum of v_i in ascending i, no fused multiply-add
+ *   Q [Nq, Lq, d] int8, q_scale [Nq, Lq] fp32 (> 0)
+ *   D_packed [T, d] int8, d_scale [T] fp32 (> 0), cu_seqlens as above.
+ */
+int maxsim_fwd_i8(const int8_t* Q, const float* q_scale, const int8_t* D_packed,
+                  const float* d_scale, const int32_t* cu_seqlens, int32_t Nq, int32_t Lq,
+                  int32_t B, int64_t T, int32_t max_Ld, int32_t d, float* scores, int32_t* argmax,
+                  void* stream);
+
+/* Bytes of device workspace maxsim_bwd needs for these sizes (0 on bad sizes). */
+size_t maxsim_bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld);
+
+/*
+ * Backward, padded documents (Section 4.2, Algorithm 3).
+ *   Q [Nq, Lq, d], D [B, Ld, d] (dtype), argmax [Nq, B, Lq] int32 from the
+ *   forward, grad_scores [Nq, B] fp32 = dL/dscore.
+ * Step 1, inverse-grid CSR ("Runtime Inverse-Grid Construction"): with the
+ *   source id s = (q*B + b)*Lq + i and destination dst(s) = b*Ld + argmax[s],
+ *     row_ptr [B*Ld + 1] out: exclusive prefix sum of the per-row counts,
+ *     col_idx [Nq*B*Lq]  out: the sources of row r in ascending s at
+ *                             col_idx[row_ptr[r] .. row_ptr[r+1]).
+ *   Both are deterministic (bit-identical on every call).
+ * Step 2, destination-owned dD ("Destination-Owned Reduction", Eq. (dd)):
+ *     dD [B, Ld, d] fp32 out, dD[b,t] = sum over the sources s of row b*Ld+t
+ *     of grad_scores[q(s), b] * Q[q(s), i(s)]; rows with no source are 0.
+ *     Each row is written once by its owner, no atomics.
+ * Step 3, gathered dQ (Eq. (dq)):
+ *     dQ [Nq, Lq, d] fp32 out, dQ[q,i] = sum_b grad_scores[q,b] * D[b, argmax[q,b,i]].
+ * workspace: device scratch of at least maxsim_bwd_workspace_bytes() bytes,
+ * 16-byte aligned; its contents on entry do not matter.
+ * Requires Nq, B >= 1, 1 <= Lq <= 1024, 1 <= Ld <= 4096, Nq*B*Lq < 2^31,
+ * B*Ld < 2^31.
+ */
+int maxsim_bwd(const void* Q, const void* D, int32_t dtype, const int32_t* argmax,
+               const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B, int32_t Ld, int32_t d,
+               float* dQ, float* dD, int32_t* row_ptr, int32_t* col_idx, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* maxsim_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAXSIM_H */

@@ -1,0 +1,235 @@
+"""Thin ctypes binding over libmaxsim.so, with the C entry points' names.
+
+Only argument marshalling happens here: tensors become device pointers, the
+current torch stream becomes the hipStream_t, and a non-zero status becomes a
+``MaxSimError``.  Every step of the computation runs in the HIP kernels; there
+is no CPU fallback: if the library was not built, importing this module raises.
+PyTorch is used for device memory (outputs the caller does not pass are
+allocated with torch) and streams.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmaxsim.so")
+
+MAXSIM_OK = 0
+MAXSIM_ERR_NULL = 1
+MAXSIM_ERR_SHAPE = 2
+MAXSIM_ERR_UNSUPPORTED = 3
+MAXSIM_ERR_ALIGN = 4
+MAXSIM_ERR_WORKSPACE = 5
+MAXSIM_ERR_HIP = 6
+MAXSIM_F16 = 0
+MAXSIM_BF16 = 1
+
+# name -> (restype, argtypes); must match include/maxsim.h
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+SIGNATURES = {
+    "maxsim_fwd": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "maxsim_fwd_varlen": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P, _P]),
+    "maxsim_fwd_i8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _P, _P, _P]),
+    "maxsim_bwd_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
+    "maxsim_bwd": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
+                                  ctypes.c_size_t, _P]),
+    "maxsim_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+class MaxSimError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = lib().maxsim_status_string(status).decode()
+        super().__init__("%s: %s (status %d)" % (where, msg, status))
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmaxsim.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmaxsim.so is not built; run `python -m late_interaction_retrieval_amd.build` "
+                              "(or __graft_entry__.build())")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+lib()  # fail loudly at import time if the native library is missing
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status, where):
+    if status != MAXSIM_OK:
+        raise MaxSimError(status, where)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float16:
+        return MAXSIM_F16
+    if t.dtype == torch.bfloat16:
+        return MAXSIM_BF16
+    raise TypeError("Q and D must be float16 or bfloat16, got %s" % t.dtype)
+
+
+def _need(t, name, dtype=None, device=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def maxsim_fwd(Q, D, d_lens=None, scores=None, argmax=None, with_argmax=True, stream=None):
+    """Padded forward.  Q [Nq, Lq, 128], D [B, Ld, 128] (fp16/bf16), d_lens [B] int32 or None.
+
+    Returns (scores [Nq, B] fp32, argmax [Nq, B, Lq] int32 or None).
+    """
+    Nq, Lq, d = Q.shape
+    B, Ld, d2 = D.shape
+    if d2 != d or Q.dtype != D.dtype:
+        raise ValueError("Q and D must share dtype and width")
+    _need(Q, "Q")
+    _need(D, "D", device=Q.device)
+    if d_lens is not None:
+        _need(d_lens, "d_lens", torch.int32, Q.device)
+    if scores is None:
+        scores = torch.empty((Nq, B), dtype=torch.float32, device=Q.device)
+    _need(scores, "scores", torch.float32, Q.device)
+    if argmax is None and with_argmax:
+        argmax = torch.empty((Nq, B, Lq), dtype=torch.int32, device=Q.device)
+    if argmax is not None:
+        _need(argmax, "argmax", torch.int32, Q.device)
+    st = lib().maxsim_fwd(_ptr(Q), _ptr(D), _ptr(d_lens), Nq, Lq, B, Ld, d, _dtype_code(Q),
+                          _ptr(scores), _ptr(argmax), _stream(Q, stream))
+    _check(st, "maxsim_fwd")
+    return scores, argmax
+
+
+def maxsim_fwd_varlen(Q, D_packed, cu_seqlens, max_Ld, scores=None, argmax=None, with_argmax=True,
+                      stream=None):
+    """Padding-free forward.  D_packed [T, 128], cu_seqlens [B+1] int32 on the device."""
+    Nq, Lq, d = Q.shape
+    T, d2 = D_packed.shape
+    B = cu_seqlens.shape[0] - 1
+    if d2 != d or Q.dtype != D_packed.dtype:
+        raise ValueError("Q and D_packed must share dtype and width")
+    _need(Q, "Q")
+    _need(D_packed, "D_packed", device=Q.device)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, Q.device)
+    if scores is None:
+        scores = torch.empty((Nq, B), dtype=torch.float32, device=Q.device)
+    _need(scores, "scores", torch.float32, Q.device)
+    if argmax is None and with_argmax:
+        argmax = torch.empty((Nq, B, Lq), dtype=torch.int32, device=Q.device)
+    if argmax is not None:
+        _need(argmax, "argmax", torch.int32, Q.device)
+    st = lib().maxsim_fwd_varlen(_ptr(Q), _ptr(D_packed), _ptr(cu_seqlens), Nq, Lq, B, T, int(max_Ld), d,
+                                 _dtype_code(Q), _ptr(scores), _ptr(argmax), _stream(Q, stream))
+    _check(st, "maxsim_fwd_varlen")
+    return scores, argmax
+
+
+def maxsim_fwd_i8(Q, q_scale, D_packed, d_scale, cu_seqlens, max_Ld, scores=None, argmax=None,
+                  with_argmax=True, stream=None):
+    """INT8 x INT8 padding-free forward (int8 rows, fp32 per-token scales)."""
+    Nq, Lq, d = Q.shape
+    T, d2 = D_packed.shape
+    B = cu_seqlens.shape[0] - 1
+    if d2 != d:
+        raise ValueError("Q and D_packed must share the width")
+    _need(Q, "Q", torch.int8)
+    _need(D_packed, "D_packed", torch.int8, Q.device)
+    _need(q_scale, "q_scale", torch.float32, Q.device)
+    _need(d_scale, "d_scale", torch.float32, Q.device)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, Q.device)
+    if scores is None:
+        scores = torch.empty((Nq, B), dtype=torch.float32, device=Q.device)
+    _need(scores, "scores", torch.float32, Q.device)
+    if argmax is None and with_argmax:
+        argmax = torch.empty((Nq, B, Lq), dtype=torch.int32, device=Q.device)
+    if argmax is not None:
+        _need(argmax, "argmax", torch.int32, Q.device)
+    st = lib().maxsim_fwd_i8(_ptr(Q), _ptr(q_scale), _ptr(D_packed), _ptr(d_scale), _ptr(cu_seqlens), Nq, Lq,
+                             B, T, int(max_Ld), d, _ptr(scores), _ptr(argmax), _stream(Q, stream))
+    _check(st, "maxsim_fwd_i8")
+    return scores, argmax
+
+
+def maxsim_bwd_workspace_bytes(Nq, B, Lq, Ld):
+    return int(lib().maxsim_bwd_workspace_bytes(Nq, B, Lq, Ld))
+
+
+def maxsim_bwd(Q, D, argmax, grad_scores, dQ=None, dD=None, row_ptr=None, col_idx=None, workspace=None,
+               stream=None):
+    """Backward over padded documents.  Returns (dQ, dD, row_ptr, col_idx)."""
+    Nq, Lq, d = Q.shape
+    B, Ld, _ = D.shape
+    dev = Q.device
+    _need(Q, "Q")
+    _need(D, "D", device=dev)
+    _need(argmax, "argmax", torch.int32, dev)
+    _need(grad_scores, "grad_scores", torch.float32, dev)
+    if dQ is None:
+        dQ = torch.empty((Nq, Lq, d), dtype=torch.float32, device=dev)
+    if dD is None:
+        dD = torch.empty((B, Ld, d), dtype=torch.float32, device=dev)
+    if row_ptr is None:
+        row_ptr = torch.empty(B * Ld + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(Nq * B * Lq, dtype=torch.int32, device=dev)
+    nbytes = maxsim_bwd_workspace_bytes(Nq, B, Lq, Ld)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    for t, n in ((dQ, "dQ"), (dD, "dD"), (row_ptr, "row_ptr"), (col_idx, "col_idx"), (workspace, "workspace")):
+        _need(t, n, device=dev)
+    st = lib().maxsim_bwd(_ptr(Q), _ptr(D), _dtype_code(Q), _ptr(argmax), _ptr(grad_scores), Nq, Lq, B, Ld, d,
+                          _ptr(dQ), _ptr(dD), _ptr(row_ptr), _ptr(col_idx), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(Q, stream))
+    _check(st, "maxsim_bwd")
+    return dQ, dD, row_ptr, col_idx
+
+
+class MaxSimFunction(torch.autograd.Function):
+    """score = MaxSim(Q, D) as an autograd op: the forward saves the argmax and the
+    backward builds the inverse-grid CSR and the gradients (paper Section 4.2)."""
+
+    @staticmethod
+    def forward(ctx, Q, D):
+        scores, argmax = maxsim_fwd(Q, D)
+        ctx.save_for_backward(Q, D, argmax)
+        return scores
+
+    @staticmethod
+    def backward(ctx, grad_scores):
+        Q, D, argmax = ctx.saved_tensors
+        dQ, dD, _, _ = maxsim_bwd(Q, D, argmax, grad_scores.float().contiguous())
+        return dQ.to(Q.dtype), dD.to(D.dtype)
+
+
+def maxsim(Q, D):
+    """All-pairs MaxSim scores [Nq, B] with autograd support."""
+    return MaxSimFunction.apply(Q, D)

@@ -1,0 +1,171 @@
+// capi.cpp -- the C ABI declared in include/maxsim.h: host-side argument
+// validation (no HIP call before it passes), then the kernel launchers.
+#include "maxsim.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include "internal.h"
+
+namespace {
+
+using maxsim::kDim;
+using maxsim::kMaxLq;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_common(int32_t Nq, int32_t Lq, int32_t B, int32_t d) {
+    if (Nq < 0 || B < 0 || Lq < 1) return MAXSIM_ERR_SHAPE;
+    if (d != kDim || Lq > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
+    // every output index (q*B + b)*Lq + i must fit in int64 comfortably and the
+    // grid in 32 bits; sizes beyond 2^40 outputs are rejected outright
+    if ((int64_t)Nq * B > (int64_t)1 << 40) return MAXSIM_ERR_SHAPE;
+    return MAXSIM_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int maxsim_fwd(const void* Q, const void* D, const int32_t* d_lens, int32_t Nq, int32_t Lq,
+               int32_t B, int32_t Ld, int32_t d, int32_t dtype, float* scores, int32_t* argmax,
+               void* stream) {
+    int st = check_common(Nq, Lq, B, d);
+    if (st != MAXSIM_OK) return st;
+    if (Ld < 1) return MAXSIM_ERR_SHAPE;
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_UNSUPPORTED;
+    if (Nq == 0 || B == 0) return MAXSIM_OK;
+    if (!Q || !D || !scores) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(scores, 4) || !aligned(argmax, 4) ||
+        !aligned(d_lens, 4))
+        return MAXSIM_ERR_ALIGN;
+    maxsim::FwdArgs a{};
+    a.Q = Q;
+    a.D = D;
+    a.d_lens = d_lens;
+    a.Nq = Nq;
+    a.Lq = Lq;
+    a.B = B;
+    a.Ld = Ld;
+    a.T = (int64_t)B * Ld;
+    a.scores = scores;
+    a.argmax = argmax;
+    a.elem = dtype == MAXSIM_BF16 ? maxsim::kBF16 : maxsim::kF16;
+    a.varlen = false;
+    return hip_status(maxsim::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int maxsim_fwd_varlen(const void* Q, const void* D_packed, const int32_t* cu_seqlens, int32_t Nq,
+                      int32_t Lq, int32_t B, int64_t T, int32_t max_Ld, int32_t d, int32_t dtype,
+                      float* scores, int32_t* argmax, void* stream) {
+    int st = check_common(Nq, Lq, B, d);
+    if (st != MAXSIM_OK) return st;
+    if (T < 0 || max_Ld < 1) return MAXSIM_ERR_SHAPE;
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_UNSUPPORTED;
+    if (Nq == 0 || B == 0) return MAXSIM_OK;
+    if (!Q || !cu_seqlens || !scores || (T > 0 && !D_packed)) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D_packed, 16) || !aligned(cu_seqlens, 4) ||
+        !aligned(scores, 4) || !aligned(argmax, 4))
+        return MAXSIM_ERR_ALIGN;
+    maxsim::FwdArgs a{};
+    a.Q = Q;
+    a.D = D_packed;
+    a.cu = cu_seqlens;
+    a.Nq = Nq;
+    a.Lq = Lq;
+    a.B = B;
+    a.Ld = max_Ld;
+    a.T = T;
+    a.scores = scores;
+    a.argmax = argmax;
+    a.elem = dtype == MAXSIM_BF16 ? maxsim::kBF16 : maxsim::kF16;
+    a.varlen = true;
+    return hip_status(maxsim::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int maxsim_fwd_i8(const int8_t* Q, const float* q_scale, const int8_t* D_packed,
+                  const float* d_scale, const int32_t* cu_seqlens, int32_t Nq, int32_t Lq,
+                  int32_t B, int64_t T, int32_t max_Ld, int32_t d, float* scores, int32_t* argmax,
+                  void* stream) {
+    int st = check_common(Nq, Lq, B, d);
+    if (st != MAXSIM_OK) return st;
+    if (T < 0 || max_Ld < 1) return MAXSIM_ERR_SHAPE;
+    if (Nq == 0 || B == 0) return MAXSIM_OK;
+    if (!Q || !q_scale || !cu_seqlens || !scores || (T > 0 && (!D_packed || !d_scale)))
+        return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D_packed, 16) || !aligned(q_scale, 4) ||
+        !aligned(d_scale, 4) || !aligned(cu_seqlens, 4) || !aligned(scores, 4) ||
+        !aligned(argmax, 4))
+        return MAXSIM_ERR_ALIGN;
+    maxsim::FwdArgs a{};
+    a.Q = Q;
+    a.D = D_packed;
+    a.cu = cu_seqlens;
+    a.q_scale = q_scale;
+    a.d_scale = d_scale;
+    a.Nq = Nq;
+    a.Lq = Lq;
+    a.B = B;
+    a.Ld = max_Ld;
+    a.T = T;
+    a.scores = scores;
+    a.argmax = argmax;
+    a.elem = maxsim::kI8;
+    a.varlen = true;
+    return hip_status(maxsim::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t maxsim_bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld) {
+    if (Nq < 1 || B < 1 || Lq < 1 || Ld < 1) return 0;
+    return maxsim::bwd_workspace_bytes(Nq, B, Lq, Ld);
+}
+
+int maxsim_bwd(const void* Q, const void* D, int32_t dtype, const int32_t* argmax,
+               const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B, int32_t Ld, int32_t d,
+               float* dQ, float* dD, int32_t* row_ptr, int32_t* col_idx, void* workspace,
+               size_t workspace_bytes, void* stream) {
+    if (Nq < 1 || B < 1 || Lq < 1 || Ld < 1) return MAXSIM_ERR_SHAPE;
+    if ((int64_t)Nq * B * Lq >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
+    if ((int64_t)B * Ld >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
+    if (d != kDim || Lq > kMaxLq || Ld > maxsim::kMaxLdBwd) return MAXSIM_ERR_UNSUPPORTED;
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_UNSUPPORTED;
+    if (!Q || !D || !argmax || !grad_scores || !dQ || !dD || !row_ptr || !col_idx || !workspace)
+        return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(dQ, 16) || !aligned(dD, 16) ||
+        !aligned(argmax, 4) || !aligned(grad_scores, 4) || !aligned(row_ptr, 4) ||
+        !aligned(col_idx, 4) || !aligned(workspace, 16))
+        return MAXSIM_ERR_ALIGN;
+    if (workspace_bytes < maxsim::bwd_workspace_bytes(Nq, B, Lq, Ld)) return MAXSIM_ERR_WORKSPACE;
+    maxsim::BwdArgs a{};
+    a.Q = Q;
+    a.D = D;
+    a.argmax = argmax;
+    a.g = grad_scores;
+    a.Nq = Nq;
+    a.Lq = Lq;
+    a.B = B;
+    a.Ld = Ld;
+    a.elem = dtype == MAXSIM_BF16 ? maxsim::kBF16 : maxsim::kF16;
+    a.dQ = dQ;
+    a.dD = dD;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.workspace = workspace;
+    return hip_status(maxsim::launch_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* maxsim_status_string(int status) {
+    switch (status) {
+        case MAXSIM_OK: return "MAXSIM_OK";
+        case MAXSIM_ERR_NULL: return "MAXSIM_ERR_NULL: a required pointer is NULL";
+        case MAXSIM_ERR_SHAPE: return "MAXSIM_ERR_SHAPE: invalid or overflowing size";
+        case MAXSIM_ERR_UNSUPPORTED: return "MAXSIM_ERR_UNSUPPORTED: d, Lq, Ld or dtype outside what the kernels support";
+        case MAXSIM_ERR_ALIGN: return "MAXSIM_ERR_ALIGN: misaligned pointer";
+        case MAXSIM_ERR_WORKSPACE: return "MAXSIM_ERR_WORKSPACE: workspace too small";
+        case MAXSIM_ERR_HIP: return "MAXSIM_ERR_HIP: kernel launch failed";
+        default: return "unknown maxsim status";
+    }
+}
+
+}  // extern "C"

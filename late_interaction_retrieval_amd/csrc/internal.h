@@ -1,0 +1,53 @@
+// internal.h -- host-side interface between the C ABI (capi.cpp) and the
+// kernel launchers (fwd.hip, bwd.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace maxsim {
+
+enum ElemType { kF16 = 0, kBF16 = 1, kI8 = 2 };
+
+constexpr int kDim = 128;        // embedding width every kernel is built for
+constexpr int kMaxLq = 1024;     // query tokens one workgroup keeps on chip
+constexpr int kMaxLdBwd = 4096;  // document tokens the CSR fill kernel keeps in LDS
+
+struct FwdArgs {
+    const void* Q;            // [Nq, Lq, 128]
+    const void* D;            // padded [B, Ld, 128] or packed [T, 128]
+    const int32_t* d_lens;    // padded: [B] or nullptr
+    const int32_t* cu;        // packed: [B+1]
+    const float* q_scale;     // int8: [Nq, Lq]
+    const float* d_scale;     // int8: [T]
+    int64_t T;                // packed: rows of D
+    int32_t Nq, Lq, B, Ld;    // Ld: padded row stride per document
+    float* scores;            // [Nq, B]
+    int32_t* argmax;          // [Nq, B, Lq] or nullptr
+    int elem;                 // ElemType
+    bool varlen;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+struct BwdArgs {
+    const void* Q;            // [Nq, Lq, 128]
+    const void* D;            // [B, Ld, 128]
+    const int32_t* argmax;    // [Nq, B, Lq]
+    const float* g;           // [Nq, B]
+    int32_t Nq, Lq, B, Ld;
+    int elem;                 // kF16 / kBF16
+    float* dQ;                // [Nq, Lq, 128]
+    float* dD;                // [B, Ld, 128]
+    int32_t* row_ptr;         // [B*Ld + 1]
+    int32_t* col_idx;         // [Nq*B*Lq]
+    void* workspace;
+};
+
+// Queries per CSR group (one wave each) for a document length; 0 if unsupported.
+int bwd_group(int32_t Ld);
+size_t bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace maxsim

@@ -1,0 +1,151 @@
+"""C ABI of libmaxsim.so on a host without a GPU.
+
+Checks that the library loads, exports every function include/maxsim.h
+declares with the argument count the binding uses, and that host-side
+validation returns the documented status codes.  Only invalid or empty
+arguments are passed: validation rejects them before any HIP call, so no
+device work is attempted.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "maxsim.h")
+LIB = os.path.join(ROOT, "late_interaction_retrieval_amd", "libmaxsim.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        from late_interaction_retrieval_amd import build
+        build.build()
+
+
+_ensure_built()
+from late_interaction_retrieval_amd import binding as bd  # noqa: E402
+
+L = bd.lib()
+A = ctypes.c_void_p(0x10000)  # aligned non-null fake pointers: never dereferenced
+M = ctypes.c_void_p(0x10001)  # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(maxsim_\w+)\s*\(([^)]*)\)\s*;", text, flags=re.M):
+        params = [p for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+        out[m.group(1)] = len(params)
+    return out
+
+
+def test_every_declared_symbol_is_exported_with_binding_arity():
+    decl = declared_functions()
+    assert set(decl) == {"maxsim_fwd", "maxsim_fwd_varlen", "maxsim_fwd_i8", "maxsim_bwd_workspace_bytes",
+                         "maxsim_bwd", "maxsim_status_string"}
+    raw = ctypes.CDLL(LIB)
+    for name, nargs in decl.items():
+        assert hasattr(raw, name), name
+        assert len(bd.SIGNATURES[name][1]) == nargs, name
+
+
+def fwd(**kw):
+    a = dict(Q=A, D=A, d_lens=None, Nq=2, Lq=32, B=3, Ld=10, d=128, dt=0, scores=A, argmax=A, stream=None)
+    a.update(kw)
+    return L.maxsim_fwd(a["Q"], a["D"], a["d_lens"], a["Nq"], a["Lq"], a["B"], a["Ld"], a["d"], a["dt"],
+                        a["scores"], a["argmax"], a["stream"])
+
+
+def fwd_varlen(**kw):
+    a = dict(Q=A, D=A, cu=A, Nq=2, Lq=32, B=3, T=100, maxld=50, d=128, dt=1, scores=A, argmax=None,
+             stream=None)
+    a.update(kw)
+    return L.maxsim_fwd_varlen(a["Q"], a["D"], a["cu"], a["Nq"], a["Lq"], a["B"], a["T"], a["maxld"], a["d"],
+                               a["dt"], a["scores"], a["argmax"], a["stream"])
+
+
+def fwd_i8(**kw):
+    a = dict(Q=A, qs=A, D=A, ds=A, cu=A, Nq=2, Lq=32, B=3, T=100, maxld=50, d=128, scores=A, argmax=A,
+             stream=None)
+    a.update(kw)
+    return L.maxsim_fwd_i8(a["Q"], a["qs"], a["D"], a["ds"], a["cu"], a["Nq"], a["Lq"], a["B"], a["T"],
+                           a["maxld"], a["d"], a["scores"], a["argmax"], a["stream"])
+
+
+def bwd(**kw):
+    a = dict(Q=A, D=A, dt=0, A=A, g=A, Nq=4, Lq=32, B=5, Ld=64, d=128, dQ=A, dD=A, rp=A, ci=A, ws=A,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.maxsim_bwd(a["Q"], a["D"], a["dt"], a["A"], a["g"], a["Nq"], a["Lq"], a["B"], a["Ld"], a["d"],
+                        a["dQ"], a["dD"], a["rp"], a["ci"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), bd.MAXSIM_ERR_NULL), (dict(D=None), bd.MAXSIM_ERR_NULL),
+    (dict(scores=None), bd.MAXSIM_ERR_NULL),
+    (dict(Lq=0), bd.MAXSIM_ERR_SHAPE), (dict(Nq=-1), bd.MAXSIM_ERR_SHAPE), (dict(B=-2), bd.MAXSIM_ERR_SHAPE),
+    (dict(Ld=0), bd.MAXSIM_ERR_SHAPE),
+    (dict(d=64), bd.MAXSIM_ERR_UNSUPPORTED), (dict(Lq=1025), bd.MAXSIM_ERR_UNSUPPORTED),
+    (dict(dt=7), bd.MAXSIM_ERR_UNSUPPORTED),
+    (dict(Q=M), bd.MAXSIM_ERR_ALIGN), (dict(D=M), bd.MAXSIM_ERR_ALIGN), (dict(scores=M), bd.MAXSIM_ERR_ALIGN),
+    (dict(argmax=M), bd.MAXSIM_ERR_ALIGN), (dict(d_lens=M), bd.MAXSIM_ERR_ALIGN),
+    (dict(Nq=0, Q=None), bd.MAXSIM_OK), (dict(B=0, D=None), bd.MAXSIM_OK),
+])
+def test_fwd_validation(kw, code):
+    assert fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), bd.MAXSIM_ERR_NULL), (dict(D=None), bd.MAXSIM_ERR_NULL),
+    (dict(D=None, T=0), bd.MAXSIM_ERR_ALIGN),  # D may be NULL when T == 0; argmax/cu still checked
+    (dict(T=-1), bd.MAXSIM_ERR_SHAPE), (dict(maxld=0), bd.MAXSIM_ERR_SHAPE),
+    (dict(dt=2), bd.MAXSIM_ERR_UNSUPPORTED), (dict(d=256), bd.MAXSIM_ERR_UNSUPPORTED),
+    (dict(cu=M), bd.MAXSIM_ERR_ALIGN), (dict(Q=M), bd.MAXSIM_ERR_ALIGN),
+    (dict(B=0), bd.MAXSIM_OK),
+])
+def test_fwd_varlen_validation(kw, code):
+    if kw.get("T") == 0:
+        kw = dict(kw, cu=M)
+    assert fwd_varlen(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qs=None), bd.MAXSIM_ERR_NULL), (dict(ds=None), bd.MAXSIM_ERR_NULL), (dict(cu=None), bd.MAXSIM_ERR_NULL),
+    (dict(Lq=-3), bd.MAXSIM_ERR_SHAPE), (dict(T=-5), bd.MAXSIM_ERR_SHAPE),
+    (dict(d=127), bd.MAXSIM_ERR_UNSUPPORTED), (dict(Lq=4096), bd.MAXSIM_ERR_UNSUPPORTED),
+    (dict(Q=M), bd.MAXSIM_ERR_ALIGN), (dict(ds=M), bd.MAXSIM_ERR_ALIGN), (dict(qs=M), bd.MAXSIM_ERR_ALIGN),
+    (dict(Nq=0), bd.MAXSIM_OK),
+])
+def test_fwd_i8_validation(kw, code):
+    assert fwd_i8(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), bd.MAXSIM_ERR_NULL), (dict(ws=None), bd.MAXSIM_ERR_NULL), (dict(ci=None), bd.MAXSIM_ERR_NULL),
+    (dict(Nq=0), bd.MAXSIM_ERR_SHAPE), (dict(Ld=0), bd.MAXSIM_ERR_SHAPE),
+    (dict(Nq=1 << 15, B=1 << 10, Lq=1 << 6), bd.MAXSIM_ERR_SHAPE),  # Nq*B*Lq >= 2^31
+    (dict(Ld=5000), bd.MAXSIM_ERR_UNSUPPORTED), (dict(d=96), bd.MAXSIM_ERR_UNSUPPORTED),
+    (dict(dt=3), bd.MAXSIM_ERR_UNSUPPORTED),
+    (dict(dQ=M), bd.MAXSIM_ERR_ALIGN), (dict(ws=M), bd.MAXSIM_ERR_ALIGN), (dict(g=M), bd.MAXSIM_ERR_ALIGN),
+    (dict(wsb=0), bd.MAXSIM_ERR_WORKSPACE),
+])
+def test_bwd_validation(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_workspace_bytes():
+    # one int32 count per (document, group of queries, row)
+    n = L.maxsim_bwd_workspace_bytes(64, 64, 1024, 1024)
+    assert n == 64 * 16 * 1024 * 4  # Ld = 1024 -> 4 queries per group -> 16 groups
+    assert L.maxsim_bwd_workspace_bytes(0, 1, 1, 1) == 0
+    assert L.maxsim_bwd_workspace_bytes(1, 1, 1, 5000) == 0
+    assert bwd(wsb=n - 1, Nq=64, B=64, Lq=1024, Ld=1024) == bd.MAXSIM_ERR_WORKSPACE
+
+
+def test_status_strings():
+    for code in range(7):
+        s = L.maxsim_status_string(code).decode()
+        assert s.startswith("MAXSIM_")
+    assert "unknown" in L.maxsim_status_string(99).decode()

@@ -1,0 +1,193 @@
+"""GPU parity of the fused forward (fp16 / bf16, padded and cu_seqlens) against
+the CPU oracle, through the C ABI.  Run on an MI355X: pytest -m gpu."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from late_interaction_retrieval_amd import inputs
+from gpu_util import (DEV, check_argmax, check_scores, oracle_dtype, pad_width, sub_corpus, to_dev)
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "maxsim_hand.json")
+
+
+@pytest.fixture(scope="module")
+def bd():
+    from late_interaction_retrieval_amd import binding
+    assert torch.cuda.is_available()
+    return binding
+
+
+def run_padded(bd, Q, D, dtn, lens=None, with_argmax=True):
+    s, a = bd.maxsim_fwd(to_dev(Q, dtn), to_dev(D, dtn), None if lens is None else to_dev(lens),
+                         with_argmax=with_argmax)
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), (a.cpu().numpy() if a is not None else None)
+
+
+def run_varlen(bd, Q, Dp, cu, dtn, with_argmax=True):
+    lens = np.diff(cu)
+    s, a = bd.maxsim_fwd_varlen(to_dev(Q, dtn), to_dev(Dp, dtn), to_dev(cu), max(1, int(lens.max(initial=1))),
+                                with_argmax=with_argmax)
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), (a.cpu().numpy() if a is not None else None)
+
+
+def full_check_varlen(bd, Q, Dp, cu, dtn, where):
+    odt = oracle_dtype(dtn)
+    s_ref, a_ref, m_ref = oracle.fwd_varlen(Q, Dp, cu, odt, want_rowmax=True)
+    s, a = run_varlen(bd, Q, Dp, cu, dtn)
+    Lq = Q.shape[1]
+    check_scores(s, s_ref, Lq, where)
+    sim = oracle.sim_at(Q, Dp, cu, odt, a)
+    check_argmax(a, a_ref, m_ref, sim, np.diff(cu), where)
+    s2, a2 = run_varlen(bd, Q, Dp, cu, dtn, with_argmax=False)
+    assert np.array_equal(s2, s), where + ": scores differ with and without argmax"
+    return s, a
+
+
+@pytest.mark.parametrize("dtn", [inputs.F16, inputs.BF16])
+def test_golden_hand_case(bd, dtn):
+    g = json.load(open(GOLD))["fwd_padded"]
+    f = np.array(g["Q"], np.float32)
+    dd = np.array(g["D"], np.float32)
+    if dtn == inputs.F16:
+        Q, D = pad_width(f.astype(np.float16)), pad_width(dd.astype(np.float16))
+    else:
+        Q, D = pad_width(inputs.f32_to_bf16_bits(f)), pad_width(inputs.f32_to_bf16_bits(dd))
+    lens = np.array(g["d_lens"], np.int32)
+    s, a = run_padded(bd, Q, D, dtn, lens)
+    assert np.array_equal(s, np.array(g["scores"], np.float32))
+    assert np.array_equal(a, np.array(g["argmax"]))
+    cu = inputs.cu_seqlens(lens)
+    Dp = np.concatenate([D[b, :lens[b]] for b in range(len(lens))])
+    s, a = run_varlen(bd, Q, Dp, cu, dtn)
+    assert np.array_equal(s, np.array(g["scores"], np.float32))
+    assert np.array_equal(a, np.array(g["argmax"]))
+
+
+SHAPES = [  # Nq, Lq, B, (Ld lo, hi)
+    (1, 1, 3, (1, 1)),
+    (1, 7, 5, (1, 40)),
+    (2, 16, 7, (16, 16)),
+    (1, 32, 40, (100, 180)),
+    (3, 31, 9, (0, 70)),
+    (5, 33, 11, (1, 129)),
+    (40, 32, 17, (32, 300)),
+    (3, 128, 6, (60, 200)),
+    (2, 300, 4, (1, 513)),
+    (1, 1024, 3, (1000, 1100)),
+    (2, 1000, 2, (64, 64)),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+@pytest.mark.parametrize("dtn", [inputs.F16, inputs.BF16])
+def test_random_shapes_varlen_and_padded(bd, shape, dtn):
+    Nq, Lq, B, (lo, hi) = shape
+    seed = sum(shape[:3]) + lo + hi
+    Q = inputs.random_rows(seed, Nq * Lq, 128, dtn).reshape(Nq, Lq, 128)
+    lens = np.random.default_rng(seed).integers(lo, hi + 1, size=B).astype(np.int32)
+    cu = inputs.cu_seqlens(lens)
+    Dp = inputs.random_rows(seed + 1, int(cu[-1]), 128, dtn, stream=4)
+    where = "%s %s" % (dtn, shape)
+    s, a = full_check_varlen(bd, Q, Dp, cu, dtn, where)
+    # padded + d_lens gives bit-identical results (same tiles, same order)
+    Ld = max(1, int(lens.max()))
+    Dpad = inputs.pad_packed(Dp, cu, Ld)
+    s2, a2 = run_padded(bd, Q, Dpad, dtn, lens)
+    assert np.array_equal(s2, s) and np.array_equal(a2, a), where + ": padded != varlen"
+
+
+def test_padding_never_selected_all_negative(bd):
+    """All valid similarities negative, padding rows huge: padding is never picked."""
+    Q = np.full((2, 40, 128), 0.05, np.float16)
+    D = np.full((3, 70, 128), -0.02, np.float16)
+    D[:, 50:] = 30.0
+    D[1, 17] = -0.01
+    lens = np.array([50, 50, 0], np.int32)
+    s, a = run_padded(bd, Q, D, inputs.F16, lens)
+    s_ref, a_ref = oracle.fwd_padded(Q, D, oracle.F16, d_lens=lens)
+    check_scores(s, s_ref, 40, "all-negative")
+    assert np.all(a[:, 0] == 0) and np.all(a[:, 1] == 17) and np.all(a[:, 2] == -1)
+    assert np.all(np.isneginf(s[:, 2]))
+
+
+@pytest.mark.parametrize("dtn", [inputs.F16, inputs.BF16])
+def test_signed_basis_gives_exactly_lq(bd, dtn):
+    d, Lq = 128, 96
+    rng = np.random.default_rng(5)
+    ks = rng.integers(0, d, size=Lq)
+    sg = rng.choice([-1.0, 1.0], size=Lq).astype(np.float32)
+    Qf = np.zeros((1, Lq, d), np.float32)
+    Qf[0, np.arange(Lq), ks] = sg
+    others = inputs.random_rows(6, 300, d, dtn)
+    if dtn == inputs.F16:
+        Q, basis = Qf.astype(np.float16), Qf[0].astype(np.float16)
+    else:
+        Q, basis = inputs.f32_to_bf16_bits(Qf), inputs.f32_to_bf16_bits(Qf[0])
+    Dp = np.concatenate([others[:150], basis, others[150:]])
+    Dp = Dp[rng.permutation(len(Dp))]
+    cu = np.array([0, len(Dp)], np.int32)
+    s, a = run_varlen(bd, Q, Dp, cu, dtn)
+    assert s[0, 0] == np.float32(Lq)
+
+
+def test_deterministic_reruns(bd):
+    Q = inputs.random_rows(70, 64 * 32, 128, inputs.F16).reshape(64, 32, 128)
+    lens = inputs.lengths(0, 70, 300, 32, 300)
+    cu = inputs.cu_seqlens(lens)
+    Dp = inputs.random_rows(71, int(cu[-1]), 128, inputs.F16)
+    s1, a1 = run_varlen(bd, Q, Dp, cu, inputs.F16)
+    s2, a2 = run_varlen(bd, Q, Dp, cu, inputs.F16)
+    assert np.array_equal(s1, s2) and np.array_equal(a1, a2)
+
+
+# ---------------------------------------------------------------------------
+# Workload-sized runs: the GPU runs the whole workload in the same launch
+# configuration the benchmark times; the oracle checks a seeded sample of
+# documents (all of them for the tiny workload).
+# ---------------------------------------------------------------------------
+def sampled_check(bd, w, docs, where):
+    dtn = w["dtype"]
+    Q, Dp, cu = w["Q"], w["D_packed"], w["cu_seqlens"]
+    s, a = run_varlen(bd, Q, Dp, cu, dtn)
+    sub, subcu = sub_corpus(Dp, cu, docs)
+    odt = oracle_dtype(dtn)
+    s_ref, a_ref, m_ref = oracle.fwd_varlen(Q, sub, subcu, odt, want_rowmax=True)
+    check_scores(s[:, docs], s_ref, w["Lq"], where)
+    sim = oracle.sim_at(Q, sub, subcu, odt, a[:, docs])
+    flips = check_argmax(a[:, docs], a_ref, m_ref, sim, np.diff(subcu), where)
+    print("%s: %d docs checked, %d argmax near-tie flips" % (where, len(docs), flips), flush=True)
+    return s, a
+
+
+def test_workload_colbert_tiny_full(bd):
+    w = inputs.make("colbert_tiny")
+    sampled_check(bd, w, np.arange(w["B"]), "colbert_tiny")
+    # the padded path (fixed Ld = 180) gives the same bits
+    Dpad = w["D_packed"].reshape(w["B"], 180, 128)
+    s, a = run_padded(bd, w["Q"], Dpad, inputs.F16)
+    s2, a2 = run_varlen(bd, w["Q"], w["D_packed"], w["cu_seqlens"], inputs.F16)
+    assert np.array_equal(s, s2) and np.array_equal(a, a2)
+
+
+def test_workload_colbert_rerank_varlen_sampled(bd):
+    w = inputs.make("colbert_rerank_varlen")
+    docs = np.sort(np.random.default_rng(1).choice(w["B"], size=64, replace=False))
+    docs[0], docs[-1] = 0, w["B"] - 1
+    s, _ = sampled_check(bd, w, docs, "colbert_rerank_varlen")
+    # padded to 300 with d_lens: identical scores
+    Dpad = inputs.pad_packed(w["D_packed"], w["cu_seqlens"], 300)
+    s2, _ = run_padded(bd, w["Q"], Dpad, inputs.F16, w["lens"], with_argmax=False)
+    assert np.array_equal(s, s2)
+
+
+def test_workload_colpali_sampled(bd):
+    w = inputs.make("colpali_fwd")
+    docs = np.array([0, 1, 4999, 9998, 9999])
+    sampled_check(bd, w, docs, "colpali_fwd")

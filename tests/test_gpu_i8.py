@@ -1,0 +1,94 @@
+"""GPU parity of the INT8 x INT8 forward: bit-exact scores and argmax against the
+oracle, through the C ABI.  Run on an MI355X: pytest -m gpu."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from late_interaction_retrieval_amd import inputs
+from gpu_util import pad_width, sub_corpus, to_dev
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "maxsim_hand.json")
+
+
+@pytest.fixture(scope="module")
+def bd():
+    from late_interaction_retrieval_amd import binding
+    assert torch.cuda.is_available()
+    return binding
+
+
+def run_i8(bd, Q, qs, Dp, ds, cu, with_argmax=True):
+    lens = np.diff(cu)
+    s, a = bd.maxsim_fwd_i8(to_dev(Q), to_dev(qs), to_dev(Dp), to_dev(ds), to_dev(cu),
+                            max(1, int(lens.max(initial=1))), with_argmax=with_argmax)
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), (a.cpu().numpy() if a is not None else None)
+
+
+def assert_bits_equal(got, ref, where):
+    got = np.asarray(got, np.float32)
+    ref = np.asarray(ref, np.float32)
+    bad = got.view(np.uint32) != ref.view(np.uint32)
+    assert not bad.any(), "%s: %d scores differ, first at %s: %r vs %r" % (
+        where, int(bad.sum()), np.argwhere(bad)[0], got[bad][0], ref[bad][0])
+
+
+def test_golden_hand_case(bd):
+    g = json.load(open(GOLD))["fwd_i8"]
+    Q = pad_width(np.array(g["Q"], np.int8))
+    Dp = pad_width(np.array(g["D"], np.int8))
+    s, a = run_i8(bd, Q, np.array(g["q_scale"], np.float32), Dp, np.array(g["d_scale"], np.float32),
+                  np.array(g["cu_seqlens"], np.int32))
+    exp = np.array([[float(v) for v in row] for row in g["scores"]], np.float32)
+    assert_bits_equal(s, exp, "golden")
+    assert np.array_equal(a, np.array(g["argmax"]))
+
+
+SHAPES = [(1, 1, 4, (1, 3)), (2, 7, 9, (0, 40)), (3, 32, 20, (32, 512)), (40, 32, 13, (1, 100)),
+          (1, 300, 5, (10, 600)), (2, 1024, 3, (100, 200))]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+def test_random_shapes_bit_exact(bd, shape):
+    Nq, Lq, B, (lo, hi) = shape
+    seed = 500 + sum(shape[:3]) + lo + hi
+    Q, qs = inputs.random_rows(seed, Nq * Lq, 128, inputs.I8)
+    lens = np.random.default_rng(seed).integers(lo, hi + 1, size=B).astype(np.int32)
+    cu = inputs.cu_seqlens(lens)
+    Dp, ds = inputs.random_rows(seed + 1, int(cu[-1]), 128, inputs.I8, stream=4)
+    Q, qs = Q.reshape(Nq, Lq, 128), qs.reshape(Nq, Lq)
+    s_ref, a_ref = oracle.fwd_i8(Q, qs, Dp, ds, cu)
+    s, a = run_i8(bd, Q, qs, Dp, ds, cu)
+    assert_bits_equal(s, s_ref, str(shape))
+    assert np.array_equal(a, a_ref)
+    s2, _ = run_i8(bd, Q, qs, Dp, ds, cu, with_argmax=False)
+    assert_bits_equal(s2, s_ref, str(shape) + " no argmax")
+
+
+def test_duplicate_tokens_tie_to_first(bd):
+    Q, qs = inputs.random_rows(41, 64, 128, inputs.I8)
+    D, ds = inputs.random_rows(42, 90, 128, inputs.I8)
+    Dp = np.concatenate([D, D[::-1]])
+    dsp = np.concatenate([ds, ds[::-1]])
+    cu = np.array([0, 180], np.int32)
+    Q, qs = Q.reshape(2, 32, 128), qs.reshape(2, 32)
+    s_ref, a_ref = oracle.fwd_i8(Q, qs, Dp, dsp, cu)
+    s, a = run_i8(bd, Q, qs, Dp, dsp, cu)
+    assert_bits_equal(s, s_ref, "dup")
+    assert np.array_equal(a, a_ref) and np.all(a < 90)
+
+
+def test_workload_int8_sampled(bd):
+    w = inputs.make("int8_varlen")
+    s, a = run_i8(bd, w["Q"], w["q_scale"], w["D_packed"], w["d_scale"], w["cu_seqlens"])
+    docs = np.sort(np.random.default_rng(2).choice(w["B"], size=200, replace=False))
+    docs[0], docs[-1] = 0, w["B"] - 1
+    sub, subcu, subds = sub_corpus(w["D_packed"], w["cu_seqlens"], docs, w["d_scale"])
+    s_ref, a_ref = oracle.fwd_i8(w["Q"], w["q_scale"], sub, subds, subcu)
+    assert_bits_equal(s[:, docs], s_ref, "int8_varlen")
+    assert np.array_equal(a[:, docs], a_ref)
