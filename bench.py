@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MaxSim hot path on one MI355X.
+
+    python bench.py [--workload NAME] [--steps K] [--warmup W] [--gpus 1]
+
+Prints ONE JSON line.  A step is one pass of the hot path over one batch of
+seeded synthetic input already resident in HBM:
+  colbert_rerank_varlen (default): 64 queries x 32 tokens against a 10,000
+      document corpus, lengths uniform in [32, 300], packed by cu_seqlens,
+      fp16 -> scores [64, 10000] (maxsim_fwd_varlen);
+  colbert_tiny:  1 query x 1,000 documents of 180 tokens, fp16, scores+argmax;
+  colpali_fwd:   4 queries x 10,000 documents, Lq = Ld = 1024, bf16, scores+argmax;
+  contrastive_train: 64 x 64 in-batch pairs, Lq = Ld = 1024, bf16: forward
+      with argmax, InfoNCE gradient (tau = 0.02), backward (CSR, dD, dQ);
+  int8_varlen:   32 queries x 32 tokens against 100,000 int8 documents,
+      lengths uniform in [32, 512] -> scores (maxsim_fwd_i8).
+`value` is the algorithmic TFLOP/s (TOP/s for int8) of the whole step:
+2*Nq*Lq*d per (query, document token) pair, real tokens only.  The roofline
+object reports the dominant kernel against MI355X's published peaks, timed
+with HIP events on the stream it is launched on; the CPU baseline is the
+oracle timed on the host's cores on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MaxSim fwd/bwd TFLOP/s + doc-tokens/s; % of MFMA or HBM roofline; peak mem"
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0}  # dense, MI355X
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "fwd": ["late_interaction_retrieval_amd/csrc/fwd.hip"],
+    "bwd": ["late_interaction_retrieval_amd/csrc/bwd.hip"],
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="colbert_rerank_varlen",
+                    choices=["colbert_rerank_varlen", "colbert_tiny", "colpali_fwd", "contrastive_train",
+                             "int8_varlen"])
+    ap.add_argument("--argmax", choices=["auto", "on", "off"], default="auto",
+                    help="save the argmax in inference workloads (auto: as the workload specifies)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    return ap.parse_args()
+
+
+def source_sha(kind):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, "traffic_%s_%s.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != source_sha(kernel):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (one process, one MI355X); --gpus %d is not "
+              "supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    lib_path = os.path.join(ROOT, "late_interaction_retrieval_amd", "libmaxsim.so")
+    if not os.path.exists(lib_path):
+        from late_interaction_retrieval_amd import build
+        build.build()
+    from late_interaction_retrieval_amd import binding as bd
+    from late_interaction_retrieval_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = args.workload
+    w = inputs.make(name)
+    Nq, Lq, B, d, T = w["Nq"], w["Lq"], w["B"], w["d"], w["T"]
+    dtn = w["dtype"]
+    want_argmax = {"colbert_rerank_varlen": False, "colbert_tiny": True, "colpali_fwd": True,
+                   "contrastive_train": True, "int8_varlen": False}[name]
+    if args.argmax != "auto":
+        want_argmax = args.argmax == "on"
+
+    def dev_t(a, bf16=False):
+        a = np.ascontiguousarray(a)
+        if bf16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    isbf = dtn == inputs.BF16
+    Q = dev_t(w["Q"], isbf)
+    cu = dev_t(w["cu_seqlens"])
+    max_ld = int(w["lens"].max())
+    pair_flops = 2.0 * Nq * Lq * d  # per real document token
+    fwd_flops = pair_flops * T
+    extra = {}
+    stream = torch.cuda.current_stream(dev)
+
+    # D copies: the small tiny workload fits the 256 MB MALL, so it rotates
+    # 12 copies (>= 550 MB) between steps to time HBM, not the cache.
+    ncopies = 12 if name == "colbert_tiny" else 1
+    if name == "int8_varlen":
+        Ds = [dev_t(w["D_packed"]) for _ in range(ncopies)]
+        q_scale = dev_t(w["q_scale"])
+        d_scale = dev_t(w["d_scale"])
+    elif name == "contrastive_train":
+        Ds = [dev_t(w["D_packed"].reshape(B, w["Ld_max"], d), isbf)]
+    else:
+        Ds = [dev_t(w["D_packed"], isbf) for _ in range(ncopies)]
+
+    scores = torch.empty((Nq, B), dtype=torch.float32, device=dev)
+    amax = torch.empty((Nq, B, Lq), dtype=torch.int32, device=dev) if want_argmax else None
+
+    kernel_ms = []  # dominant kernel (the forward) per launch, HIP events on its stream
+    bwd_ms = []
+    ev_pool = []
+
+    if name == "contrastive_train":
+        Dd = Ds[0]
+        Ld = w["Ld_max"]
+        ws = torch.empty(max(16, bd.maxsim_bwd_workspace_bytes(Nq, B, Lq, Ld)), dtype=torch.uint8, device=dev)
+        dQ = torch.empty((Nq, Lq, d), dtype=torch.float32, device=dev)
+        dD = torch.empty((B, Ld, d), dtype=torch.float32, device=dev)
+        rp = torch.empty(B * Ld + 1, dtype=torch.int32, device=dev)
+        ci = torch.empty(Nq * B * Lq, dtype=torch.int32, device=dev)
+        tau = w["tau"]
+        eye = torch.eye(Nq, device=dev, dtype=torch.float32)
+
+        def step(i, timed):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3)) if timed else (None,) * 3
+            if timed:
+                e0.record(stream)
+            bd.maxsim_fwd(Q, Dd, scores=scores, argmax=amax)
+            if timed:
+                e1.record(stream)
+            # InfoNCE over scores / tau with the diagonal as positives (harness, torch)
+            p = torch.softmax(scores / tau, dim=1)
+            g = ((p - eye) / (tau * Nq)).contiguous()
+            if timed:
+                e2b = torch.cuda.Event(enable_timing=True)
+                e2b.record(stream)
+            bd.maxsim_bwd(Q, Dd, amax, g, dQ=dQ, dD=dD, row_ptr=rp, col_idx=ci, workspace=ws)
+            if timed:
+                e2.record(stream)
+                ev_pool.append((e0, e1, e2b, e2))
+
+        bwd_flops = 4.0 * d * Nq * B * Lq
+        step_flops = fwd_flops + bwd_flops
+    elif name == "int8_varlen":
+        def step(i, timed):
+            Dc = Ds[i % ncopies]
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            bd.maxsim_fwd_i8(Q, q_scale, Dc, d_scale, cu, max_ld, scores=scores, argmax=amax,
+                             with_argmax=want_argmax)
+            if timed:
+                e1.record(stream)
+                ev_pool.append((e0, e1))
+
+        step_flops = fwd_flops
+    else:
+        def step(i, timed):
+            Dc = Ds[i % ncopies]
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            bd.maxsim_fwd_varlen(Q, Dc, cu, max_ld, scores=scores, argmax=amax, with_argmax=want_argmax)
+            if timed:
+                e1.record(stream)
+                ev_pool.append((e0, e1))
+
+        step_flops = fwd_flops
+
+    # default K / W: about a second of timed GPU work
+    probe_iters = 3
+    for i in range(probe_iters):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step(0, False)
+    torch.cuda.synchronize()
+    est = max(1e-5, time.perf_counter() - t0)
+    steps = args.steps if args.steps is not None else int(min(2000, max(10, 1.0 / est)))
+    warmup = args.warmup if args.warmup is not None else int(min(50, max(3, 0.2 / est)))
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    peak_mem = torch.cuda.max_memory_allocated(dev)
+
+    for evs in ev_pool:
+        kernel_ms.append(evs[0].elapsed_time(evs[1]))
+        if len(evs) == 4:
+            bwd_ms.append(evs[2].elapsed_time(evs[3]))
+    k_avg_ms = float(np.mean(kernel_ms))
+    k_med_ms = float(np.median(kernel_ms))
+    ms_per_step = elapsed * 1e3 / steps
+    value = step_flops * steps / elapsed / 1e12
+
+    # roofline of the dominant kernel: the forward
+    el = {"f16": "f16", "bf16": "bf16", "i8": "i8"}[dtn]
+    peak = MFMA_PEAK_TFLOPS[el]
+    achieved = fwd_flops / (k_avg_ms * 1e-3) / 1e12
+    rowb = 128 if el == "i8" else 256
+    fwd_bytes = T * rowb + Nq * Lq * rowb + 4 * (B + 1) + 4 * Nq * B
+    if el == "i8":
+        fwd_bytes += 4 * T + 4 * Nq * Lq
+    if want_argmax:
+        fwd_bytes += 4 * Nq * B * Lq
+    traffic = read_traffic("fwd", name)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "kernel": "fwd_kernel", "kernel_avg_ms": round(k_avg_ms, 5), "kernel_median_ms": round(k_med_ms, 5),
+                "algorithmic_flops_per_launch": fwd_flops, "algorithmic_bytes_per_launch": fwd_bytes,
+                "hbm_frac_of_algorithmic_bytes": round(fwd_bytes / (k_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if el == "i8":
+        roofline["unit"] = "TOP/s"
+    if bwd_ms:
+        b_avg = float(np.mean(bwd_ms))
+        Ld = w["Ld_max"]
+        # argmax read, Q and D read (bf16), dQ and dD written (fp32), col_idx written
+        # and read back, row_ptr, upstream gradient
+        bwd_bytes = (4 * Nq * B * Lq + 2 * d * (Nq * Lq + B * Ld) + 4 * d * (Nq * Lq + B * Ld)
+                     + 2 * 4 * Nq * B * Lq + 4 * (B * Ld + 1) + 4 * Nq * B)
+        extra["bwd"] = {"avg_ms": round(b_avg, 5), "algorithmic_bytes": bwd_bytes,
+                        "hbm_gbs": round(bwd_bytes / (b_avg * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(bwd_bytes / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOP/s" if el == "i8" else "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": el,
+        "data": "synthetic (seeded N(0,1) rows, l2-normalised; stands in for ColBERT/ColPali embeddings)",
+        "config": {"workload": name, "Nq": Nq, "Lq": Lq, "B": B, "T_doc_tokens": T, "d": d,
+                   "Ld_range": [int(w["lens"].min()), int(w["lens"].max())], "argmax_saved": want_argmax,
+                   "layout": "padded" if name == "contrastive_train" else "cu_seqlens"},
+        "doc_tokens_per_s": round(T * steps / elapsed, 1),
+        "query_doc_token_pairs_per_s": round(Nq * T * steps / elapsed, 1),
+        "peak_mem_bytes": int(peak_mem),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if extra:
+        out["extra"] = extra
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, target_s):
+    """The oracle as it stands, on the host's cores, on the first n documents
+    of the same workload (all queries), n scaled to about target_s seconds."""
+    import oracle
+
+    name = w["name"]
+    Q, Dp, cu = w["Q"], w["D_packed"], w["cu_seqlens"]
+    Nq, Lq, d = w["Nq"], w["Lq"], w["d"]
+    isi8 = w["dtype"] == "i8"
+    odt = oracle.BF16 if w["dtype"] == "bf16" else oracle.F16
+
+    def run(n):
+        sub = Dp[:cu[n]]
+        subcu = np.ascontiguousarray(cu[:n + 1])
+        t0 = time.perf_counter()
+        if isi8:
+            oracle.fwd_i8(Q, w["q_scale"], sub, w["d_scale"][:cu[n]], subcu)
+        elif name == "contrastive_train":
+            oracle.fwd_varlen(Q[:1], sub, subcu, odt)
+        else:
+            oracle.fwd_varlen(Q, sub, subcu, odt)
+        return time.perf_counter() - t0
+
+    n = 1
+    t = run(n)
+    while t < 0.5 and n < w["B"]:
+        n = min(w["B"], n * 4)
+        t = run(n)
+    if t < target_s and n < w["B"]:
+        n = int(min(w["B"], max(n, n * target_s / max(t, 1e-6))))
+        t = run(n)
+    toks = int(cu[n])
+    nq = 1 if name == "contrastive_train" else Nq
+    flops = 2.0 * nq * Lq * d * toks
+    return {"value": round(flops / t / 1e12, 6), "unit": "TOP/s" if isi8 else "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d queries x first %d documents (%d doc tokens) of the same workload, forward, %.1f s" %
+                      (nq, n, toks, t),
+            "doc_tokens_per_s": round(toks / t, 1)}
+
+
+if __name__ == "__main__":
+    main()
