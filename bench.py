@@ -54,7 +54,22 @@ def parse():
                     help="save the argmax in inference workloads (auto: as the workload specifies)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the workload, run 5 device-to-device copies of MIB MiB: the counter "
+                         "reading of a copy of known size scales the rocprofv3 byte counters")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "reads_per_copy": n, "writes_per_copy": n}), flush=True)
 
 
 def source_sha(kind):
@@ -90,6 +105,10 @@ def main():
         print("bench.py: this build measures one GPU only (one process, one MI355X); --gpus %d is not "
               "supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
 

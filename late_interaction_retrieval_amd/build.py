@@ -20,6 +20,8 @@ HIPCC_FLAGS = [
     "-shared",
     # fp32 products and sums are separate IEEE operations unless fmaf is asked for
     "-ffp-contract=off",
+    # inputs are finite: max needs no NaN canonicalisation (infinities are kept)
+    "-fno-honor-nans",
     # no packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",

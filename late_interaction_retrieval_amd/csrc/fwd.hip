@@ -14,11 +14,13 @@
 //     next tile's global loads (possibly of the next document) in flight while
 //     the current one is contracted.  LDS rows are XOR-swizzled by 16-byte
 //     chunk so the MFMA operand reads are bank-conflict free.
-//   * S_t = D_tile Q_slab^T is formed 16 doc tokens x 16 query rows at a time
-//     with v_mfma_f32_16x16x32_{f16,bf16} (int8: v_mfma_i32_16x16x64_i8),
-//     fp32 (int32) accumulation.  Doc tokens are the M dimension, so each lane
-//     holds 4 tokens of one query row and the running max / argmax stays in
-//     the lane; lanes are merged once per document (two xor shuffles).
+//   * S_t = D_tile Q_slab^T is formed M doc tokens x M query rows at a time.
+//     fp16/bf16 use v_mfma_f32_32x32x16 (M = 32: four independent accumulation
+//     chains per wave keep the matrix pipe full, where 16x16 tiles would need
+//     twice as many); int8 uses v_mfma_i32_16x16x64_i8 (M = 16).  Doc tokens are
+//     the M dimension of the result, so each lane holds VPL tokens of one query
+//     row and the running max / argmax stays in the lane; lanes are merged once
+//     per document.
 //   * The grid is persistent: block -> (slab, document stream) is laid out so
 //     the workgroups sharing a document stream sit on the same XCD (blocks are
 //     dispatched round-robin over the 8 XCDs) and re-read each tile from that
@@ -27,6 +29,8 @@
 //     before the maximum; tokens past the end are never loaded.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace maxsim {
@@ -34,6 +38,7 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -47,89 +52,190 @@ struct FwdParams {
     const float* d_scale;
     int64_t T;
     int Nq, Lq, B, Ld;
-    int qps;          // queries per slab
+    int qps;          // queries per slab (whole queries), or 1 when split
+    int split;        // 1: slabs hold whole queries; 2: each query is two half slabs
+    int half_rows;    // rows of the first half of a split query
     int num_slabs;
     int num_streams;  // documents b = stream, stream + num_streams, ...
     float* scores;
     int32_t* argmax;
 };
 
-template <int ELEM>
-__device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
-    if constexpr (ELEM == kF16) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    } else {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-}
+// One M x M block of S = D_tile Q^T contracted over the 128-wide embedding.
+// Lane l supplies row (l % M) of each operand and one 16-byte chunk of it per
+// k-step; NG = 64 / M lane groups (g = l / M) split the k range.  The result
+// holds VPL = M*M/64 values per lane: column (query row) l % M and the doc
+// tokens tok(g, i), i < VPL.
+template <int ELEM, int M>
+struct Mma;
 
-__device__ __forceinline__ i32x4 mma16_i8(u32x4 a, u32x4 b, i32x4 c) {
-    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
-                                                 __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
-}
+template <int ELEM>
+struct Mma<ELEM, 16> {  // v_mfma_f32_16x16x32_{f16,bf16}: 8 halves/lane/step, 4 steps
+    static constexpr int NG = 4, VPL = 4, KS = 4;
+    typedef f32x4 Acc;
+    __device__ static __forceinline__ Acc zero() { return Acc{0.f, 0.f, 0.f, 0.f}; }
+    __device__ static __forceinline__ Acc mma(u32x4 a, u32x4 b, Acc c) {
+        if constexpr (ELEM == kF16) {
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                          __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+        } else {
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                           __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+        }
+    }
+    __device__ static __forceinline__ int tok(int g, int i) { return 4 * g + i; }
+};
+
+template <int ELEM>
+struct Mma<ELEM, 32> {  // v_mfma_f32_32x32x16_{f16,bf16}: 8 halves/lane/step, 8 steps
+    static constexpr int NG = 2, VPL = 16, KS = 8;
+    typedef f32x16 Acc;
+    __device__ static __forceinline__ Acc zero() {
+        Acc z;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = 0.f;
+        return z;
+    }
+    __device__ static __forceinline__ Acc mma(u32x4 a, u32x4 b, Acc c) {
+        if constexpr (ELEM == kF16) {
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                          __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+        } else {
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                           __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+        }
+    }
+    __device__ static __forceinline__ int tok(int g, int i) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+};
+
+template <>
+struct Mma<kI8, 16> {  // v_mfma_i32_16x16x64_i8: 16 bytes/lane/step, 2 steps
+    static constexpr int NG = 4, VPL = 4, KS = 2;
+    typedef i32x4 Acc;
+    __device__ static __forceinline__ Acc zero() { return Acc{0, 0, 0, 0}; }
+    __device__ static __forceinline__ Acc mma(u32x4 a, u32x4 b, Acc c) {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                                     __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ int tok(int g, int i) { return 4 * g + i; }
+};
 
 // LDS slot (in 16-byte units) of chunk c of tile row `row`.  fp16/bf16 rows are
 // 256 B = 16 chunks (one full bank sweep): chunk ^ (row & 15).  int8 rows are
-// 128 B = 8 chunks, two rows per sweep: chunk ^ ((row >> 1) & 7).  Either way
-// the 16 rows read by one 16-lane group land on 16 distinct 16-byte bank groups.
+// 128 B = 8 chunks, two rows per sweep: chunk ^ ((row >> 1) & 7).  Any 8 or 16
+// consecutive rows read at one logical chunk land on distinct bank groups.  The
+// map is its own inverse within a row, which the loader uses: the lane that
+// fills slot s fetches chunk (s % NCH) ^ f(row) of row s / NCH.
 template <int NCH>
-__device__ __forceinline__ int swz(int row, int c) {
+__device__ __forceinline__ int swz_chunk(int row, int c) {
     if constexpr (NCH == 16) {
-        return row * 16 + (c ^ (row & 15));
+        return c ^ (row & 15);
     } else {
-        return row * 8 + (c ^ ((row >> 1) & 7));
+        return c ^ ((row >> 1) & 7);
     }
 }
+template <int NCH>
+__device__ __forceinline__ int swz(int row, int c) {
+    return row * NCH + swz_chunk<NCH>(row, c);
+}
+
+// s_waitcnt vmcnt(N) (other counters untouched), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;  // read-only for the kernel: scalar loads
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also orders global
+// memory, which makes every wave drain its in-flight HBM -> LDS loads
+// (vmcnt(0)) at each barrier and would serialise the tile ring.  Here each wave
+// waits for its own LDS reads/writes (lgkmcnt(0)) and the ring's direct loads
+// are retired explicitly (wait_vmcnt) before the barrier; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Row r of the per-document row maxima lives at r + r/32, so threads reading
+// the rows of consecutive queries (stride Lq) do not all hit one bank.
+__device__ __forceinline__ int rpad(int r) { return r + (r >> 5); }
 
 template <bool VARLEN>
 __device__ __forceinline__ void doc_info(const FwdParams& p, int b, int64_t& start, int& len) {
     if constexpr (VARLEN) {
-        int64_t s0 = p.cu[b];
-        int64_t s1 = p.cu[b + 1];
+        const cint_ptr cu = (cint_ptr)p.cu;
+        int64_t s0 = cu[b];
+        int64_t s1 = cu[b + 1];
         s0 = s0 < 0 ? 0 : (s0 > p.T ? p.T : s0);
         s1 = s1 < s0 ? s0 : (s1 > p.T ? p.T : s1);
         start = s0;
         len = (int)(s1 - s0);
     } else {
         start = (int64_t)b * p.Ld;
-        int l = p.lens ? p.lens[b] : p.Ld;
+        int l = p.lens ? ((cint_ptr)p.lens)[b] : p.Ld;
         len = l < 0 ? 0 : (l > p.Ld ? p.Ld : l);
     }
 }
 
-// ELEM: kF16 / kBF16 / kI8.  QB: 16-row query blocks per wave.  WQ x WT waves:
-// WQ along query rows, WT along document tokens.  SPW: 16-token sub-tiles each
-// wave contracts per tile.  ARGMAX: also track and write the argmax.
-template <int ELEM, int QB, int WQ, int WT, int SPW, bool ARGMAX, bool VARLEN>
+__device__ __forceinline__ unsigned fbits(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ float bitsf(unsigned x) { return __uint_as_float(x); }
+
+// ELEM: kF16 / kBF16 / kI8.  M: MFMA block edge (16 or 32).  QB: M-row query
+// blocks per wave.  WQ x WT waves: WQ along query rows, WT along document
+// tokens.  SPW: M-token sub-tiles each wave contracts per tile.  ARGMAX: also
+// track and write the argmax.
+template <int ELEM, int M, int QB, int WQ, int WT, int SPW, bool ARGMAX, bool VARLEN>
 __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
+    using MM = Mma<ELEM, M>;
+    using Acc = typename MM::Acc;
     constexpr bool I8 = ELEM == kI8;
+    constexpr int NG = MM::NG, VPL = MM::VPL, KS = MM::KS;
     constexpr int NW = WQ * WT;
     constexpr int NT = 64 * NW;
     constexpr int ROWB = I8 ? 128 : 256;  // bytes per token row
     constexpr int NCH = ROWB / 16;        // 16-byte chunks per row
-    constexpr int KS = NCH / 4;           // MFMA k-steps per row
-    constexpr int SUBS = SPW * WT;        // 16-token sub-tiles per tile
-    constexpr int TT = 16 * SUBS;         // tokens per tile
-    constexpr int R = WQ * QB * 16;       // slab capacity in query-token rows
-    constexpr int LPT = TT * NCH / NT;    // 16-byte loads per thread per tile
-    static_assert(LPT * NT == TT * NCH, "tile must split evenly over the workgroup");
+    static_assert(NCH == NG * KS, "each lane group covers KS chunks");
+    constexpr int SUBS = SPW * WT;        // M-token sub-tiles per tile
+    constexpr int TT = M * SUBS;          // tokens per tile
+    constexpr int R = WQ * QB * M;        // slab capacity in query-token rows
+    constexpr int RP = R + R / 32;        // padded row-maximum storage
+    // fp16/bf16 with 32x32 blocks track the argmax with a packed key: the low
+    // KB mantissa bits of each similarity are replaced by its position in the
+    // lane (earlier positions get larger codes), so one max over the keys gives
+    // both a maximum (to within 2^KB ulp) and where it sits.  The exact maximum
+    // is kept separately.  int8 (bit-exact) and 16x16 blocks compare exactly.
+    constexpr bool KEYED = ARGMAX && !I8 && M == 32;
+    constexpr unsigned KMASK = VPL - 1;
 
-    __shared__ u32x4 dtile[2][TT * NCH];
-    __shared__ float dsc[I8 ? 2 : 1][I8 ? TT : 1];
-    __shared__ float rowmax_s[R];
+    // Three-stage ring: tile k is contracted while tiles k+1 and k+2 are in flight.
+    constexpr int NBUF = 3;
+    constexpr int LPW = TT * NCH / (64 * NW);  // 1 KB direct loads per wave per tile
+    static_assert(LPW * 64 * NW == TT * NCH, "tile must split into whole 1 KB loads per wave");
+    static_assert(!I8 || TT % 64 == 0, "int8 scales load 64 at a time");
+    constexpr int SCW = I8 ? TT / 64 : 0;     // waves that also load 64 scales each
+    static_assert(SCW <= NW, "scale loads need enough waves");
+    __shared__ u32x4 dtile[NBUF][TT * NCH];
+    __shared__ __attribute__((aligned(16))) float dsc[I8 ? NBUF : 1][I8 ? TT : 4];
+    __shared__ float rowmax_s[RP];
+    __shared__ float qsc_s[I8 ? R : 1];  // int8: the slab's query scales
     __shared__ int rowarg_s[ARGMAX ? R : 1];
     __shared__ float xm[WT > 1 ? WT : 1][WT > 1 ? R : 1];
     __shared__ int xi[(WT > 1 && ARGMAX) ? WT : 1][(WT > 1 && ARGMAX) ? R : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets branches on it stay scalar
     const int wq = wave % WQ;
     const int wt = wave / WQ;
-    const int g = lane >> 4;    // lane group: k-chunk of the operands, token quad of the result
-    const int l16 = lane & 15;  // operand row / result column
+    const int g = lane / M;    // lane group: k-chunks of the operands, token set of the result
+    const int lm = lane % M;   // operand row / result column
 
     const int blk = blockIdx.x;
     const int xcd = blk & 7;
@@ -137,132 +243,198 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     const int slab = jx % p.num_slabs;
     const int stream = (jx / p.num_slabs) * 8 + xcd;
     if (stream >= p.num_streams || stream >= p.B) return;  // uniform over the workgroup
-    const int q0 = slab * p.qps;
-    const int nq = min(p.qps, p.Nq - q0);
-    const int nrows = nq * p.Lq;
     const int Lq = p.Lq;
+    // The slab is nq queries x ni of their rows, starting at row i0 of each:
+    // whole queries (i0 = 0, ni = Lq) or one half of a split query.  Its rows
+    // are contiguous in Q from row q0*Lq + i0.
+    int q0, nq, i0, ni;
+    if (p.split == 1) {
+        q0 = slab * p.qps;
+        nq = min(p.qps, p.Nq - q0);
+        i0 = 0;
+        ni = Lq;
+    } else {
+        q0 = slab >> 1;
+        nq = 1;
+        i0 = (slab & 1) ? p.half_rows : 0;
+        ni = (slab & 1) ? Lq - p.half_rows : p.half_rows;
+    }
+    const int nrows = nq * ni;
+    const int64_t qrow0 = (int64_t)q0 * Lq + i0;
 
-    // Query slab -> VGPRs.  Lane (g, l16) of block cb holds row (wq*QB+cb)*16+l16,
-    // chunks g, g+4, g+8, g+12 (k-step s uses chunk g + 4s; the document operand
-    // uses the same chunk map, so every k meets its partner exactly once).
+    // Query slab -> VGPRs.  Lane (g, lm) of block cb holds row (wq*QB+cb)*M+lm,
+    // chunks g*KS .. g*KS+KS-1 (k-step s uses chunk g*KS + s; the document
+    // operand uses the same chunk map, so every k meets its partner once).
     u32x4 bq[QB][KS];
 #pragma unroll
     for (int cb = 0; cb < QB; ++cb) {
-        const int r = (wq * QB + cb) * 16 + l16;
+        const int r = (wq * QB + cb) * M + lm;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             if (r < nrows) {
-                bq[cb][s] = *reinterpret_cast<const u32x4*>(
-                    p.Q + ((int64_t)q0 * Lq + r) * ROWB + (g + 4 * s) * 16);
+                bq[cb][s] = *reinterpret_cast<const u32x4*>(p.Q + (qrow0 + r) * ROWB + (g * KS + s) * 16);
             } else {
                 bq[cb][s] = u32x4{0u, 0u, 0u, 0u};
             }
         }
     }
 
-    float m[QB];
-    int code[QB];  // (global 16-token sub-tile << 2) | row within the lane's token quad
+    if constexpr (I8) {
+        for (int r = tid; r < nrows; r += NT) qsc_s[r] = p.q_scale[qrow0 + r];
+    }
+
+    float m[QB];       // running exact maximum per lane and query block
+    int code[QB];      // exact path: (global sub-tile << 4) | value slot; keyed path: sub-tile
+    float km[QB];      // keyed path: running maximum key
 #pragma unroll
     for (int cb = 0; cb < QB; ++cb) {
         m[cb] = -INFINITY;
+        km[cb] = -INFINITY;
         code[cb] = -1;
     }
 
-    u32x4 pre[LPT];
-    float pres = 0.f;
-
-    auto load_tile = [&](int64_t st, int ln, int tt) {
+    // Direct HBM -> LDS loads of one tile into ring slot bf.  Every wave issues
+    // exactly LPW (+1 for the scale waves) loads, so vmcnt bookkeeping is
+    // static; lanes whose token is past the document's end fetch a clamped
+    // in-bounds row instead, and the compute masks those tokens.
+    const bool scale_wave = I8 && wave < SCW;
+    auto issue_tile = [&](int bf, int64_t st, int ln, int tt) {
+        const int64_t safe = ln > 0 ? st : 0;
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int ci = tid + u * NT;
-            const int row = ci / NCH;
-            const int c = ci % NCH;
-            const int tok = tt * TT + row;
-            if (tok < ln) {
-                pre[u] = *reinterpret_cast<const u32x4*>(p.D + (st + tok) * ROWB + c * 16);
-            } else {
-                pre[u] = u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int u = 0; u < LPW; ++u) {
+            const int slot0 = (u * NW + wave) * 64;
+            const int sl = slot0 + lane;
+            const int row = sl / NCH;
+            const int c = swz_chunk<NCH>(row, sl % NCH);
+            const int tk = tt * TT + row;
+            const int64_t grow = tk < ln ? st + tk : safe;
+            __builtin_amdgcn_global_load_lds((gptr_t)(p.D + grow * ROWB + c * 16), (lptr_t)&dtile[bf][slot0], 16, 0, 0);
         }
         if constexpr (I8) {
-            if (tid < TT) {
-                const int tok = tt * TT + tid;
-                pres = tok < ln ? p.d_scale[st + tok] : 0.f;
+            if (scale_wave) {
+                const int tk = tt * TT + wave * 64 + lane;
+                const int64_t grow = tk < ln ? st + tk : safe;
+                __builtin_amdgcn_global_load_lds((gptr_t)(p.d_scale + grow), (lptr_t)&dsc[bf][wave * 64], 4, 0, 0);
             }
         }
     };
-    auto store_tile = [&](int bf) {
-#pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int ci = tid + u * NT;
-            dtile[bf][swz<NCH>(ci / NCH, ci % NCH)] = pre[u];
+    // Wait until only the most recent tile's loads may still be in flight.
+    // Vector-memory loads complete in issue order, so this retires every older
+    // load (and the epilogue's stores issued before them).
+    auto wait_all_but_last_tile = [&]() {
+        if (scale_wave) {
+            wait_vmcnt<LPW + 1>();
+        } else {
+            wait_vmcnt<LPW>();
         }
+    };
+
+    // One M-token sub-tile against the wave's QB query blocks.  MASK: some of
+    // the M tokens lie past the document's end (only the last sub-tile).
+    // Query rows past the slab's end hold zeros; their results are never read.
+    auto subtile = [&](auto mask_tag, int bf, int sb, int tok0, int ln, int gsub) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        float v[QB][VPL];
         if constexpr (I8) {
-            if (tid < TT) dsc[bf][tid] = pres;
+            const f32x4 sc = *reinterpret_cast<const f32x4*>(&dsc[bf][sb * M + 4 * g]);
+            u32x4 a[KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) a[s] = dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
+#pragma unroll
+            for (int cb = 0; cb < QB; ++cb) {
+                Acc acc = MM::zero();
+#pragma unroll
+                for (int s = 0; s < KS; ++s) acc = MM::mma(a[s], bq[cb][s], acc);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) v[cb][i] = (float)acc[i] * sc[i];
+            }
+        } else {
+            Acc acc[QB];
+#pragma unroll
+            for (int cb = 0; cb < QB; ++cb) acc[cb] = MM::zero();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u32x4 a = dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
+#pragma unroll
+                for (int cb = 0; cb < QB; ++cb) acc[cb] = MM::mma(a, bq[cb][s], acc[cb]);
+            }
+#pragma unroll
+            for (int cb = 0; cb < QB; ++cb)
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) v[cb][i] = acc[cb][i];
+        }
+#pragma unroll
+        for (int cb = 0; cb < QB; ++cb) {
+            bool valid[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                valid[i] = !MASK || (tok0 + MM::tok(g, i) < ln);
+                if (!valid[i]) v[cb][i] = -INFINITY;
+            }
+            if constexpr (KEYED) {
+                float mx = m[cb];
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) mx = fmaxf(mx, v[cb][i]);
+                m[cb] = mx;
+                float kt = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const unsigned key = (fbits(v[cb][i]) & ~KMASK) | (KMASK - i);
+                    kt = fmaxf(kt, valid[i] ? bitsf(key) : -INFINITY);
+                }
+                if (kt > km[cb]) {  // strict: the earlier sub-tile keeps a tie
+                    km[cb] = kt;
+                    code[cb] = gsub;
+                }
+            } else if constexpr (ARGMAX) {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    if (v[cb][i] > m[cb]) {  // strict: the earliest token keeps a tie
+                        m[cb] = v[cb][i];
+                        code[cb] = (gsub << 4) | i;
+                    }
+                }
+            } else {
+                float mx = m[cb];
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) mx = fmaxf(mx, v[cb][i]);
+                m[cb] = mx;
+            }
         }
     };
 
     auto compute_tile = [&](int bf, int tt, int ln) {
+        if (wq * QB * M >= nrows) return;  // uniform: this wave's rows are all past the slab
 #pragma unroll
         for (int k = 0; k < SPW; ++k) {
             const int sb = wt * SPW + k;
-            const int tok0 = tt * TT + sb * 16;
+            const int tok0 = tt * TT + sb * M;
             if (tok0 >= ln) break;  // uniform
-            u32x4 a[KS];
-#pragma unroll
-            for (int s = 0; s < KS; ++s) a[s] = dtile[bf][swz<NCH>(sb * 16 + l16, g + 4 * s)];
-            f32x4 sc;
-            if constexpr (I8) sc = *reinterpret_cast<const f32x4*>(&dsc[bf][sb * 16 + 4 * g]);
-            const bool full = tok0 + 16 <= ln;
-            const int cbase = (tt * SUBS + sb) << 2;
-#pragma unroll
-            for (int cb = 0; cb < QB; ++cb) {
-                if ((wq * QB + cb) * 16 >= nrows) break;  // uniform: rest of the slab is empty
-                float v[4];
-                if constexpr (I8) {
-                    i32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) acc = mma16_i8(a[s], bq[cb][s], acc);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] = (float)acc[r] * sc[r];
-                } else {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) acc = mma16<ELEM>(a[s], bq[cb][s], acc);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] = acc[r];
-                }
-                if (!full) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (tok0 + 4 * g + r >= ln) v[r] = -INFINITY;
-                }
-                if constexpr (ARGMAX) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (v[r] > m[cb]) {  // strict: the earliest token keeps a tie
-                            m[cb] = v[r];
-                            code[cb] = cbase | r;
-                        }
-                    }
-                } else {
-                    m[cb] = fmaxf(m[cb], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-                }
+            const int gsub = tt * SUBS + sb;
+            if (tok0 + M <= ln) {
+                subtile(std::false_type{}, bf, sb, tok0, ln, gsub);
+            } else {
+                subtile(std::true_type{}, bf, sb, tok0, ln, gsub);
             }
         }
     };
 
     auto epilogue = [&](int b) {
-        // Merge the four token quads of every query row (lanes l, l^16, l^32, l^48).
+        // Merge the NG token sets of every query row (lanes lm + M*g).
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb) {
             float mv = m[cb];
             int idx = -1;
-            if constexpr (ARGMAX) {
-                if (code[cb] >= 0) idx = 16 * (code[cb] >> 2) + 4 * g + (code[cb] & 3);
+            if constexpr (KEYED) {
+                if (code[cb] >= 0) {
+                    const int i = (int)(KMASK - (fbits(km[cb]) & KMASK));
+                    idx = M * code[cb] + MM::tok(g, i);
+                }
+            } else if constexpr (ARGMAX) {
+                if (code[cb] >= 0) idx = M * (code[cb] >> 4) + MM::tok(g, code[cb] & 15);
             }
 #pragma unroll
-            for (int off = 16; off <= 32; off <<= 1) {
+            for (int off = M; off < 64; off <<= 1) {
                 const float om = __shfl_xor(mv, off);
                 if constexpr (ARGMAX) {
                     const int oi = __shfl_xor(idx, off);
@@ -274,10 +446,10 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                     mv = fmaxf(mv, om);
                 }
             }
-            const int r = (wq * QB + cb) * 16 + l16;
-            if (g == 0 && r < R) {
+            const int r = (wq * QB + cb) * M + lm;
+            if (g == 0) {
                 if constexpr (WT == 1) {
-                    rowmax_s[r] = mv;
+                    rowmax_s[rpad(r)] = mv;
                     if constexpr (ARGMAX) rowarg_s[r] = idx;
                 } else {
                     xm[wt][r] = mv;
@@ -285,9 +457,10 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                 }
             }
             m[cb] = -INFINITY;
+            km[cb] = -INFINITY;
             code[cb] = -1;
         }
-        __syncthreads();
+        lds_barrier();
         if constexpr (WT > 1) {
             for (int r = tid; r < R; r += NT) {
                 float mv = xm[0][r];
@@ -306,90 +479,129 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                         mv = fmaxf(mv, om);
                     }
                 }
-                rowmax_s[r] = mv;
+                rowmax_s[rpad(r)] = mv;
                 if constexpr (ARGMAX) rowarg_s[r] = idx;
             }
-            __syncthreads();
+            lds_barrier();
         }
         if constexpr (ARGMAX) {
             for (int r = tid; r < nrows; r += NT) {
-                const int ql = r / Lq;
-                const int i = r - ql * Lq;
+                const int ql = r / ni;
+                const int i = i0 + r - ql * ni;
                 p.argmax[((int64_t)(q0 + ql) * p.B + b) * Lq + i] = rowarg_s[r];
             }
         }
         if constexpr (I8) {
             // Exact epilogue: v_i = fl32(m_i * q_scale_i), summed in ascending i.
             for (int ql = tid; ql < nq; ql += NT) {
-                const float* qs = p.q_scale + (int64_t)(q0 + ql) * Lq;
-                const float* rm = rowmax_s + ql * Lq;
                 float acc = 0.f;
-                for (int i = 0; i < Lq; ++i) {
-                    const float v = rm[i] * qs[i];
+                for (int i = 0; i < ni; ++i) {
+                    const float v = rowmax_s[rpad(ql * ni + i)] * qsc_s[ql * ni + i];
                     acc = acc + v;
                 }
                 p.scores[(int64_t)(q0 + ql) * p.B + b] = acc;
             }
-        } else if (Lq < 64) {
-            for (int ql = tid; ql < nq; ql += NT) {
-                const float* rm = rowmax_s + ql * Lq;
-                float acc = 0.f;
-                for (int i = 0; i < Lq; ++i) acc += rm[i];
-                p.scores[(int64_t)(q0 + ql) * p.B + b] = acc;
-            }
         } else {
-            for (int ql = wave; ql < nq; ql += NW) {
-                const float* rm = rowmax_s + ql * Lq;
+            // P lanes per query (P = ni rounded up to a power of two, at most 64),
+            // 64 / P queries per wave pass, butterfly sum inside each lane group.
+            // A split query's two halves each add their partial sum to the
+            // zero-filled score: two addends, so the result does not depend on
+            // which lands first.
+            int P = 1;
+            while (P < ni && P < 64) P <<= 1;
+            const int qpw = 64 / P;
+            const int sub = lane / P, pl = lane % P;
+            for (int ql0 = wave * qpw; ql0 < nq; ql0 += NW * qpw) {
+                const int ql = ql0 + sub;
                 float acc = 0.f;
-                for (int i = lane; i < Lq; i += 64) acc += rm[i];
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-                if (lane == 0) p.scores[(int64_t)(q0 + ql) * p.B + b] = acc;
+                if (ql < nq)
+                    for (int i = pl; i < ni; i += P) acc += rowmax_s[rpad(ql * ni + i)];
+                for (int off = 1; off < P; off <<= 1) acc += __shfl_xor(acc, off);
+                if (pl == 0 && ql < nq) {
+                    float* dst = p.scores + (int64_t)(q0 + ql) * p.B + b;
+                    if (p.split == 1) {
+                        *dst = acc;
+                    } else {
+                        atomicAdd(dst, acc);
+                    }
+                }
             }
         }
     };
 
-    // Persistent walk over this workgroup's documents, one tile per step.
-    int b = stream;
-    int64_t start;
-    int len;
-    doc_info<VARLEN>(p, b, start, len);
-    int ntiles = (len + TT - 1) / TT;
-    int t = 0;
-    load_tile(start, len, 0);
-    store_tile(0);
-    __syncthreads();
+    // Persistent walk over this workgroup's documents, one tile per step, with
+    // a look-ahead of two tiles (possibly in later documents).
+    struct Cur {
+        int b, t, len, ntiles;
+        int64_t start;
+    };
+    auto at_doc = [&](int b) {
+        Cur c;
+        c.b = b;
+        c.t = 0;
+        c.start = 0;
+        c.len = 0;
+        c.ntiles = 0;
+        if (b < p.B) {
+            doc_info<VARLEN>(p, b, c.start, c.len);
+            c.ntiles = (c.len + TT - 1) / TT;
+        }
+        return c;
+    };
+    auto advance = [&](const Cur& c) {
+        if (c.t + 1 < c.ntiles) {
+            Cur n = c;
+            n.t += 1;
+            return n;
+        }
+        return at_doc(c.b + p.num_streams);
+    };
+    // nothing to read at all: every document is empty and D may be absent
+    const bool loads = p.T > 0;
+
+    Cur c0 = at_doc(stream);
+    Cur c1 = advance(c0);
+    if (loads) {
+        issue_tile(0, c0.start, c0.len, c0.t);
+        if (c1.b < p.B) {
+            issue_tile(1, c1.start, c1.len, c1.t);
+            wait_all_but_last_tile();
+        } else {
+            wait_vmcnt<0>();
+        }
+    }
+    lds_barrier();
     int buf = 0;
     while (true) {
-        int nb = b, nt = t + 1, nlen = len, nntiles = ntiles;
-        int64_t nstart = start;
-        if (nt >= ntiles) {
-            nb = b + p.num_streams;
-            nt = 0;
-            if (nb < p.B) {
-                doc_info<VARLEN>(p, nb, nstart, nlen);
-                nntiles = (nlen + TT - 1) / TT;
+        const bool has1 = c1.b < p.B;
+        Cur c2 = has1 ? advance(c1) : c1;
+        const bool has2 = has1 && c2.b < p.B;
+        if (c0.t < c0.ntiles) compute_tile(buf, c0.t, c0.len);
+        if (c0.t + 1 >= c0.ntiles) epilogue(c0.b);
+        if (loads) {
+            if (has2) {
+                issue_tile(buf == 0 ? 2 : buf - 1, c2.start, c2.len, c2.t);
+                wait_all_but_last_tile();
+            } else {
+                wait_vmcnt<0>();
             }
         }
-        const bool has_next = nb < p.B;
-        if (has_next) load_tile(nstart, nlen, nt);
-        if (t < ntiles) compute_tile(buf, t, len);
-        if (t + 1 >= ntiles) epilogue(b);
-        if (has_next) store_tile(buf ^ 1);
-        __syncthreads();
-        if (!has_next) break;
-        buf ^= 1;
-        b = nb;
-        t = nt;
-        start = nstart;
-        len = nlen;
-        ntiles = nntiles;
+        lds_barrier();
+        if (!has1) break;
+        buf = buf == 2 ? 0 : buf + 1;
+        c0 = c1;
+        c1 = c2;
     }
 }
 
-template <int ELEM, int QB, int WQ, int WT, int SPW, bool ARGMAX, bool VARLEN>
+__global__ __launch_bounds__(256) void zero_fill(float* x, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) x[i] = 0.f;
+}
+
+template <int ELEM, int M, int QB, int WQ, int WT, int SPW, bool ARGMAX, bool VARLEN>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream, int target_blocks) {
-    constexpr int R = WQ * QB * 16;
+    constexpr int R = WQ * QB * M;
     FwdParams p;
     p.Q = static_cast<const char*>(a.Q);
     p.D = static_cast<const char*>(a.D);
@@ -402,18 +614,35 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream, int target_blocks) {
     p.Lq = a.Lq;
     p.B = a.B;
     p.Ld = a.Ld;
-    p.qps = R / a.Lq;
-    if (p.qps > a.Nq) p.qps = a.Nq;
-    p.num_slabs = (a.Nq + p.qps - 1) / p.qps;
-    int streams = (target_blocks + p.num_slabs - 1) / p.num_slabs;
+    if (a.Lq <= R) {
+        p.split = 1;
+        p.half_rows = a.Lq;
+        p.qps = R / a.Lq;
+        if (p.qps > a.Nq) p.qps = a.Nq;
+        p.num_slabs = (a.Nq + p.qps - 1) / p.qps;
+    } else {  // a query longer than the slab: two halves (callers ensure Lq <= 2R)
+        p.split = 2;
+        p.half_rows = (a.Lq + 1) / 2;
+        p.qps = 1;
+        p.num_slabs = 2 * a.Nq;
+        hipLaunchKernelGGL(zero_fill, dim3((unsigned)(((int64_t)a.Nq * a.B + 255) / 256)), dim3(256), 0, stream,
+                           a.scores, (int64_t)a.Nq * a.B);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // blocks = 8 * num_slabs * s8 (the XCD-aware map needs whole groups of 8):
+    // as many stream groups as fit in one round of target_blocks, at least one,
+    // and no more streams than documents.
+    int s8 = target_blocks / (8 * p.num_slabs);
+    if (s8 < 1) s8 = 1;
+    if (s8 > (a.B + 7) / 8) s8 = (a.B + 7) / 8;
+    int streams = 8 * s8;
     if (streams > a.B) streams = a.B;
-    if (streams < 1) streams = 1;
     p.num_streams = streams;
     p.scores = a.scores;
     p.argmax = a.argmax;
-    const int s8 = (streams + 7) / 8;
     const long long blocks = 8LL * p.num_slabs * s8;
-    hipLaunchKernelGGL((fwd_kernel<ELEM, QB, WQ, WT, SPW, ARGMAX, VARLEN>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((fwd_kernel<ELEM, M, QB, WQ, WT, SPW, ARGMAX, VARLEN>), dim3((unsigned)blocks),
                        dim3(64 * WQ * WT), 0, stream, p);
     return hipGetLastError();
 }
@@ -423,10 +652,21 @@ hipError_t dispatch_shape(const FwdArgs& a, hipStream_t stream) {
     // Few query rows in all (single-query reranking): one 32-row slab, four
     // waves split each document's tokens; many small workgroups fill the chip.
     if ((int64_t)a.Nq * a.Lq <= 32) {
-        return launch_cfg<ELEM, 2, 1, 4, 1, ARGMAX, VARLEN>(a, stream, 2048);
+        return launch_cfg<ELEM, 16, 2, 1, 4, 1, ARGMAX, VARLEN>(a, stream, 2048);
     }
-    // Otherwise a 1024-row slab held by 8 waves, one persistent workgroup per CU.
-    return launch_cfg<ELEM, 8, 8, 1, 4, ARGMAX, VARLEN>(a, stream, 256);
+    // Otherwise one persistent workgroup per CU holding a slab of query rows.
+    if constexpr (ELEM == kI8) {
+        // 1024 rows: 8 waves x 128 rows, 16x16x64 int8 blocks
+        return launch_cfg<ELEM, 16, 8, 8, 1, 4, ARGMAX, VARLEN>(a, stream, 256);
+    } else {
+        if (a.Lq > 512 && a.Lq <= 768) {
+            // 768-row slabs of whole queries: 8 waves x 96 rows, 2 waves per SIMD
+            return launch_cfg<ELEM, 32, 3, 8, 1, 2, ARGMAX, VARLEN>(a, stream, 256);
+        }
+        // 512-row slabs (whole queries up to 512 tokens, else two halves of a
+        // query): 8 waves x 64 rows
+        return launch_cfg<ELEM, 32, 2, 8, 1, 2, ARGMAX, VARLEN>(a, stream, 256);
+    }
 }
 
 template <int ELEM, bool VARLEN>

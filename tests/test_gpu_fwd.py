@@ -113,7 +113,9 @@ def test_padding_never_selected_all_negative(bd):
     s, a = run_padded(bd, Q, D, inputs.F16, lens)
     s_ref, a_ref = oracle.fwd_padded(Q, D, oracle.F16, d_lens=lens)
     check_scores(s, s_ref, 40, "all-negative")
-    assert np.all(a[:, 0] == 0) and np.all(a[:, 1] == 17) and np.all(a[:, 2] == -1)
+    # document 0: every valid token ties, any of them is a correct argmax
+    assert np.all((a[:, 0] >= 0) & (a[:, 0] < 50))
+    assert np.all(a[:, 1] == 17) and np.all(a[:, 2] == -1)
     assert np.all(np.isneginf(s[:, 2]))
 
 
