@@ -10,9 +10,10 @@
 //     keeps it stationary in VGPRs as the MFMA B operand for its whole life.
 //     This is the query-reuse member of the page's kernel family (Section 4.1
 //     "Kernel Family"): every document tile it reads is used against all R rows.
-//   * Documents stream HBM -> LDS in tiles of 64 tokens, double-buffered, the
-//     next tile's global loads (possibly of the next document) in flight while
-//     the current one is contracted.  LDS rows are XOR-swizzled by 16-byte
+//   * Documents stream HBM -> LDS in tiles of 128 tokens (64 for the small
+//     single-query configuration) through a three-stage ring of direct
+//     (global_load_lds) loads: the tiles two steps ahead, possibly of later
+//     documents, are in flight while the current one is contracted.  LDS rows are XOR-swizzled by 16-byte
 //     chunk so the MFMA operand reads are bank-conflict free.
 //   * S_t = D_tile Q_slab^T is formed M doc tokens x M query rows at a time.
 //     fp16/bf16 use v_mfma_f32_32x32x16 (M = 32: four independent accumulation
@@ -189,9 +190,9 @@ __device__ __forceinline__ float bitsf(unsigned x) { return __uint_as_float(x); 
 
 // ELEM: kF16 / kBF16 / kI8.  M: MFMA block edge (16 or 32).  QB: M-row query
 // blocks per wave.  WQ x WT waves: WQ along query rows, WT along document
-// tokens.  SPW: M-token sub-tiles each wave contracts per tile.  ARGMAX: also
-// track and write the argmax.
-template <int ELEM, int M, int QB, int WQ, int WT, int SPW, bool ARGMAX, bool VARLEN>
+// tokens.  SPW: M-token sub-tiles each wave contracts per tile, NSI of them at
+// a time (1 or 2).  ARGMAX: also track and write the argmax.
+template <int ELEM, int M, int QB, int WQ, int WT, int SPW, int NSI, bool ARGMAX, bool VARLEN>
 __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     using MM = Mma<ELEM, M>;
     using Acc = typename MM::Acc;
@@ -223,11 +224,14 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     static_assert(SCW <= NW, "scale loads need enough waves");
     __shared__ u32x4 dtile[NBUF][TT * NCH];
     __shared__ __attribute__((aligned(16))) float dsc[I8 ? NBUF : 1][I8 ? TT : 4];
-    __shared__ float rowmax_s[RP];
+    // Per-document row maxima / argmax of each token-wave, double-buffered by
+    // document parity: a document's rows are written at the end of its last
+    // step and consumed (sums, argmax stores) at the start of the next step,
+    // so the step barrier is the only one.
+    __shared__ float rowmax_s[2][WT][RP];
+    __shared__ int rowarg_s[ARGMAX ? 2 : 1][ARGMAX ? WT : 1][ARGMAX ? R : 1];
     __shared__ float qsc_s[I8 ? R : 1];  // int8: the slab's query scales
-    __shared__ int rowarg_s[ARGMAX ? R : 1];
-    __shared__ float xm[WT > 1 ? WT : 1][WT > 1 ? R : 1];
-    __shared__ int xi[(WT > 1 && ARGMAX) ? WT : 1][(WT > 1 && ARGMAX) ? R : 1];
+    __shared__ int docpf[2][2];          // prefetched document bounds
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -329,98 +333,130 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         }
     };
 
-    // One M-token sub-tile against the wave's QB query blocks.  MASK: some of
-    // the M tokens lie past the document's end (only the last sub-tile).
-    // Query rows past the slab's end hold zeros; their results are never read.
-    auto subtile = [&](auto mask_tag, int bf, int sb, int tok0, int ln, int gsub) {
+    // NS consecutive M-token sub-tiles (starting at sb0) against the wave's QB
+    // query blocks; their NS*QB accumulation chains are interleaved so the
+    // matrix pipe always has independent work.  MASK: some tokens of these
+    // sub-tiles lie past the document's end (only the last sub-tiles).  Query
+    // rows past the slab's end hold zeros; their results are never read.
+    auto subtiles = [&](auto ns_tag, auto mask_tag, int bf, int sb0, int tok0, int ln, int gsub0) {
+        constexpr int NS = decltype(ns_tag)::value;
         constexpr bool MASK = decltype(mask_tag)::value;
-        float v[QB][VPL];
+        float v[NS][QB][VPL];
         if constexpr (I8) {
-            const f32x4 sc = *reinterpret_cast<const f32x4*>(&dsc[bf][sb * M + 4 * g]);
-            u32x4 a[KS];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) a[s] = dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
+            for (int n = 0; n < NS; ++n) {
+                const int sb = sb0 + n;
+                const f32x4 sc = *reinterpret_cast<const f32x4*>(&dsc[bf][sb * M + 4 * g]);
+                u32x4 a[KS];
 #pragma unroll
-            for (int cb = 0; cb < QB; ++cb) {
-                Acc acc = MM::zero();
+                for (int s = 0; s < KS; ++s) a[s] = dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
 #pragma unroll
-                for (int s = 0; s < KS; ++s) acc = MM::mma(a[s], bq[cb][s], acc);
+                for (int cb = 0; cb < QB; ++cb) {
+                    Acc acc = MM::zero();
 #pragma unroll
-                for (int i = 0; i < VPL; ++i) v[cb][i] = (float)acc[i] * sc[i];
+                    for (int s = 0; s < KS; ++s) acc = MM::mma(a[s], bq[cb][s], acc);
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) v[n][cb][i] = (float)acc[i] * sc[i];
+                }
             }
         } else {
-            Acc acc[QB];
+            Acc acc[NS][QB];
 #pragma unroll
-            for (int cb = 0; cb < QB; ++cb) acc[cb] = MM::zero();
+            for (int n = 0; n < NS; ++n)
+#pragma unroll
+                for (int cb = 0; cb < QB; ++cb) acc[n][cb] = MM::zero();
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const u32x4 a = dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
+                u32x4 a[NS];
 #pragma unroll
-                for (int cb = 0; cb < QB; ++cb) acc[cb] = MM::mma(a, bq[cb][s], acc[cb]);
+                for (int n = 0; n < NS; ++n) a[n] = dtile[bf][swz<NCH>((sb0 + n) * M + lm, g * KS + s)];
+#pragma unroll
+                for (int cb = 0; cb < QB; ++cb)
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) acc[n][cb] = MM::mma(a[n], bq[cb][s], acc[n][cb]);
             }
 #pragma unroll
-            for (int cb = 0; cb < QB; ++cb)
+            for (int n = 0; n < NS; ++n)
 #pragma unroll
-                for (int i = 0; i < VPL; ++i) v[cb][i] = acc[cb][i];
+                for (int cb = 0; cb < QB; ++cb)
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) v[n][cb][i] = acc[n][cb][i];
         }
 #pragma unroll
-        for (int cb = 0; cb < QB; ++cb) {
-            bool valid[VPL];
+        for (int n = 0; n < NS; ++n) {
+            const int tk0 = tok0 + n * M;
+            const int gsub = gsub0 + n;
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                valid[i] = !MASK || (tok0 + MM::tok(g, i) < ln);
-                if (!valid[i]) v[cb][i] = -INFINITY;
-            }
-            if constexpr (KEYED) {
-                float mx = m[cb];
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) mx = fmaxf(mx, v[cb][i]);
-                m[cb] = mx;
-                float kt = -INFINITY;
+            for (int cb = 0; cb < QB; ++cb) {
+                bool valid[VPL];
 #pragma unroll
                 for (int i = 0; i < VPL; ++i) {
-                    const unsigned key = (fbits(v[cb][i]) & ~KMASK) | (KMASK - i);
-                    kt = fmaxf(kt, valid[i] ? bitsf(key) : -INFINITY);
+                    valid[i] = !MASK || (tk0 + MM::tok(g, i) < ln);
+                    if (!valid[i]) v[n][cb][i] = -INFINITY;
                 }
-                if (kt > km[cb]) {  // strict: the earlier sub-tile keeps a tie
-                    km[cb] = kt;
-                    code[cb] = gsub;
-                }
-            } else if constexpr (ARGMAX) {
+                if constexpr (KEYED) {
+                    float mx = m[cb];
 #pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    if (v[cb][i] > m[cb]) {  // strict: the earliest token keeps a tie
-                        m[cb] = v[cb][i];
-                        code[cb] = (gsub << 4) | i;
+                    for (int i = 0; i < VPL; ++i) mx = fmaxf(mx, v[n][cb][i]);
+                    m[cb] = mx;
+                    float kt = -INFINITY;
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) {
+                        const unsigned key = (fbits(v[n][cb][i]) & ~KMASK) | (KMASK - i);
+                        kt = fmaxf(kt, valid[i] ? bitsf(key) : -INFINITY);
                     }
-                }
-            } else {
-                float mx = m[cb];
+                    if (kt > km[cb]) {  // strict: the earlier sub-tile keeps a tie
+                        km[cb] = kt;
+                        code[cb] = gsub;
+                    }
+                } else if constexpr (ARGMAX) {
 #pragma unroll
-                for (int i = 0; i < VPL; ++i) mx = fmaxf(mx, v[cb][i]);
-                m[cb] = mx;
+                    for (int i = 0; i < VPL; ++i) {
+                        if (v[n][cb][i] > m[cb]) {  // strict: the earliest token keeps a tie
+                            m[cb] = v[n][cb][i];
+                            code[cb] = (gsub << 4) | i;
+                        }
+                    }
+                } else {
+                    float mx = m[cb];
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) mx = fmaxf(mx, v[n][cb][i]);
+                    m[cb] = mx;
+                }
             }
         }
     };
 
     auto compute_tile = [&](int bf, int tt, int ln) {
         if (wq * QB * M >= nrows) return;  // uniform: this wave's rows are all past the slab
+        const int tok_w = tt * TT + wt * SPW * M;  // first token of this wave's sub-tiles
+        int nsub = (ln - tok_w + M - 1) / M;       // sub-tiles holding at least one valid token
+        nsub = nsub < 0 ? 0 : (nsub > SPW ? SPW : nsub);
 #pragma unroll
-        for (int k = 0; k < SPW; ++k) {
+        for (int k = 0; k < SPW; k += NSI) {
+            if (k >= nsub) break;  // uniform
             const int sb = wt * SPW + k;
-            const int tok0 = tt * TT + sb * M;
-            if (tok0 >= ln) break;  // uniform
+            const int tok0 = tok_w + k * M;
             const int gsub = tt * SUBS + sb;
-            if (tok0 + M <= ln) {
-                subtile(std::false_type{}, bf, sb, tok0, ln, gsub);
+            if (NSI == 2 && k + 1 < nsub) {
+                if (tok0 + 2 * M <= ln) {
+                    subtiles(std::integral_constant<int, 2>{}, std::false_type{}, bf, sb, tok0, ln, gsub);
+                } else {
+                    subtiles(std::integral_constant<int, 2>{}, std::true_type{}, bf, sb, tok0, ln, gsub);
+                }
             } else {
-                subtile(std::true_type{}, bf, sb, tok0, ln, gsub);
+                if (tok0 + M <= ln) {
+                    subtiles(std::integral_constant<int, 1>{}, std::false_type{}, bf, sb, tok0, ln, gsub);
+                } else {
+                    subtiles(std::integral_constant<int, 1>{}, std::true_type{}, bf, sb, tok0, ln, gsub);
+                }
             }
         }
     };
 
-    auto epilogue = [&](int b) {
-        // Merge the NG token sets of every query row (lanes lm + M*g).
+    // End of a document, part 1 (before the step barrier): merge the NG token
+    // sets of every query row (lanes lm + M*g) and park the row results.
+    auto epilogue_merge = [&](int par) {
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb) {
             float mv = m[cb];
@@ -448,47 +484,45 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             }
             const int r = (wq * QB + cb) * M + lm;
             if (g == 0) {
-                if constexpr (WT == 1) {
-                    rowmax_s[rpad(r)] = mv;
-                    if constexpr (ARGMAX) rowarg_s[r] = idx;
-                } else {
-                    xm[wt][r] = mv;
-                    if constexpr (ARGMAX) xi[wt][r] = idx;
-                }
+                rowmax_s[par][wt][rpad(r)] = mv;
+                if constexpr (ARGMAX) rowarg_s[par][wt][r] = idx;
             }
             m[cb] = -INFINITY;
             km[cb] = -INFINITY;
             code[cb] = -1;
         }
-        lds_barrier();
-        if constexpr (WT > 1) {
-            for (int r = tid; r < R; r += NT) {
-                float mv = xm[0][r];
-                int idx = 0;
-                if constexpr (ARGMAX) idx = xi[0][r];
+    };
+    // Row r's maximum / argmax over the token-waves (ties: lower index).
+    auto row_max = [&](int par, int r) {
+        float mv = rowmax_s[par][0][rpad(r)];
 #pragma unroll
-                for (int w = 1; w < WT; ++w) {
-                    const float om = xm[w][r];
-                    if constexpr (ARGMAX) {
-                        const int oi = xi[w][r];
-                        if (om > mv || (om == mv && (unsigned)oi < (unsigned)idx)) {
-                            mv = om;
-                            idx = oi;
-                        }
-                    } else {
-                        mv = fmaxf(mv, om);
-                    }
-                }
-                rowmax_s[rpad(r)] = mv;
-                if constexpr (ARGMAX) rowarg_s[r] = idx;
+        for (int w = 1; w < WT; ++w) mv = fmaxf(mv, rowmax_s[par][w][rpad(r)]);
+        return mv;
+    };
+    auto row_arg = [&](int par, int r) {
+        float mv = rowmax_s[par][0][rpad(r)];
+        int idx = rowarg_s[par][0][r];
+#pragma unroll
+        for (int w = 1; w < WT; ++w) {
+            const float om = rowmax_s[par][w][rpad(r)];
+            const int oi = rowarg_s[par][w][r];
+            if (om > mv || (om == mv && (unsigned)oi < (unsigned)idx)) {
+                mv = om;
+                idx = oi;
             }
-            lds_barrier();
         }
+        return idx;
+    };
+    // End of a document, part 2 (after the step barrier): argmax stores and
+    // the per-query sums of the row maxima.
+    auto epilogue_out = [&](int b, int par) {
         if constexpr (ARGMAX) {
+            // r = ql * ni + i; r, ni < 2^11, so the float quotient floors exactly
+            const float inv_ni = 1.0f / (float)ni;
             for (int r = tid; r < nrows; r += NT) {
-                const int ql = r / ni;
+                const int ql = (int)(((float)r + 0.5f) * inv_ni);
                 const int i = i0 + r - ql * ni;
-                p.argmax[((int64_t)(q0 + ql) * p.B + b) * Lq + i] = rowarg_s[r];
+                p.argmax[((int64_t)(q0 + ql) * p.B + b) * Lq + i] = row_arg(par, r);
             }
         }
         if constexpr (I8) {
@@ -496,7 +530,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             for (int ql = tid; ql < nq; ql += NT) {
                 float acc = 0.f;
                 for (int i = 0; i < ni; ++i) {
-                    const float v = rowmax_s[rpad(ql * ni + i)] * qsc_s[ql * ni + i];
+                    const float v = row_max(par, ql * ni + i) * qsc_s[ql * ni + i];
                     acc = acc + v;
                 }
                 p.scores[(int64_t)(q0 + ql) * p.B + b] = acc;
@@ -515,8 +549,10 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                 const int ql = ql0 + sub;
                 float acc = 0.f;
                 if (ql < nq)
-                    for (int i = pl; i < ni; i += P) acc += rowmax_s[rpad(ql * ni + i)];
-                for (int off = 1; off < P; off <<= 1) acc += __shfl_xor(acc, off);
+                    for (int i = pl; i < ni; i += P) acc += row_max(par, ql * ni + i);
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1)
+                    if (off < P) acc += __shfl_xor(acc, off);  // uniform guard, constant lane offsets
                 if (pl == 0 && ql < nq) {
                     float* dst = p.scores + (int64_t)(q0 + ql) * p.B + b;
                     if (p.split == 1) {
@@ -548,19 +584,68 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         }
         return c;
     };
-    auto advance = [&](const Cur& c) {
+    // Inside the loop the bounds of the next document travel like tile data:
+    // one wave DMAs them (two lanes) into an LDS slot just before issuing a
+    // step's tile loads, the step-end wait retires them, and after the barrier
+    // every wave reads them from LDS.  No scalar-memory load (whose counter is
+    // shared with LDS and returns out of order) and no vector load into
+    // registers sits in the loop.  Slot k&1 is written at the end of step k and
+    // read at the start of step k+1.
+    const bool doc_wave = wave == NW - 1;
+    auto prefetch_doc = [&](int slot, int b) {
+        if (doc_wave && b < p.B && lane < 2) {
+            const int32_t* src;
+            if constexpr (VARLEN) {
+                src = p.cu + b + lane;
+            } else {
+                src = p.lens ? p.lens + b : nullptr;
+            }
+            if (src) __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)&docpf[slot][0], 4, 0, 0);
+        }
+    };
+    auto from_prefetch = [&](int slot, int b) {
+        Cur c;
+        c.b = b;
+        c.t = 0;
+        c.start = 0;
+        c.len = 0;
+        c.ntiles = 0;
+        if (b < p.B) {
+            const int v0 = (VARLEN || p.lens) ? docpf[slot][0] : p.Ld;
+            if constexpr (VARLEN) {
+                const int v1 = docpf[slot][1];
+                int64_t s0 = v0, s1 = v1;
+                s0 = s0 < 0 ? 0 : (s0 > p.T ? p.T : s0);
+                s1 = s1 < s0 ? s0 : (s1 > p.T ? p.T : s1);
+                c.start = s0;
+                c.len = (int)(s1 - s0);
+            } else {
+                c.start = (int64_t)b * p.Ld;
+                c.len = v0 < 0 ? 0 : (v0 > p.Ld ? p.Ld : v0);
+            }
+            c.ntiles = (c.len + TT - 1) / TT;
+        }
+        return c;
+    };
+    auto advance = [&](int slot, const Cur& c) {  // the next step; a new document comes from the prefetch
         if (c.t + 1 < c.ntiles) {
             Cur n = c;
             n.t += 1;
             return n;
         }
-        return at_doc(c.b + p.num_streams);
+        return from_prefetch(slot, c.b + p.num_streams);
     };
     // nothing to read at all: every document is empty and D may be absent
     const bool loads = p.T > 0;
 
     Cur c0 = at_doc(stream);
-    Cur c1 = advance(c0);
+    Cur c1 = c0;
+    if (c0.t + 1 < c0.ntiles) {
+        c1.t += 1;
+    } else {
+        c1 = at_doc(stream + p.num_streams);
+    }
+    prefetch_doc(1, c1.b + p.num_streams);
     if (loads) {
         issue_tile(0, c0.start, c0.len, c0.t);
         if (c1.b < p.B) {
@@ -572,12 +657,24 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     }
     lds_barrier();
     int buf = 0;
+    int step = 0;
+    int par = 0;          // parity of the next document to finish
+    int pend = -1;        // document whose outputs are parked in rowmax_s[par ^ 1]
     while (true) {
         const bool has1 = c1.b < p.B;
-        Cur c2 = has1 ? advance(c1) : c1;
+        Cur c2 = has1 ? advance((step + 1) & 1, c1) : c1;
         const bool has2 = has1 && c2.b < p.B;
+        if (pend >= 0) {
+            epilogue_out(pend, par ^ 1);
+            pend = -1;
+        }
         if (c0.t < c0.ntiles) compute_tile(buf, c0.t, c0.len);
-        if (c0.t + 1 >= c0.ntiles) epilogue(c0.b);
+        if (c0.t + 1 >= c0.ntiles) {
+            epilogue_merge(par);
+            pend = c0.b;
+            par ^= 1;
+        }
+        if (has2) prefetch_doc(step & 1, c2.b + p.num_streams);
         if (loads) {
             if (has2) {
                 issue_tile(buf == 0 ? 2 : buf - 1, c2.start, c2.len, c2.t);
@@ -587,8 +684,12 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             }
         }
         lds_barrier();
-        if (!has1) break;
+        if (!has1) {
+            if (pend >= 0) epilogue_out(pend, par ^ 1);
+            break;
+        }
         buf = buf == 2 ? 0 : buf + 1;
+        ++step;
         c0 = c1;
         c1 = c2;
     }
@@ -599,7 +700,7 @@ __global__ __launch_bounds__(256) void zero_fill(float* x, int64_t n) {
     if (i < n) x[i] = 0.f;
 }
 
-template <int ELEM, int M, int QB, int WQ, int WT, int SPW, bool ARGMAX, bool VARLEN>
+template <int ELEM, int M, int QB, int WQ, int WT, int SPW, int NSI, bool ARGMAX, bool VARLEN>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream, int target_blocks) {
     constexpr int R = WQ * QB * M;
     FwdParams p;
@@ -642,7 +743,7 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream, int target_blocks) {
     p.scores = a.scores;
     p.argmax = a.argmax;
     const long long blocks = 8LL * p.num_slabs * s8;
-    hipLaunchKernelGGL((fwd_kernel<ELEM, M, QB, WQ, WT, SPW, ARGMAX, VARLEN>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((fwd_kernel<ELEM, M, QB, WQ, WT, SPW, NSI, ARGMAX, VARLEN>), dim3((unsigned)blocks),
                        dim3(64 * WQ * WT), 0, stream, p);
     return hipGetLastError();
 }
@@ -652,20 +753,20 @@ hipError_t dispatch_shape(const FwdArgs& a, hipStream_t stream) {
     // Few query rows in all (single-query reranking): one 32-row slab, four
     // waves split each document's tokens; many small workgroups fill the chip.
     if ((int64_t)a.Nq * a.Lq <= 32) {
-        return launch_cfg<ELEM, 16, 2, 1, 4, 1, ARGMAX, VARLEN>(a, stream, 2048);
+        return launch_cfg<ELEM, 16, 2, 1, 4, 1, 1, ARGMAX, VARLEN>(a, stream, 2048);
     }
     // Otherwise one persistent workgroup per CU holding a slab of query rows.
     if constexpr (ELEM == kI8) {
         // 1024 rows: 8 waves x 128 rows, 16x16x64 int8 blocks
-        return launch_cfg<ELEM, 16, 8, 8, 1, 4, ARGMAX, VARLEN>(a, stream, 256);
+        return launch_cfg<ELEM, 16, 8, 8, 1, 8, 1, ARGMAX, VARLEN>(a, stream, 256);
     } else {
         if (a.Lq > 512 && a.Lq <= 768) {
             // 768-row slabs of whole queries: 8 waves x 96 rows, 2 waves per SIMD
-            return launch_cfg<ELEM, 32, 3, 8, 1, 2, ARGMAX, VARLEN>(a, stream, 256);
+            return launch_cfg<ELEM, 32, 3, 8, 1, 4, 1, ARGMAX, VARLEN>(a, stream, 256);
         }
         // 512-row slabs (whole queries up to 512 tokens, else two halves of a
         // query): 8 waves x 64 rows
-        return launch_cfg<ELEM, 32, 2, 8, 1, 2, ARGMAX, VARLEN>(a, stream, 256);
+        return launch_cfg<ELEM, 32, 2, 8, 1, 4, 2, ARGMAX, VARLEN>(a, stream, 256);
     }
 }
 
