@@ -266,13 +266,19 @@ def main():
     if want_argmax:
         fwd_bytes += 4 * Nq * B * Lq
     traffic = read_traffic("fwd", name)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel": "fwd_kernel", "kernel_avg_ms": round(k_avg_ms, 5), "kernel_median_ms": round(k_med_ms, 5),
-                "algorithmic_flops_per_launch": fwd_flops, "algorithmic_bytes_per_launch": fwd_bytes,
-                "hbm_frac_of_algorithmic_bytes": round(fwd_bytes / (k_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    if el == "i8":
-        roofline["unit"] = "TOP/s"
+    hbm_gbs = fwd_bytes / (k_avg_ms * 1e-3) / 1e9
+    # the binding roof: arithmetic intensity against the ridge point peak / HBM
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if fwd_flops / fwd_bytes >= ridge:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TOP/s" if el == "i8" else "TFLOP/s", "frac": round(achieved / peak, 4)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
+    roofline.update({"traffic": traffic, "kernel": "fwd_kernel", "kernel_avg_ms": round(k_avg_ms, 5),
+                     "kernel_median_ms": round(k_med_ms, 5), "algorithmic_flops_per_launch": fwd_flops,
+                     "algorithmic_bytes_per_launch": fwd_bytes, "arithmetic_intensity": round(fwd_flops / fwd_bytes, 1),
+                     "mfma_frac": round(achieved / peak, 4), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4)})
     if bwd_ms:
         b_avg = float(np.mean(bwd_ms))
         Ld = w["Ld_max"]
