@@ -19,9 +19,9 @@
 //                  as its rank.  OR is commutative, so the result is
 //                  deterministic, and the per-query prefix over the group
 //                  makes the whole fill stable.
-//   4. dd_owner  : one 16-lane group owns one dD row, walks its sources and
-//                  writes the row once (no atomics).
-//   5. dq_gather : one 16-lane group owns one dQ row and loops over the B
+//   4. dd_owner  : a 16-lane group owns dD rows, walks their sources and
+//                  writes each row once (no atomics).
+//   5. dq_gather : a 16-lane group owns dQ rows and loops over the B
 //                  documents (Algorithm 3 step 3).
 // argmax entries outside [0, Ld) break the forward's contract; they are
 // clamped into range so that no access leaves the buffers.
@@ -72,7 +72,9 @@ __global__ __launch_bounds__(1024) void csr_count(BwdParams p) {
     for (int t = threadIdx.x; t < p.Ld; t += nt) out[t] = hist[t];
 }
 
-// One workgroup of 1024 threads per document.
+// One workgroup of 1024 threads per document.  The per-group counts of a row
+// are read 16 at a time (independent loads), summed, and after the scan over
+// the rows read again to write each group's first slot.
 __global__ __launch_bounds__(1024) void csr_scan(BwdParams p) {
     __shared__ int wsum[16];
     __shared__ int carry_s;
@@ -86,10 +88,12 @@ __global__ __launch_bounds__(1024) void csr_scan(BwdParams p) {
         const int t = t0 + tid;
         int tot = 0;
         if (t < p.Ld) {
-            for (int qg = 0; qg < p.NG; ++qg) {
-                const int c = ws[(int64_t)qg * p.Ld + t];
-                ws[(int64_t)qg * p.Ld + t] = tot;
-                tot += c;
+            for (int g0 = 0; g0 < p.NG; g0 += 16) {
+                int c[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) c[j] = g0 + j < p.NG ? ws[(int64_t)(g0 + j) * p.Ld + t] : 0;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) tot += c[j];
             }
         }
         // inclusive scan of tot over the 1024 threads
@@ -106,9 +110,18 @@ __global__ __launch_bounds__(1024) void csr_scan(BwdParams p) {
         const int carry = carry_s;
         const int excl = carry + wpre + x - tot;
         if (t < p.Ld) {
-            const int rp = (int)(doc_base + excl);
-            p.row_ptr[(int64_t)b * p.Ld + t] = rp;
-            for (int qg = 0; qg < p.NG; ++qg) ws[(int64_t)qg * p.Ld + t] += rp;
+            int run = (int)(doc_base + excl);
+            p.row_ptr[(int64_t)b * p.Ld + t] = run;
+            for (int g0 = 0; g0 < p.NG; g0 += 16) {
+                int c[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) c[j] = g0 + j < p.NG ? ws[(int64_t)(g0 + j) * p.Ld + t] : 0;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    if (g0 + j < p.NG) ws[(int64_t)(g0 + j) * p.Ld + t] = run;
+                    run += c[j];
+                }
+            }
         }
         __syncthreads();
         if (tid == 1023) carry_s = carry + wpre + x;
@@ -119,6 +132,10 @@ __global__ __launch_bounds__(1024) void csr_scan(BwdParams p) {
 
 // One wave per query of the group.  Dynamic LDS: G*Ld int (next slot per
 // (query, row)) followed by G*Ld*2 uint (64-bit lane masks per (query, row)).
+// A wave reads its query's Lq argmax entries once, into registers (at most
+// kMaxLq / 64 per lane), and uses them for both the count and the fill.
+constexpr int kFillIt = kMaxLq / 64;
+
 __global__ __launch_bounds__(1024) void csr_fill(BwdParams p) {
     extern __shared__ int lds[];
     const int qg = blockIdx.x % p.NG;
@@ -128,17 +145,23 @@ __global__ __launch_bounds__(1024) void csr_fill(BwdParams p) {
     const int Ld = p.Ld;
     int* slot = lds;                                            // [G][Ld]
     unsigned* mask = reinterpret_cast<unsigned*>(lds + p.G * Ld);  // [G][Ld][2]
+    const int q = qg * p.G + wave;
+    const int32_t* a = p.A + ((int64_t)q * p.B + b) * p.Lq;
+    int tk[kFillIt];  // -1: no source in this lane for step k
+#pragma unroll
+    for (int k = 0; k < kFillIt; ++k) {
+        const int i = k * 64 + lane;
+        tk[k] = (q < p.Nq && i < p.Lq) ? clamp_tok(a[i], Ld) : -1;
+    }
     for (int e = tid; e < p.G * Ld; e += nt) {
         slot[e] = 0;
         mask[2 * e] = 0u;
         mask[2 * e + 1] = 0u;
     }
     __syncthreads();
-    const int q = qg * p.G + wave;
-    const int32_t* a = p.A + ((int64_t)q * p.B + b) * p.Lq;
-    if (q < p.Nq) {
-        for (int i = lane; i < p.Lq; i += 64) atomicAdd(&slot[wave * Ld + clamp_tok(a[i], Ld)], 1);
-    }
+#pragma unroll
+    for (int k = 0; k < kFillIt; ++k)
+        if (tk[k] >= 0) atomicAdd(&slot[wave * Ld + tk[k]], 1);
     __syncthreads();
     // per row: exclusive prefix over the group's queries + the group's first slot
     const int32_t* first = p.ws + ((int64_t)b * p.NG + qg) * Ld;
@@ -156,10 +179,11 @@ __global__ __launch_bounds__(1024) void csr_fill(BwdParams p) {
         unsigned* mymask = mask + 2 * wave * Ld;
         const unsigned long long below = (1ull << lane) - 1ull;
         const int64_t s0 = ((int64_t)q * p.B + b) * p.Lq;
-        for (int i0 = 0; i0 < p.Lq; i0 += 64) {
-            const int i = i0 + lane;
-            const bool active = i < p.Lq;
-            const int t = active ? clamp_tok(a[i], Ld) : 0;
+#pragma unroll
+        for (int k = 0; k < kFillIt; ++k) {
+            if (k * 64 >= p.Lq) break;  // uniform
+            const int t = tk[k];
+            const bool active = t >= 0;
             if (active) atomicOr(&mymask[2 * t + (lane >> 5)], 1u << (lane & 31));
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the ORs have landed
             __builtin_amdgcn_wave_barrier();
@@ -173,7 +197,7 @@ __global__ __launch_bounds__(1024) void csr_fill(BwdParams p) {
             __builtin_amdgcn_wave_barrier();
             if (active) {
                 const int rank = __popcll(mk & below);
-                p.col_idx[base + rank] = (int)(s0 + i);
+                p.col_idx[base + rank] = (int)(s0 + k * 64 + lane);
                 if (rank == 0) {  // the lowest lane of the row advances it and clears the mask
                     myslot[t] = base + __popcll(mk);
                     mymask[2 * t] = 0u;
@@ -187,8 +211,7 @@ __global__ __launch_bounds__(1024) void csr_fill(BwdParams p) {
 }
 
 template <int ELEM>
-__device__ __forceinline__ void load8(const char* row, float* v) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(row);
+__device__ __forceinline__ void cvt8(const u32x4 raw, float* v) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
         const unsigned w = raw[h];
@@ -202,74 +225,193 @@ __device__ __forceinline__ void load8(const char* row, float* v) {
     }
 }
 
-// 16 lanes per dD row, 16 rows per 256-thread workgroup.
-template <int ELEM>
-__global__ __launch_bounds__(256) void dd_owner(BwdParams p) {
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int l16 = threadIdx.x & 15;
-    const int64_t nrows = (int64_t)p.B * p.Ld;
-    if (row >= nrows) return;
-    const int b = (int)(row / p.Ld);
-    const int kb = p.row_ptr[row], ke = p.row_ptr[row + 1];
-    const int BLq = p.B * p.Lq;
-    float acc[8];
+// The two gradient kernels are gather-bound: every dD row pulls ~Nq*Lq/Ld
+// query rows and every dQ row pulls one document row per document.  Both are
+// persistent (kGatherBlocks workgroups, all resident) and every 16-lane
+// group owns up to kRowsPerGroup output rows, which it advances together
+// through the reduction index -- documents b for dQ, query windows for dD --
+// in the same order as every other group.  The workgroups of one XCD so
+// work on the same few documents (or queries) at a time and the rows they
+// gather stay in that XCD's L2.  Each row still sums its terms one by one in
+// ascending source order, so runs are bit-identical.
+constexpr int kGatherThreads = 512;
+constexpr int kGatherGroups = kGatherThreads / 16;  // 16-lane groups per workgroup
+constexpr int kGatherBlocks = 512;                  // 2 per CU on 256 CUs
+constexpr int kRowsPerGroup = 4;
+constexpr int kDocStep = 2;       // documents per dQ step
+constexpr int kQueryWindow = 16;  // queries per dD step
+constexpr int kDdBatch = 12;      // dD sources gathered per round (loads in flight)
+
+__device__ __forceinline__ void fma8(float* acc, float g, const float* v) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int k = kb; k < ke; ++k) {
-        const int s = p.col_idx[k];
-        int q = (int)(((unsigned long long)(unsigned)s * p.magic) >> (32 + p.shift));
-        int i = s - q * BLq - b * p.Lq;
-        q = q < 0 ? 0 : (q >= p.Nq ? p.Nq - 1 : q);  // a consistent map never clamps
-        i = i < 0 ? 0 : (i >= p.Lq ? p.Lq - 1 : i);
-        const float gq = p.g[(int64_t)q * p.B + b];
-        float v[8];
-        load8<ELEM>(p.Q + ((int64_t)q * p.Lq + i) * 256 + l16 * 16, v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(gq, v[e], acc[e]);
-    }
-    f32x4* out = reinterpret_cast<f32x4*>(p.dD + row * 128 + l16 * 8);
+    for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(g, v[e], acc[e]);
+}
+
+__device__ __forceinline__ void store8(float* dst, const float* acc) {
+    f32x4* out = reinterpret_cast<f32x4*>(dst);
     out[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
     out[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
 }
 
-// 16 lanes per dQ row, 16 rows per 256-thread workgroup.
+// rows of group gid: gid + k * ngroups, k < rows_per_group (consecutive
+// groups hold consecutive rows, so index loads of a wave share cache lines).
+// Per query window the index loads of all the group's rows are issued
+// together, then each row's gathers.
 template <int ELEM>
-__global__ __launch_bounds__(256) void dq_gather(BwdParams p) {
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // q*Lq + i
+__global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void dd_owner(BwdParams p, int rows_per_group) {
     const int l16 = threadIdx.x & 15;
-    if (row >= (int64_t)p.Nq * p.Lq) return;
-    const int q = (int)(row / p.Lq);
-    const int i = (int)(row - (int64_t)q * p.Lq);
-    float acc[8];
+    const int64_t ngroups = (int64_t)gridDim.x * kGatherGroups;
+    const int64_t gid = (int64_t)blockIdx.x * kGatherGroups + (threadIdx.x >> 4);
+    const int64_t nrows = (int64_t)p.B * p.Ld;
+    const int BLq = p.B * p.Lq;
+    int cur[kRowsPerGroup], end[kRowsPerGroup], bdoc[kRowsPerGroup];
+    float acc[kRowsPerGroup][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    const int32_t* a = p.A + (int64_t)q * p.B * p.Lq + i;
-    const float* gq = p.g + (int64_t)q * p.B;
-    int b = 0;
-    for (; b + 4 <= p.B; b += 4) {
-        float v[4][8];
-        float gg[4];
+    for (int k = 0; k < kRowsPerGroup; ++k) {
+        const int64_t row = gid + k * ngroups;
+        const bool ok = k < rows_per_group && row < nrows;
+        cur[k] = ok ? p.row_ptr[row] : 0;
+        end[k] = ok ? p.row_ptr[row + 1] : 0;
+        bdoc[k] = ok ? (int)(row / p.Ld) : 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int t = clamp_tok(a[(int64_t)(b + u) * p.Lq], p.Ld);
-            gg[u] = gq[b + u];
-            load8<ELEM>(p.D + ((int64_t)(b + u) * p.Ld + t) * 256 + l16 * 16, v[u]);
+        for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+    }
+    const int gshift = threadIdx.x & 48;  // this group's first lane in the wave
+    for (int q0 = 0; q0 < p.Nq; q0 += kQueryWindow) {
+        const int qend = q0 + kQueryWindow;
+        bool more = true;
+        while (more) {  // uniform per 16-lane group; a second round only when a row has > kDdBatch sources here
+            int src[kRowsPerGroup];
+#pragma unroll
+            for (int k = 0; k < kRowsPerGroup; ++k) {
+                const int navail = min(kDdBatch, end[k] - cur[k]);
+                src[k] = l16 < navail ? p.col_idx[cur[k] + l16] : -1;
+            }
+            more = false;
+#pragma unroll
+            for (int k = 0; k < kRowsPerGroup; ++k) {
+                int qi = 0;
+                float gv = 0.f;
+                bool in = false;
+                if (src[k] >= 0) {
+                    int q = (int)(((unsigned long long)(unsigned)src[k] * p.magic) >> (32 + p.shift));
+                    int i = src[k] - q * BLq - bdoc[k] * p.Lq;
+                    q = q < 0 ? 0 : (q >= p.Nq ? p.Nq - 1 : q);  // a consistent map never clamps
+                    i = i < 0 ? 0 : (i >= p.Lq ? p.Lq - 1 : i);
+                    in = q < qend;
+                    gv = p.g[(int64_t)q * p.B + bdoc[k]];
+                    qi = q * p.Lq + i;
+                }
+                // sources are in ascending q: the ones in this window are a prefix
+                const int n = __popcll((__ballot(in) >> gshift) & 0xffffull);
+                if (n == 0) continue;
+                u32x4 raw[kDdBatch];
+#pragma unroll
+                for (int j = 0; j < kDdBatch; ++j) {
+                    const int qj = __shfl(qi, j, 16);
+                    if (j < n) raw[j] = *reinterpret_cast<const u32x4*>(p.Q + (int64_t)qj * 256 + l16 * 16);
+                }
+#pragma unroll
+                for (int j = 0; j < kDdBatch; ++j) {
+                    const float gj = __shfl(gv, j, 16);
+                    if (j < n) {
+                        float v[8];
+                        cvt8<ELEM>(raw[j], v);
+                        fma8(acc[k], gj, v);
+                    }
+                }
+                cur[k] += n;
+                if (n == kDdBatch) more = true;
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerGroup; ++k) {
+        const int64_t row = gid + k * ngroups;
+        if (k < rows_per_group && row < nrows) store8(p.dD + row * 128 + l16 * 8, acc[k]);
+    }
+}
+
+// Per step of kDocStep documents the gathers of all the group's rows are in
+// flight together.
+template <int ELEM>
+__global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void dq_gather(BwdParams p, int rows_per_group) {
+    const int l16 = threadIdx.x & 15;
+    const int64_t ngroups = (int64_t)gridDim.x * kGatherGroups;
+    const int64_t gid = (int64_t)blockIdx.x * kGatherGroups + (threadIdx.x >> 4);
+    const int64_t nrows = (int64_t)p.Nq * p.Lq;
+    int aoff[kRowsPerGroup], goff[kRowsPerGroup];  // Nq*B*Lq < 2^31 (checked by the host)
+    bool ok[kRowsPerGroup];
+    float acc[kRowsPerGroup][8];
+#pragma unroll
+    for (int k = 0; k < kRowsPerGroup; ++k) {
+        const int64_t row = gid + k * ngroups;  // q*Lq + i
+        ok[k] = k < rows_per_group && row < nrows;
+        const int q = ok[k] ? (int)(row / p.Lq) : 0;
+        const int i = ok[k] ? (int)(row - (int64_t)q * p.Lq) : 0;
+        aoff[k] = q * p.B * p.Lq + i;
+        goff[k] = q * p.B;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+    }
+    // Straight-line steps: every load is issued unconditionally from a valid
+    // address (a missing row or document reads row 0 / the last document) and
+    // its term gets weight 0, so no branch separates a load from the next.
+    for (int b0 = 0; b0 < p.B; b0 += kDocStep) {
+        const int nb = min(kDocStep, p.B - b0);
+        const bool lane_doc = l16 < nb;
+        const int bl = b0 + (lane_doc ? l16 : 0);
+        int araw[kRowsPerGroup];
+        float gv[kRowsPerGroup];
+#pragma unroll
+        for (int k = 0; k < kRowsPerGroup; ++k) {
+            araw[k] = p.A[aoff[k] + (int64_t)bl * p.Lq];
+            gv[k] = p.g[goff[k] + bl];
+        }
+        int tok[kRowsPerGroup];
+#pragma unroll
+        for (int k = 0; k < kRowsPerGroup; ++k) {
+            tok[k] = clamp_tok(araw[k], p.Ld);
+            gv[k] = (ok[k] && lane_doc) ? gv[k] : 0.f;
+        }
+        u32x4 raw[kRowsPerGroup][kDocStep];
+#pragma unroll
+        for (int k = 0; k < kRowsPerGroup; ++k) {
+#pragma unroll
+            for (int j = 0; j < kDocStep; ++j) {
+                const int tj = __shfl(tok[k], j, 16);
+                // document base is wave-uniform; the row offset fits 32 bits (Ld <= 4096)
+                const char* Db = p.D + (int64_t)min(b0 + j, p.B - 1) * p.Ld * 256;
+                raw[k][j] = *reinterpret_cast<const u32x4*>(Db + (unsigned)(tj * 256 + l16 * 16));
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int k = 0; k < kRowsPerGroup; ++k) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(gg[u], v[u][e], acc[e]);
+            for (int j = 0; j < kDocStep; ++j) {
+                const float gj = __shfl(gv[k], j, 16);
+                float v[8];
+                cvt8<ELEM>(raw[k][j], v);
+                fma8(acc[k], gj, v);
+            }
+        }
     }
-    for (; b < p.B; ++b) {
-        const int t = clamp_tok(a[(int64_t)b * p.Lq], p.Ld);
-        float v[8];
-        load8<ELEM>(p.D + ((int64_t)b * p.Ld + t) * 256 + l16 * 16, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(gq[b], v[e], acc[e]);
+    for (int k = 0; k < kRowsPerGroup; ++k) {
+        const int64_t row = gid + k * ngroups;
+        if (ok[k]) store8(p.dQ + row * 128 + l16 * 8, acc[k]);
     }
-    f32x4* out = reinterpret_cast<f32x4*>(p.dQ + row * 128 + l16 * 8);
-    out[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    out[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+}
+
+// grid and rows per group for a persistent gather over nrows rows
+void gather_grid(int64_t nrows, unsigned* blocks, int* rows_per_group) {
+    const int64_t full = (int64_t)kGatherBlocks * kGatherGroups;
+    int r = (int)((nrows + full - 1) / full);
+    if (r < 1) r = 1;
+    if (r > kRowsPerGroup) r = kRowsPerGroup;
+    const int64_t groups = (nrows + r - 1) / r;
+    *blocks = (unsigned)((groups + kGatherGroups - 1) / kGatherGroups);
+    *rows_per_group = r;
 }
 
 template <int ELEM>
@@ -283,11 +425,13 @@ hipError_t launch_bwd_elem(const BwdParams& p, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(csr_fill, dim3(groups), dim3(nthr), (size_t)p.G * p.Ld * 12, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t drows = (int64_t)p.B * p.Ld;
-    hipLaunchKernelGGL((dd_owner<ELEM>), dim3((unsigned)((drows + 15) / 16)), dim3(256), 0, stream, p);
+    unsigned blocks;
+    int rpg;
+    gather_grid((int64_t)p.B * p.Ld, &blocks, &rpg);
+    hipLaunchKernelGGL((dd_owner<ELEM>), dim3(blocks), dim3(kGatherThreads), 0, stream, p, rpg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t qrows = (int64_t)p.Nq * p.Lq;
-    hipLaunchKernelGGL((dq_gather<ELEM>), dim3((unsigned)((qrows + 15) / 16)), dim3(256), 0, stream, p);
+    gather_grid((int64_t)p.Nq * p.Lq, &blocks, &rpg);
+    hipLaunchKernelGGL((dq_gather<ELEM>), dim3(blocks), dim3(kGatherThreads), 0, stream, p, rpg);
     return hipGetLastError();
 }
 
