@@ -10,18 +10,20 @@
 //     keeps it stationary in VGPRs as the MFMA B operand for its whole life.
 //     This is the query-reuse member of the page's kernel family (Section 4.1
 //     "Kernel Family"): every document tile it reads is used against all R rows.
-//   * Documents stream HBM -> LDS in tiles of 128 tokens (64 for the small
-//     single-query configuration) through a three-stage ring of direct
-//     (global_load_lds) loads: the tiles two steps ahead, possibly of later
-//     documents, are in flight while the current one is contracted.  LDS rows are XOR-swizzled by 16-byte
-//     chunk so the MFMA operand reads are bank-conflict free.
+//   * Documents stream HBM -> LDS in tiles (256 tokens in a two-buffer ring
+//     for fp16/bf16 32x32 blocks; 128 or 64 tokens in a three-buffer ring
+//     otherwise) of direct (global_load_lds) loads: the next tiles, possibly
+//     of later documents, are in flight while the current one is contracted.
+//     LDS rows are XOR-swizzled by 16-byte chunk so the MFMA operand reads are
+//     bank-conflict free.
 //   * S_t = D_tile Q_slab^T is formed M doc tokens x M query rows at a time.
-//     fp16/bf16 use v_mfma_f32_32x32x16 (M = 32: four independent accumulation
-//     chains per wave keep the matrix pipe full, where 16x16 tiles would need
-//     twice as many); int8 uses v_mfma_i32_16x16x64_i8 (M = 16).  Doc tokens are
+//     fp16/bf16 use v_mfma_f32_32x32x16 (M = 32; one accumulation chain per
+//     query block); int8 uses v_mfma_i32_16x16x64_i8 (M = 16).  Doc tokens are
 //     the M dimension of the result, so each lane holds VPL tokens of one query
 //     row and the running max / argmax stays in the lane; lanes are merged once
-//     per document.
+//     per document.  For 32x32 blocks the sub-tiles of a tile form a software
+//     pipeline: the MFMAs of sub-tile j are interleaved with the VALU fold of
+//     sub-tile j-1, so the matrix pipe and the VALU overlap inside one wave.
 //   * The grid is persistent: block -> (slab, document stream) is laid out so
 //     the workgroups sharing a document stream sit on the same XCD (blocks are
 //     dispatched round-robin over the 8 XCDs) and re-read each tile from that
@@ -188,11 +190,22 @@ __device__ __forceinline__ void doc_info(const FwdParams& p, int b, int64_t& sta
 __device__ __forceinline__ unsigned fbits(float x) { return __float_as_uint(x); }
 __device__ __forceinline__ float bitsf(unsigned x) { return __uint_as_float(x); }
 
+// Calls f(std::integral_constant<int, j>{}) for j = 0 .. N-1, expanded at
+// compile time.
+template <int N, int J = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (J < N) {
+        f(std::integral_constant<int, J>{});
+        static_for<N, J + 1>(f);
+    }
+}
+
 // ELEM: kF16 / kBF16 / kI8.  M: MFMA block edge (16 or 32).  QB: M-row query
 // blocks per wave.  WQ x WT waves: WQ along query rows, WT along document
 // tokens.  SPW: M-token sub-tiles each wave contracts per tile, NSI of them at
-// a time (1 or 2).  ARGMAX: also track and write the argmax.
-template <int ELEM, int M, int QB, int WQ, int WT, int SPW, int NSI, bool ARGMAX, bool VARLEN>
+// a time (1 or 2).  NBUF: tile ring depth (2 or 3).  ARGMAX: also track and
+// write the argmax.
+template <int ELEM, int M, int QB, int WQ, int WT, int SPW, int NSI, int NBUF, bool ARGMAX, bool VARLEN>
 __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     using MM = Mma<ELEM, M>;
     using Acc = typename MM::Acc;
@@ -215,8 +228,9 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     constexpr bool KEYED = ARGMAX && !I8 && M == 32;
     constexpr unsigned KMASK = VPL - 1;
 
-    // Three-stage ring: tile k is contracted while tiles k+1 and k+2 are in flight.
-    constexpr int NBUF = 3;
+    // Ring of NBUF tile buffers: tile k is contracted while tiles k+1 ..
+    // k+NBUF-1 are in flight.
+    static_assert(NBUF == 2 || NBUF == 3, "ring depth");
     constexpr int LPW = TT * NCH / (64 * NW);  // 1 KB direct loads per wave per tile
     static_assert(LPW * 64 * NW == TT * NCH, "tile must split into whole 1 KB loads per wave");
     static_assert(!I8 || TT % 64 == 0, "int8 scales load 64 at a time");
@@ -322,11 +336,13 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             }
         }
     };
-    // Wait until only the most recent tile's loads may still be in flight.
-    // Vector-memory loads complete in issue order, so this retires every older
-    // load (and the epilogue's stores issued before them).
-    auto wait_all_but_last_tile = [&]() {
-        if (scale_wave) {
+    // End of a step: wait until the next tile has landed.  Vector-memory
+    // operations complete in issue order, so allowing only the loads of the
+    // NBUF-2 newest tiles to remain retires every older load and store.
+    auto wait_next_tile = [&]() {
+        if constexpr (NBUF == 2) {
+            wait_vmcnt<0>();
+        } else if (scale_wave) {
             wait_vmcnt<LPW + 1>();
         } else {
             wait_vmcnt<LPW>();
@@ -427,7 +443,122 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         }
     };
 
+    // fp16/bf16 with 32x32 blocks: the sub-tiles of a tile run as a software
+    // pipeline.  Stage j issues sub-tile j's MFMA chains (one per query block)
+    // while the VALU folds sub-tile j-1's results into the running maximum
+    // (and argmax key).  The two touch disjoint registers, and the scheduling
+    // hints below interleave them, so the matrix pipe and the VALU work side
+    // by side within one wave instead of taking turns.
+    // Per k-step the stage issues one MFMA per query block and folds VPL/KS
+    // values of each of the previous stage's blocks (a fixed, hand-interleaved
+    // order; the scheduling barrier keeps the compiler from regrouping it).
+    static_assert(M != 32 || VPL % KS == 0, "fold parts");
+    constexpr int FPS = VPL / KS;  // values folded per block per k-step
+    auto stage = [&](int bf, int sb, Acc* cur, const Acc* prev, bool has_prev, int gprev) {
+        u32x4 a[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a[s] = dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
+#pragma unroll
+        for (int cb = 0; cb < QB; ++cb) cur[cb] = MM::zero();
+        float kt[QB];
+#pragma unroll
+        for (int cb = 0; cb < QB; ++cb) kt[cb] = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+            for (int cb = 0; cb < QB; ++cb) cur[cb] = MM::mma(a[s], bq[cb][s], cur[cb]);
+            if (has_prev) {  // uniform
+#pragma unroll
+                for (int cb = 0; cb < QB; ++cb) {
+                    float mx = m[cb];
+#pragma unroll
+                    for (int f = 0; f < FPS; ++f) mx = fmaxf(mx, prev[cb][s * FPS + f]);
+                    m[cb] = mx;
+                    if constexpr (KEYED) {
+                        float k2 = kt[cb];
+#pragma unroll
+                        for (int f = 0; f < FPS; ++f) {
+                            const int i = s * FPS + f;
+                            k2 = fmaxf(k2, bitsf((fbits(prev[cb][i]) & ~KMASK) | (KMASK - i)));
+                        }
+                        kt[cb] = k2;
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (KEYED) {
+            if (has_prev) {
+#pragma unroll
+                for (int cb = 0; cb < QB; ++cb) {
+                    const bool upd = kt[cb] > km[cb];  // strict: the earlier sub-tile keeps a tie
+                    km[cb] = upd ? kt[cb] : km[cb];
+                    code[cb] = upd ? gprev : code[cb];
+                }
+            }
+        }
+    };
+    // Fold a whole block of results (the last stage of a tile, which can be
+    // partial: tokens at or past ln are -inf and never win).
+    auto fold = [&](auto mask_tag, const Acc* acc, int tok0, int ln, int gsub) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+        for (int cb = 0; cb < QB; ++cb) {
+            float v[VPL];
+            bool valid[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                valid[i] = !MASK || (tok0 + MM::tok(g, i) < ln);
+                v[i] = valid[i] ? acc[cb][i] : -INFINITY;
+            }
+            float mx = m[cb];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) mx = fmaxf(mx, v[i]);
+            m[cb] = mx;
+            if constexpr (KEYED) {
+                float kt = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const unsigned key = (fbits(v[i]) & ~KMASK) | (KMASK - i);
+                    kt = fmaxf(kt, valid[i] ? bitsf(key) : -INFINITY);
+                }
+                const bool upd = kt > km[cb];  // strict: the earlier sub-tile keeps a tie
+                km[cb] = upd ? kt : km[cb];
+                code[cb] = upd ? gsub : code[cb];
+            }
+        }
+    };
+    auto compute_tile_pipe = [&](int bf, int tt, int ln) {
+        if (wq * QB * M >= nrows) return;  // uniform: this wave's rows are all past the slab
+        const int tok_w = tt * TT + wt * SPW * M;  // first token of this wave's sub-tiles
+        int nsub = (ln - tok_w + M - 1) / M;       // sub-tiles holding at least one valid token
+        nsub = nsub < 0 ? 0 : (nsub > SPW ? SPW : nsub);
+        Acc acc0[QB], acc1[QB];  // ping-pong accumulators (even / odd stages)
+        // stages are expanded at compile time so every accumulator index is static
+        static_for<SPW>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if (j >= nsub) return;  // uniform
+            Acc* cur = (j & 1) ? acc1 : acc0;
+            const Acc* prev = (j & 1) ? acc0 : acc1;
+            const int sb = wt * SPW + j;
+            const int gsub = tt * SUBS + sb;
+            stage(bf, sb, cur, prev, j > 0, gsub - 1);
+            if (j == nsub - 1) {  // drain: fold the last sub-tile (the only one that can be partial)
+                const int tok0 = tok_w + j * M;
+                if (tok0 + M <= ln) {
+                    fold(std::false_type{}, cur, tok0, ln, gsub);
+                } else {
+                    fold(std::true_type{}, cur, tok0, ln, gsub);
+                }
+            }
+        });
+    };
+
     auto compute_tile = [&](int bf, int tt, int ln) {
+        if constexpr (!I8 && M == 32 && QB <= 2) {  // two stages of accumulators fit in registers
+            compute_tile_pipe(bf, tt, ln);
+            return;
+        }
         if (wq * QB * M >= nrows) return;  // uniform: this wave's rows are all past the slab
         const int tok_w = tt * TT + wt * SPW * M;  // first token of this wave's sub-tiles
         int nsub = (ln - tok_w + M - 1) / M;       // sub-tiles holding at least one valid token
@@ -638,60 +769,67 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     // nothing to read at all: every document is empty and D may be absent
     const bool loads = p.T > 0;
 
-    Cur c0 = at_doc(stream);
-    Cur c1 = c0;
-    if (c0.t + 1 < c0.ntiles) {
-        c1.t += 1;
-    } else {
-        c1 = at_doc(stream + p.num_streams);
-    }
-    prefetch_doc(1, c1.b + p.num_streams);
-    if (loads) {
-        issue_tile(0, c0.start, c0.len, c0.t);
-        if (c1.b < p.B) {
-            issue_tile(1, c1.start, c1.len, c1.t);
-            wait_all_but_last_tile();
+    // cs[0] is the tile contracted in this step, cs[j] the one j steps later.
+    // The tiles cs[0 .. NBUF-2] are in flight or landed at the top of a step;
+    // the step issues cs[NBUF-1] into the buffer freed by the previous step.
+    Cur cs[NBUF];
+    cs[0] = at_doc(stream);
+    if constexpr (NBUF == 3) {
+        cs[1] = cs[0];
+        if (cs[1].t + 1 < cs[1].ntiles) {
+            cs[1].t += 1;
         } else {
-            wait_vmcnt<0>();
+            cs[1] = at_doc(cs[0].b + p.num_streams);
         }
     }
+    prefetch_doc(1, cs[NBUF - 2].b + p.num_streams);
+    if (loads) {
+        static_for<NBUF - 1>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if (cs[j].b < p.B) issue_tile(j, cs[j].start, cs[j].len, cs[j].t);
+        });
+        wait_vmcnt<0>();
+    }
     lds_barrier();
-    int buf = 0;
+    int buf = 0;          // ring slot of cs[0]
     int step = 0;
     int par = 0;          // parity of the next document to finish
     int pend = -1;        // document whose outputs are parked in rowmax_s[par ^ 1]
     while (true) {
-        const bool has1 = c1.b < p.B;
-        Cur c2 = has1 ? advance((step + 1) & 1, c1) : c1;
-        const bool has2 = has1 && c2.b < p.B;
+        const bool has0 = cs[0].b < p.B;
+        const bool hasl = cs[NBUF - 2].b < p.B;
+        cs[NBUF - 1] = hasl ? advance((step + 1) & 1, cs[NBUF - 2]) : cs[NBUF - 2];
+        const bool hasn = hasl && cs[NBUF - 1].b < p.B;
         if (pend >= 0) {
             epilogue_out(pend, par ^ 1);
             pend = -1;
         }
-        if (c0.t < c0.ntiles) compute_tile(buf, c0.t, c0.len);
-        if (c0.t + 1 >= c0.ntiles) {
+        if (hasn) prefetch_doc(step & 1, cs[NBUF - 1].b + p.num_streams);
+        if (loads && hasn) {
+            const int nb = buf + NBUF - 1;
+            issue_tile(nb >= NBUF ? nb - NBUF : nb, cs[NBUF - 1].start, cs[NBUF - 1].len, cs[NBUF - 1].t);
+        }
+        if (!has0) break;  // nothing issued or pending past here (has0 false => hasn false)
+        if (cs[0].t < cs[0].ntiles) compute_tile(buf, cs[0].t, cs[0].len);
+        if (cs[0].t + 1 >= cs[0].ntiles) {
             epilogue_merge(par);
-            pend = c0.b;
+            pend = cs[0].b;
             par ^= 1;
         }
-        if (has2) prefetch_doc(step & 1, c2.b + p.num_streams);
         if (loads) {
-            if (has2) {
-                issue_tile(buf == 0 ? 2 : buf - 1, c2.start, c2.len, c2.t);
-                wait_all_but_last_tile();
+            if (hasn) {
+                wait_next_tile();
             } else {
-                wait_vmcnt<0>();
+                wait_vmcnt<0>();  // no newer tile: everything outstanding must land
             }
         }
         lds_barrier();
-        if (!has1) {
-            if (pend >= 0) epilogue_out(pend, par ^ 1);
-            break;
-        }
-        buf = buf == 2 ? 0 : buf + 1;
+        buf = buf == NBUF - 1 ? 0 : buf + 1;
         ++step;
-        c0 = c1;
-        c1 = c2;
+        static_for<NBUF - 1>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            cs[j] = cs[j + 1];
+        });
     }
 }
 
@@ -700,7 +838,7 @@ __global__ __launch_bounds__(256) void zero_fill(float* x, int64_t n) {
     if (i < n) x[i] = 0.f;
 }
 
-template <int ELEM, int M, int QB, int WQ, int WT, int SPW, int NSI, bool ARGMAX, bool VARLEN>
+template <int ELEM, int M, int QB, int WQ, int WT, int SPW, int NSI, int NBUF, bool ARGMAX, bool VARLEN>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream, int target_blocks) {
     constexpr int R = WQ * QB * M;
     FwdParams p;
@@ -743,7 +881,7 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream, int target_blocks) {
     p.scores = a.scores;
     p.argmax = a.argmax;
     const long long blocks = 8LL * p.num_slabs * s8;
-    hipLaunchKernelGGL((fwd_kernel<ELEM, M, QB, WQ, WT, SPW, NSI, ARGMAX, VARLEN>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((fwd_kernel<ELEM, M, QB, WQ, WT, SPW, NSI, NBUF, ARGMAX, VARLEN>), dim3((unsigned)blocks),
                        dim3(64 * WQ * WT), 0, stream, p);
     return hipGetLastError();
 }
@@ -753,20 +891,20 @@ hipError_t dispatch_shape(const FwdArgs& a, hipStream_t stream) {
     // Few query rows in all (single-query reranking): one 32-row slab, four
     // waves split each document's tokens; many small workgroups fill the chip.
     if ((int64_t)a.Nq * a.Lq <= 32) {
-        return launch_cfg<ELEM, 16, 2, 1, 4, 1, 1, ARGMAX, VARLEN>(a, stream, 2048);
+        return launch_cfg<ELEM, 16, 2, 1, 4, 1, 1, 3, ARGMAX, VARLEN>(a, stream, 2048);
     }
     // Otherwise one persistent workgroup per CU holding a slab of query rows.
     if constexpr (ELEM == kI8) {
         // 1024 rows: 8 waves x 128 rows, 16x16x64 int8 blocks
-        return launch_cfg<ELEM, 16, 8, 8, 1, 8, 1, ARGMAX, VARLEN>(a, stream, 256);
+        return launch_cfg<ELEM, 16, 8, 8, 1, 8, 1, 3, ARGMAX, VARLEN>(a, stream, 256);
     } else {
         if (a.Lq > 512 && a.Lq <= 768) {
             // 768-row slabs of whole queries: 8 waves x 96 rows, 2 waves per SIMD
-            return launch_cfg<ELEM, 32, 3, 8, 1, 4, 1, ARGMAX, VARLEN>(a, stream, 256);
+            return launch_cfg<ELEM, 32, 3, 8, 1, 4, 1, 3, ARGMAX, VARLEN>(a, stream, 256);
         }
         // 512-row slabs (whole queries up to 512 tokens, else two halves of a
         // query): 8 waves x 64 rows
-        return launch_cfg<ELEM, 32, 2, 8, 1, 4, 2, ARGMAX, VARLEN>(a, stream, 256);
+        return launch_cfg<ELEM, 32, 2, 8, 1, 8, 2, 2, ARGMAX, VARLEN>(a, stream, 256);
     }
 }
 
