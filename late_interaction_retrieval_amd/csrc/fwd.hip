@@ -190,6 +190,14 @@ __device__ __forceinline__ void doc_info(const FwdParams& p, int b, int64_t& sta
 __device__ __forceinline__ unsigned fbits(float x) { return __float_as_uint(x); }
 __device__ __forceinline__ float bitsf(unsigned x) { return __uint_as_float(x); }
 
+// Value of lane l ^ 32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ unsigned xor32_u(unsigned v, int lane) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return lane < 32 ? r[1] : r[0];
+}
+__device__ __forceinline__ float xor32_f(float v, int lane) { return bitsf(xor32_u(fbits(v), lane)); }
+
+
 // Calls f(std::integral_constant<int, j>{}) for j = 0 .. N-1, expanded at
 // compile time.
 template <int N, int J = 0, typename F>
@@ -602,9 +610,9 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             }
 #pragma unroll
             for (int off = M; off < 64; off <<= 1) {
-                const float om = __shfl_xor(mv, off);
+                const float om = off == 32 ? xor32_f(mv, lane) : __shfl_xor(mv, off);
                 if constexpr (ARGMAX) {
-                    const int oi = __shfl_xor(idx, off);
+                    const int oi = off == 32 ? (int)xor32_u((unsigned)idx, lane) : __shfl_xor(idx, off);
                     if (om > mv || (om == mv && (unsigned)oi < (unsigned)idx)) {
                         mv = om;
                         idx = oi;
@@ -770,44 +778,59 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     const bool loads = p.T > 0;
 
     // cs[0] is the tile contracted in this step, cs[j] the one j steps later.
-    // The tiles cs[0 .. NBUF-2] are in flight or landed at the top of a step;
-    // the step issues cs[NBUF-1] into the buffer freed by the previous step.
+    // The prologue issues tiles 0 .. NBUF-1 (every buffer); at the top of
+    // step k >= 1, cs[NBUF-1] = tile k+NBUF-1 goes into the buffer that step
+    // k-1 freed.  So at any time the next NBUF-1 tiles are in flight or landed.
     Cur cs[NBUF];
     cs[0] = at_doc(stream);
-    if constexpr (NBUF == 3) {
-        cs[1] = cs[0];
-        if (cs[1].t + 1 < cs[1].ntiles) {
-            cs[1].t += 1;
+    static_for<NBUF - 1>([&](auto jc) {
+        constexpr int j = decltype(jc)::value + 1;
+        cs[j] = cs[j - 1];
+        if (cs[j].t + 1 < cs[j].ntiles) {
+            cs[j].t += 1;
         } else {
-            cs[1] = at_doc(cs[0].b + p.num_streams);
+            cs[j] = at_doc(cs[j - 1].b + p.num_streams);
         }
-    }
-    prefetch_doc(1, cs[NBUF - 2].b + p.num_streams);
+    });
+    prefetch_doc(1, cs[NBUF - 1].b + p.num_streams);
     if (loads) {
-        static_for<NBUF - 1>([&](auto jc) {
+        static_for<NBUF>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             if (cs[j].b < p.B) issue_tile(j, cs[j].start, cs[j].len, cs[j].t);
         });
-        wait_vmcnt<0>();
+        // tile 0 has landed once only the loads of tiles 1 .. NBUF-1 may remain;
+        // when the stream ends earlier, fewer were issued: wait for all
+        if (cs[NBUF - 1].b < p.B) {
+            if (scale_wave) {
+                wait_vmcnt<(NBUF - 1) * (LPW + 1)>();
+            } else {
+                wait_vmcnt<(NBUF - 1) * LPW>();
+            }
+        } else {
+            wait_vmcnt<0>();
+        }
     }
     lds_barrier();
     int buf = 0;          // ring slot of cs[0]
     int step = 0;
     int par = 0;          // parity of the next document to finish
     int pend = -1;        // document whose outputs are parked in rowmax_s[par ^ 1]
+    bool hasn = cs[NBUF - 1].b < p.B;  // the newest tile (cs[NBUF-1]) exists
     while (true) {
         const bool has0 = cs[0].b < p.B;
-        const bool hasl = cs[NBUF - 2].b < p.B;
-        cs[NBUF - 1] = hasl ? advance((step + 1) & 1, cs[NBUF - 2]) : cs[NBUF - 2];
-        const bool hasn = hasl && cs[NBUF - 1].b < p.B;
-        if (pend >= 0) {
+        if (pend >= 0) {  // stores first: they must be older than this step's loads
             epilogue_out(pend, par ^ 1);
             pend = -1;
         }
-        if (hasn) prefetch_doc(step & 1, cs[NBUF - 1].b + p.num_streams);
-        if (loads && hasn) {
-            const int nb = buf + NBUF - 1;
-            issue_tile(nb >= NBUF ? nb - NBUF : nb, cs[NBUF - 1].start, cs[NBUF - 1].len, cs[NBUF - 1].t);
+        if (step > 0) {
+            const bool hasl = cs[NBUF - 2].b < p.B;
+            cs[NBUF - 1] = hasl ? advance(step & 1, cs[NBUF - 2]) : cs[NBUF - 2];
+            hasn = hasl && cs[NBUF - 1].b < p.B;
+            if (hasn) prefetch_doc((step + 1) & 1, cs[NBUF - 1].b + p.num_streams);
+            if (loads && hasn) {
+                const int nb = buf + NBUF - 1;
+                issue_tile(nb >= NBUF ? nb - NBUF : nb, cs[NBUF - 1].start, cs[NBUF - 1].len, cs[NBUF - 1].t);
+            }
         }
         if (!has0) break;  // nothing issued or pending past here (has0 false => hasn false)
         if (cs[0].t < cs[0].ntiles) compute_tile(buf, cs[0].t, cs[0].len);
@@ -830,6 +853,122 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             constexpr int j = decltype(jc)::value;
             cs[j] = cs[j + 1];
         });
+    }
+}
+
+// Few query rows in all (Nq * Lq <= 32, e.g. one ColBERT query): the work per
+// document token is tiny and the kernel is bound by reading D.  One workgroup
+// per document; each of its W waves takes SPL 16-token sub-tiles per round
+// and loads them straight from HBM into MFMA operand registers (no LDS
+// staging, no barrier until the end), all of a round's loads in flight at
+// once.  Lane group g reads 16 contiguous bytes at chunk s*4 + g of its row in
+// k-step s, so one load instruction covers 64 contiguous bytes of 16 rows.
+// The argmax is exact (first index on ties).  The waves' row results meet in
+// LDS once at the end.
+template <int ELEM, int W, int SPL, bool ARGMAX, bool VARLEN>
+__global__ __launch_bounds__(64 * W) void fwd_tiny_kernel(FwdParams p) {
+    using MM = Mma<ELEM, 16>;
+    using Acc = typename MM::Acc;
+    constexpr int M = 16, NG = MM::NG, KS = MM::KS, VPL = MM::VPL, ROWB = 256;
+    __shared__ float rowmax_s[W][2 * M];
+    __shared__ int rowarg_s[W][2 * M];
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane / M, lm = lane % M;
+    int64_t st;
+    int len;
+    doc_info<VARLEN>(p, b, st, len);
+    const int nrows = p.Nq * p.Lq;  // <= 32: two 16-row blocks
+    u32x4 bq[2][KS];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int r = cb * M + lm;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2)
+            bq[cb][s2] = r < nrows ? *reinterpret_cast<const u32x4*>(p.Q + (int64_t)r * ROWB + (s2 * NG + g) * 16)
+                                   : u32x4{0u, 0u, 0u, 0u};
+    }
+    float m[2] = {-INFINITY, -INFINITY};
+    int best[2] = {-1, -1};  // token index of the maximum (first on ties)
+    const int nsub = (len + M - 1) / M;
+    const int64_t safe = len > 0 ? st : 0;
+    for (int base = wave * SPL; base < nsub; base += W * SPL) {  // uniform
+        u32x4 a[SPL][KS];
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            const int tok = (base + j) * M + lm;
+            const int64_t row = tok < len ? st + tok : safe;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2)
+                a[j][s2] = *reinterpret_cast<const u32x4*>(p.D + row * ROWB + (s2 * NG + g) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            const int sb = base + j;
+            if (sb >= nsub) break;  // uniform
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                Acc acc = MM::zero();
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) acc = MM::mma(a[j][s2], bq[cb][s2], acc);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int tk = sb * M + MM::tok(g, i);
+                    const float v = tk < len ? acc[i] : -INFINITY;
+                    if (v > m[cb]) {  // strict: the earliest token keeps a tie
+                        m[cb] = v;
+                        best[cb] = tk;
+                    }
+                }
+            }
+        }
+    }
+    // merge the four lane groups of every query row, then the waves
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+        for (int off = M; off < 64; off <<= 1) {
+            const float om = off == 32 ? xor32_f(m[cb], lane) : __shfl_xor(m[cb], off);
+            const int oi = off == 32 ? (int)xor32_u((unsigned)best[cb], lane) : __shfl_xor(best[cb], off);
+            if (om > m[cb] || (om == m[cb] && (unsigned)oi < (unsigned)best[cb])) {
+                m[cb] = om;
+                best[cb] = oi;
+            }
+        }
+        if (g == 0) {
+            rowmax_s[wave][cb * M + lm] = m[cb];
+            rowarg_s[wave][cb * M + lm] = best[cb];
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float mv = -INFINITY;
+    int idx = -1;
+    if (lane < nrows) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) {  // ties: the lower token index
+            const float om = rowmax_s[w][lane];
+            const int oi = rowarg_s[w][lane];
+            if (om > mv || (om == mv && (unsigned)oi < (unsigned)idx)) {
+                mv = om;
+                idx = oi;
+            }
+        }
+        rowmax_s[0][lane] = mv;  // only this wave reads it from here on
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the row maxima are in LDS
+    __builtin_amdgcn_wave_barrier();
+    const int Lq = p.Lq;
+    if (lane < nrows) {
+        const int q = lane / Lq, i = lane - q * Lq;
+        if (ARGMAX) p.argmax[((int64_t)q * p.B + b) * Lq + i] = idx;
+    }
+    if (lane < p.Nq) {  // query lane: its Lq row maxima in ascending order
+        float acc = 0.f;
+        for (int i = 0; i < Lq; ++i) acc += rowmax_s[0][lane * Lq + i];
+        p.scores[(int64_t)lane * p.B + b] = acc;
     }
 }
 
@@ -887,10 +1026,29 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream, int target_blocks) {
 }
 
 template <int ELEM, bool ARGMAX, bool VARLEN>
+hipError_t launch_tiny(const FwdArgs& a, hipStream_t stream) {
+    FwdParams p{};
+    p.Q = static_cast<const char*>(a.Q);
+    p.D = static_cast<const char*>(a.D);
+    p.lens = a.d_lens;
+    p.cu = a.cu;
+    p.T = a.T;
+    p.Nq = a.Nq;
+    p.Lq = a.Lq;
+    p.B = a.B;
+    p.Ld = a.Ld;
+    p.scores = a.scores;
+    p.argmax = a.argmax;
+    hipLaunchKernelGGL((fwd_tiny_kernel<ELEM, 4, 3, ARGMAX, VARLEN>), dim3((unsigned)a.B), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int ELEM, bool ARGMAX, bool VARLEN>
 hipError_t dispatch_shape(const FwdArgs& a, hipStream_t stream) {
     // Few query rows in all (single-query reranking): one 32-row slab, four
     // waves split each document's tokens; many small workgroups fill the chip.
     if ((int64_t)a.Nq * a.Lq <= 32) {
+        if constexpr (ELEM != kI8) return launch_tiny<ELEM, ARGMAX, VARLEN>(a, stream);
         return launch_cfg<ELEM, 16, 2, 1, 4, 1, 1, 3, ARGMAX, VARLEN>(a, stream, 2048);
     }
     // Otherwise one persistent workgroup per CU holding a slab of query rows.

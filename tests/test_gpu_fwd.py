@@ -82,6 +82,11 @@ SHAPES = [  # Nq, Lq, B, (Ld lo, hi)
     (2, 300, 4, (1, 513)),
     (1, 1024, 3, (1000, 1100)),
     (2, 1000, 2, (64, 64)),
+    # short queries (one 32-row block each): documents packed by 32-token
+    # sub-tile, many empty / one-token documents, bounds chunks crossed
+    (17, 24, 300, (0, 100)),
+    (2, 17, 5000, (1, 40)),
+    (16, 32, 2100, (0, 3)),
 ]
 
 
