@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--argmax", choices=["auto", "on", "off"], default="auto",
                     help="save the argmax in inference workloads (auto: as the workload specifies)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sustained", action="store_true",
+                    help="skip measuring the sustained MFMA rate (libmaxsim_probe.so) for the roofline")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only measure the sustained MFMA rate for f16, bf16 and int8 and exit")
     ap.add_argument("--no-graph", action="store_true",
                     help="tiny workload: time eager launches instead of HIP-graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
@@ -72,6 +76,60 @@ def calibrate_copy(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n, "reads_per_copy": n, "writes_per_copy": n}), flush=True)
+
+
+PROBE_KIND = {"f16": 0, "bf16": 1, "i8": 2}
+
+
+def sustained_peak(el, seconds=0.04):
+    """Matrix-core rate this GPU sustains for the kernel's MFMA instruction on
+    random operands shaped like the workload's data (libmaxsim_probe.so), in
+    TFLOP/s (TOP/s for int8): the power limit lowers the clock below the one
+    the published peak assumes."""
+    import ctypes
+    import torch
+    from late_interaction_retrieval_amd import build
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    lib.maxsim_probe_operand_bytes.restype = ctypes.c_size_t
+    lib.maxsim_probe_operand_bytes.argtypes = [ctypes.c_int32]
+    lib.maxsim_probe_ops_per_launch.restype = ctypes.c_double
+    lib.maxsim_probe_ops_per_launch.argtypes = [ctypes.c_int32] * 3
+    lib.maxsim_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    blocks = 256
+    nbytes = lib.maxsim_probe_operand_bytes(blocks)
+    rng = np.random.default_rng(1234)
+    if el == "i8":
+        host = rng.integers(-127, 128, size=nbytes, dtype=np.int8).view(np.uint8)
+    else:  # entries of l2-normalised 128-d rows: about N(0, 1/128)
+        x = (rng.standard_normal(nbytes // 2) / np.sqrt(128.0)).astype(np.float32)
+        host = (x.astype(np.float16).view(np.uint16) if el == "f16"
+                else inputs_bf16_bits(x)).view(np.uint8)
+    ops_dev = torch.from_numpy(np.ascontiguousarray(host)).to("cuda:0")
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    kind = PROBE_KIND[el]
+
+    def run(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = lib.maxsim_probe_mfma(kind, ctypes.c_void_p(ops_dev.data_ptr()), blocks, iters,
+                                   ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        assert rc == 0, "probe launch failed (%d)" % rc
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+    t = run(200)
+    iters = int(max(200, min(200000, 200 * seconds / max(t, 1e-6))))
+    run(iters)
+    t = run(iters)
+    return lib.maxsim_probe_ops_per_launch(kind, blocks, iters) / t / 1e12
+
+
+def inputs_bf16_bits(x):
+    from late_interaction_retrieval_amd import inputs
+    return inputs.f32_to_bf16_bits(x)
 
 
 def source_sha(kind):
@@ -110,6 +168,11 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.mfma_ceiling:
+        out = {el: round(sustained_peak(el, 0.1), 1) for el in ("f16", "bf16", "i8")}
+        print(json.dumps({"sustained_mfma_random_operands": out, "unit": "TFLOP/s (TOP/s for i8)",
+                          "published_dense_peak": {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0}}), flush=True)
         return
 
     import torch
@@ -312,6 +375,10 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
+    if roofline["bound"] == "mfma" and not args.no_sustained:
+        sp = sustained_peak(el)
+        roofline["sustained_peak"] = round(sp, 1)
+        roofline["frac_of_sustained"] = round(achieved / sp, 4)
     roofline.update({"traffic": traffic, "kernel": "fwd_kernel", "kernel_avg_ms": round(k_avg_ms, 5),
                      "kernel_median_ms": round(k_med_ms, 5), "algorithmic_flops_per_launch": fwd_flops,
                      "algorithmic_bytes_per_launch": fwd_bytes, "arithmetic_intensity": round(fwd_flops / fwd_bytes, 1),

@@ -33,11 +33,15 @@ def hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose=False, extra=()):
-    tmp = LIB + ".tmp%d" % os.getpid()
+PROBE_LIB = os.path.join(HERE, "libmaxsim_probe.so")
+PROBE_SOURCES = ["probe.hip"]
+
+
+def _compile(sources, lib, verbose, extra):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + [
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-    ] + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+    ] + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,8 +51,14 @@ def build(verbose=False, extra=()):
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose=False, extra=()):
+    """Build libmaxsim.so and the measurement aid libmaxsim_probe.so."""
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose, extra)
+    return _compile(SOURCES, LIB, verbose, extra)
 
 
 if __name__ == "__main__":

@@ -460,9 +460,37 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     // Per k-step the stage issues one MFMA per query block and folds VPL/KS
     // values of each of the previous stage's blocks (a fixed, hand-interleaved
     // order; the scheduling barrier keeps the compiler from regrouping it).
-    static_assert(M != 32 || VPL % KS == 0, "fold parts");
+    // int8 values are the exact products fl32(float(dot) * d_scale[token]).
+    static_assert(VPL % KS == 0, "fold parts");
     constexpr int FPS = VPL / KS;  // values folded per block per k-step
-    auto stage = [&](int bf, int sb, Acc* cur, const Acc* prev, bool has_prev, int gprev) {
+    auto stage_scales = [&](int bf, int sb) {
+        if constexpr (I8) {
+            return *reinterpret_cast<const f32x4*>(&dsc[bf][sb * M + 4 * g]);
+        } else {
+            return f32x4{1.f, 1.f, 1.f, 1.f};
+        }
+    };
+    auto value = [&](const Acc& acc, int i, const f32x4& sc) -> float {
+        if constexpr (I8) {
+            return (float)acc[i] * sc[i];
+        } else {
+            return acc[i];
+        }
+    };
+    // fold value v at slot i of block cb from global sub-tile gsub (unmasked)
+    auto fold_value = [&](int cb, float v, int i, int gsub, float& kt) {
+        if constexpr (KEYED) {
+            m[cb] = fmaxf(m[cb], v);
+            kt = fmaxf(kt, bitsf((fbits(v) & ~KMASK) | (KMASK - i)));
+        } else if constexpr (ARGMAX) {
+            const bool upd = v > m[cb];  // strict: the earliest token keeps a tie
+            m[cb] = upd ? v : m[cb];
+            code[cb] = upd ? ((gsub << 4) | i) : code[cb];
+        } else {
+            m[cb] = fmaxf(m[cb], v);
+        }
+    };
+    auto stage = [&](int bf, int sb, Acc* cur, const Acc* prev, const f32x4& sc_prev, bool has_prev, int gprev) {
         u32x4 a[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) a[s] = dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
@@ -477,21 +505,12 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             for (int cb = 0; cb < QB; ++cb) cur[cb] = MM::mma(a[s], bq[cb][s], cur[cb]);
             if (has_prev) {  // uniform
 #pragma unroll
-                for (int cb = 0; cb < QB; ++cb) {
-                    float mx = m[cb];
+                for (int cb = 0; cb < QB; ++cb)
 #pragma unroll
-                    for (int f = 0; f < FPS; ++f) mx = fmaxf(mx, prev[cb][s * FPS + f]);
-                    m[cb] = mx;
-                    if constexpr (KEYED) {
-                        float k2 = kt[cb];
-#pragma unroll
-                        for (int f = 0; f < FPS; ++f) {
-                            const int i = s * FPS + f;
-                            k2 = fmaxf(k2, bitsf((fbits(prev[cb][i]) & ~KMASK) | (KMASK - i)));
-                        }
-                        kt[cb] = k2;
+                    for (int f = 0; f < FPS; ++f) {
+                        const int i = s * FPS + f;
+                        fold_value(cb, value(prev[cb], i, sc_prev), i, gprev, kt[cb]);
                     }
-                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -508,28 +527,23 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     };
     // Fold a whole block of results (the last stage of a tile, which can be
     // partial: tokens at or past ln are -inf and never win).
-    auto fold = [&](auto mask_tag, const Acc* acc, int tok0, int ln, int gsub) {
+    auto fold = [&](auto mask_tag, const Acc* acc, const f32x4& sc, int tok0, int ln, int gsub) {
         constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb) {
-            float v[VPL];
-            bool valid[VPL];
+            float kt = -INFINITY;
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
-                valid[i] = !MASK || (tok0 + MM::tok(g, i) < ln);
-                v[i] = valid[i] ? acc[cb][i] : -INFINITY;
-            }
-            float mx = m[cb];
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) mx = fmaxf(mx, v[i]);
-            m[cb] = mx;
-            if constexpr (KEYED) {
-                float kt = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    const unsigned key = (fbits(v[i]) & ~KMASK) | (KMASK - i);
-                    kt = fmaxf(kt, valid[i] ? bitsf(key) : -INFINITY);
+                const bool valid = !MASK || (tok0 + MM::tok(g, i) < ln);
+                const float v = valid ? value(acc[cb], i, sc) : -INFINITY;
+                if constexpr (KEYED) {
+                    m[cb] = fmaxf(m[cb], v);
+                    kt = fmaxf(kt, valid ? bitsf((fbits(v) & ~KMASK) | (KMASK - i)) : -INFINITY);
+                } else {
+                    fold_value(cb, v, i, gsub, kt);
                 }
+            }
+            if constexpr (KEYED) {
                 const bool upd = kt > km[cb];  // strict: the earlier sub-tile keeps a tie
                 km[cb] = upd ? kt : km[cb];
                 code[cb] = upd ? gsub : code[cb];
@@ -542,28 +556,32 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         int nsub = (ln - tok_w + M - 1) / M;       // sub-tiles holding at least one valid token
         nsub = nsub < 0 ? 0 : (nsub > SPW ? SPW : nsub);
         Acc acc0[QB], acc1[QB];  // ping-pong accumulators (even / odd stages)
+        f32x4 sc0, sc1;          // their int8 token scales
         // stages are expanded at compile time so every accumulator index is static
         static_for<SPW>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             if (j >= nsub) return;  // uniform
             Acc* cur = (j & 1) ? acc1 : acc0;
             const Acc* prev = (j & 1) ? acc0 : acc1;
+            f32x4& sc_cur = (j & 1) ? sc1 : sc0;
+            const f32x4& sc_prev = (j & 1) ? sc0 : sc1;
             const int sb = wt * SPW + j;
             const int gsub = tt * SUBS + sb;
-            stage(bf, sb, cur, prev, j > 0, gsub - 1);
+            sc_cur = stage_scales(bf, sb);
+            stage(bf, sb, cur, prev, sc_prev, j > 0, gsub - 1);
             if (j == nsub - 1) {  // drain: fold the last sub-tile (the only one that can be partial)
                 const int tok0 = tok_w + j * M;
                 if (tok0 + M <= ln) {
-                    fold(std::false_type{}, cur, tok0, ln, gsub);
+                    fold(std::false_type{}, cur, sc_cur, tok0, ln, gsub);
                 } else {
-                    fold(std::true_type{}, cur, tok0, ln, gsub);
+                    fold(std::true_type{}, cur, sc_cur, tok0, ln, gsub);
                 }
             }
         });
     };
 
     auto compute_tile = [&](int bf, int tt, int ln) {
-        if constexpr (!I8 && M == 32 && QB <= 2) {  // two stages of accumulators fit in registers
+        if constexpr ((!I8 && M == 32 && QB <= 2) || I8) {  // two stages of accumulators fit in registers
             compute_tile_pipe(bf, tt, ln);
             return;
         }
@@ -1054,7 +1072,7 @@ hipError_t dispatch_shape(const FwdArgs& a, hipStream_t stream) {
     // Otherwise one persistent workgroup per CU holding a slab of query rows.
     if constexpr (ELEM == kI8) {
         // 1024 rows: 8 waves x 128 rows, 16x16x64 int8 blocks
-        return launch_cfg<ELEM, 16, 8, 8, 1, 8, 1, 3, ARGMAX, VARLEN>(a, stream, 256);
+        return launch_cfg<ELEM, 16, 8, 8, 1, 16, 1, 2, ARGMAX, VARLEN>(a, stream, 256);
     } else {
         if (a.Lq > 512 && a.Lq <= 768) {
             // 768-row slabs of whole queries: 8 waves x 96 rows, 2 waves per SIMD

@@ -149,3 +149,34 @@ def test_status_strings():
         s = L.maxsim_status_string(code).decode()
         assert s.startswith("MAXSIM_")
     assert "unknown" in L.maxsim_status_string(99).decode()
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "maxsim_probe.h")
+PROBE_LIB = os.path.join(ROOT, "late_interaction_retrieval_amd", "libmaxsim_probe.so")
+
+
+def test_probe_library_exports_and_validation():
+    """The measurement aid: every function maxsim_probe.h declares is exported;
+    invalid arguments are rejected before any launch."""
+    if not os.path.exists(PROBE_LIB):
+        from late_interaction_retrieval_amd import build
+        build.build()
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = set(re.findall(r"\b(maxsim_probe_\w+)\s*\(", text))
+    assert names == {"maxsim_probe_operand_bytes", "maxsim_probe_ops_per_launch", "maxsim_probe_mfma"}
+    pl = ctypes.CDLL(PROBE_LIB)
+    for n in names:
+        assert hasattr(pl, n), n
+    pl.maxsim_probe_operand_bytes.restype = ctypes.c_size_t
+    pl.maxsim_probe_operand_bytes.argtypes = [ctypes.c_int32]
+    assert pl.maxsim_probe_operand_bytes(0) == 0
+    assert pl.maxsim_probe_operand_bytes(2) == 2 * 8 * 64 * 12 * 16
+    pl.maxsim_probe_ops_per_launch.restype = ctypes.c_double
+    pl.maxsim_probe_ops_per_launch.argtypes = [ctypes.c_int32] * 3
+    assert pl.maxsim_probe_ops_per_launch(0, 1, 1) == 8 * 8 * 4 * 32768.0
+    pl.maxsim_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    assert pl.maxsim_probe_mfma(0, None, 1, 1, A, None) == 1
+    assert pl.maxsim_probe_mfma(0, A, 0, 1, A, None) == 2
+    assert pl.maxsim_probe_mfma(0, A, 1, 0, A, None) == 2
+    assert pl.maxsim_probe_mfma(7, A, 1, 1, A, None) == 3
