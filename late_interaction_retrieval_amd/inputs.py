@@ -186,6 +186,16 @@ def make(name, seed=0, B=None, Nq=None, Lq=None, Ld=None):
     return out
 
 
+def fp16_of_int8_workload(w, seed=0):
+    """fp16 versions (Q [Nq, Lq, d], D_packed [T, d]) of the same normalised
+    rows an int8 workload from ``make`` was quantised from: the rescoring
+    pass of the two-stage scan reads these."""
+    wid = WORKLOADS[w["name"]]["id"]
+    q = unit_rows(seed, wid, STREAM_Q, w["Nq"] * w["Lq"], w["d"], F16).reshape(w["Nq"], w["Lq"], w["d"])
+    dd = unit_rows(seed, wid, STREAM_D, w["T"], w["d"], F16)
+    return q, dd
+
+
 def random_rows(seed, n, d, dtype, workload_id=99, stream=STREAM_EXTRA):
     """Small helper for tests: n unit rows under an arbitrary id/stream."""
     return unit_rows(seed, workload_id, stream, n, d, dtype)

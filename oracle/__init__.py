@@ -20,4 +20,7 @@ from .oracle import (  # noqa: F401
     csr_build,
     bwd,
     num_threads,
+    fwd_pairs,
+    topk,
+    two_stage_topk,
 )

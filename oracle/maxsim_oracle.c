@@ -351,6 +351,69 @@ int oracle_bwd(const uint16_t* Q, const uint16_t* D, int dtype, const int32_t* a
 }
 
 /* Number of OpenMP threads a parallel region of the oracle uses. */
+/*
+ * Scores of an explicit list of (query, document) pairs over the packed
+ * corpus: pair p is query pq[p] against document pb[p] (Eq. (1), the same
+ * definition as oracle_fwd_varlen, evaluated only for the listed pairs).
+ * This is the rescoring step of the two-stage scan the pages list in the
+ * forward kernel family (Section 4.1 "Kernel Family": an INT8 pass ranks the
+ * corpus, the candidates are scored again in fp16).
+ * Outputs: scores [P] (fp64), argmax [P, Lq] (may be NULL).
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_fwd_pairs(const uint16_t* Q, const uint16_t* D, const int32_t* cu_seqlens, int dtype,
+                     const int32_t* pq, const int32_t* pb, int P, int Nq, int Lq, int B, int d,
+                     double* scores, int32_t* argmax) {
+    if (!Q || !cu_seqlens || !pq || !pb || !scores || P < 0 || Nq < 1 || Lq < 1 || B < 1 || d < 1) return -1;
+    for (int p = 0; p < P; ++p)
+        if (pq[p] < 0 || pq[p] >= Nq || pb[p] < 0 || pb[p] >= B) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int p = 0; p < P; ++p) {
+        const int q = pq[p], b = pb[p];
+        const int64_t first = cu_seqlens[b];
+        const int len = cu_seqlens[b + 1] - cu_seqlens[b];
+        double* qd = (double*)malloc(sizeof(double) * (size_t)Lq * d);
+        double* dd = (double*)malloc(sizeof(double) * ((size_t)len * d + 1));
+        for (int64_t e = 0; e < (int64_t)Lq * d; ++e) qd[e] = decode(Q[(int64_t)q * Lq * d + e], dtype);
+        for (int64_t e = 0; e < (int64_t)len * d; ++e) dd[e] = decode(D[first * d + e], dtype);
+        scores[p] = pair_score(qd, dd, Lq, len, d, argmax ? argmax + (int64_t)p * Lq : NULL, NULL);
+        free(qd);
+        free(dd);
+    }
+    return 0;
+}
+
+/*
+ * Top-K of each query's row of scores [Nq, B]: the K documents with the
+ * largest scores, best first; equal scores are ordered by ascending document
+ * index (the selection the two-stage scan keeps, Section 4.1 "Kernel
+ * Family").  A full sort per query: plain and slow.
+ * Outputs: idx [Nq, K], val [Nq, K].  Returns 0, or -1 on a bad argument.
+ */
+static const float* topk_row;
+static int topk_cmp(const void* a, const void* b) {
+    const int32_t i = *(const int32_t*)a, j = *(const int32_t*)b;
+    const float si = topk_row[i], sj = topk_row[j];
+    if (si > sj) return -1;
+    if (si < sj) return 1;
+    return (i > j) - (i < j);
+}
+int oracle_topk(const float* scores, int Nq, int B, int K, int32_t* idx, float* val) {
+    if (!scores || !idx || !val || Nq < 1 || B < 1 || K < 1 || K > B) return -1;
+    int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
+    for (int q = 0; q < Nq; ++q) {
+        for (int b = 0; b < B; ++b) order[b] = b;
+        topk_row = scores + (int64_t)q * B;
+        qsort(order, (size_t)B, sizeof(int32_t), topk_cmp);
+        for (int k = 0; k < K; ++k) {
+            idx[(int64_t)q * K + k] = order[k];
+            val[(int64_t)q * K + k] = topk_row[order[k]];
+        }
+    }
+    free(order);
+    return 0;
+}
+
 int oracle_num_threads(void) {
     int n = 1;
 #pragma omp parallel

@@ -58,8 +58,11 @@ def _load():
         lib.oracle_sim_at.argtypes = [P, P, P, I, I, I, I, I, P, P]
         lib.oracle_csr_build.argtypes = [P, I, I, I, I, P, P]
         lib.oracle_bwd.argtypes = [P, P, I, P, P, I, I, I, I, I, P, P]
+        lib.oracle_fwd_pairs.argtypes = [P, P, P, I, P, P, I, I, I, I, I, P, P]
+        lib.oracle_topk.argtypes = [P, I, I, I, P, P]
         for name in ("oracle_fwd_padded", "oracle_fwd_varlen", "oracle_fwd_i8", "oracle_sim_at",
-                     "oracle_csr_build", "oracle_bwd", "oracle_num_threads"):
+                     "oracle_csr_build", "oracle_bwd", "oracle_num_threads", "oracle_fwd_pairs",
+                     "oracle_topk"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -185,3 +188,52 @@ def bwd(Q, D, dtype, argmax, g):
 
 def num_threads():
     return int(_load().oracle_num_threads())
+
+
+def fwd_pairs(Q, D_packed, cu_seqlens, dtype, pairs_q, pairs_b, want_argmax=True):
+    """Scores (fp64) [and argmax [P, Lq]] of the listed (query, document) pairs."""
+    Qb, Db = _bits16(Q), _bits16(D_packed)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    pq = np.ascontiguousarray(pairs_q, dtype=np.int32)
+    pb = np.ascontiguousarray(pairs_b, dtype=np.int32)
+    Nq, Lq, d = Qb.shape
+    B = cu.shape[0] - 1
+    P = pq.shape[0]
+    assert pb.shape == (P,) and Db.shape[1] == d
+    s = np.zeros(P, np.float64)
+    a = np.zeros((P, Lq), np.int32) if want_argmax else None
+    rc = _load().oracle_fwd_pairs(_p(Qb), _p(Db), _p(cu), dtype, _p(pq), _p(pb), P, Nq, Lq, B, d, _p(s), _p(a))
+    _check(rc, "fwd_pairs")
+    return (s, a) if want_argmax else s
+
+
+def topk(scores, K):
+    """Per query row of float32 scores: (indices [Nq, K], values [Nq, K]),
+    best first, equal scores by ascending index."""
+    sc = np.ascontiguousarray(scores, dtype=np.float32)
+    Nq, B = sc.shape
+    idx = np.zeros((Nq, K), np.int32)
+    val = np.zeros((Nq, K), np.float32)
+    rc = _load().oracle_topk(_p(sc), Nq, B, K, _p(idx), _p(val))
+    _check(rc, "topk")
+    return idx, val
+
+
+def two_stage_topk(Q8, q_scale, D8, d_scale, Q16, D16, cu_seqlens, dtype, K1, K2):
+    """The two-stage scan as a composition of the plain definitions: INT8 scores
+    of every pair, each query's top-K1 candidates (oracle_topk), fp16/bf16
+    scores of those candidates in fp64, their K2 best (a stable sort by
+    descending score).  Returns (candidates [Nq, K1], their int8 scores,
+    final documents [Nq, K2], final fp64 scores [Nq, K2])."""
+    s8, _ = fwd_i8(Q8, q_scale, D8, d_scale, cu_seqlens)
+    cand, cval = topk(s8, K1)
+    Nq = cand.shape[0]
+    pq = np.repeat(np.arange(Nq, dtype=np.int32), K1)
+    s16 = fwd_pairs(Q16, D16, cu_seqlens, dtype, pq, cand.reshape(-1), want_argmax=False).reshape(Nq, K1)
+    final = np.empty((Nq, K2), np.int32)
+    fval = np.empty((Nq, K2), np.float64)
+    for q in range(Nq):
+        order = np.lexsort((cand[q], -s16[q]))[:K2]  # score descending, then document index
+        final[q] = cand[q][order]
+        fval[q] = s16[q][order]
+    return cand, cval, final, fval

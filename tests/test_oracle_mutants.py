@@ -13,7 +13,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "maxsim_oracle.c")
-PINS = ["tests/test_oracle_fwd.py", "tests/test_oracle_i8.py", "tests/test_oracle_bwd.py"]
+PINS = ["tests/test_oracle_fwd.py", "tests/test_oracle_i8.py", "tests/test_oracle_bwd.py",
+        "tests/test_oracle_topk.py"]
 
 MUTANTS = {
     "tie_takes_last_index": ("            if (s > m) {\n                m = s;\n                arg = j;",
@@ -31,6 +32,12 @@ MUTANTS = {
     "dD_wrong_operand": ("ddr[k] += gqb * decode(qrow[k], dtype);", "ddr[k] += gqb * decode(drow[k], dtype);"),
     "dQ_transposed_upstream": ("double gqb = (double)g[(int64_t)q * B + b];",
                                "double gqb = (double)g[(int64_t)b * Nq + q];"),
+    "topk_ties_by_descending_index": ("    return (i > j) - (i < j);", "    return (i < j) - (i > j);"),
+    "topk_ascending_scores": ("    if (si > sj) return -1;\n    if (si < sj) return 1;",
+                              "    if (si > sj) return 1;\n    if (si < sj) return -1;"),
+    "pairs_wrong_document_start": ("        const int64_t first = cu_seqlens[b];", "        const int64_t first = cu_seqlens[q];"),
+    "pairs_wrong_query": ("++e) qd[e] = decode(Q[(int64_t)q * Lq * d + e], dtype);",
+                          "++e) qd[e] = decode(Q[(int64_t)(Nq - 1 - q) * Lq * d + e], dtype);"),
 }
 
 
