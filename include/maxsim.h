@@ -136,6 +136,56 @@ int maxsim_bwd(const void* Q, const void* D, int32_t dtype, const int32_t* argma
                float* dQ, float* dD, int32_t* row_ptr, int32_t* col_idx, void* workspace,
                size_t workspace_bytes, void* stream);
 
+/*
+ * Scores of an explicit list of (query, document) pairs over a packed corpus
+ * (Eq. (1) for each listed pair only).  This is the rescoring pass of the
+ * two-stage INT8 -> fp16 scan the pages list in the forward kernel family
+ * (Section 4.1 "Kernel Family"), where each query has its own candidates.
+ *   Q [Nq, Lq, d] and D_packed [T, d] (dtype), cu_seqlens [B+1] as for
+ *   maxsim_fwd_varlen; pair p is query pair_q[p] against document pair_b[p]
+ *   (device int32 arrays of P entries, 0 <= pair_q < Nq, 0 <= pair_b < B;
+ *   entries out of range are clamped into range).
+ *   scores [P] fp32 out; argmax [P, Lq] int32 out or NULL (exact first index
+ *   on ties; -1 and -inf for an empty document).
+ * Requires d = 128, 1 <= Lq <= 1024, P >= 0 (P = 0 does nothing).
+ */
+int maxsim_fwd_pairs(const void* Q, const void* D_packed, const int32_t* cu_seqlens, int32_t dtype,
+                     const int32_t* pair_q, const int32_t* pair_b, int32_t P, int32_t Nq, int32_t Lq,
+                     int32_t B, int64_t T, int32_t d, float* scores, int32_t* argmax, void* stream);
+
+/*
+ * Top-K of every query's row of scores [Nq, B] fp32 (the selection of the
+ * two-stage scan, Section 4.1 "Kernel Family"): top_idx [Nq, K] and
+ * top_score [Nq, K] out, best first; equal scores are ordered by ascending
+ * id, where the id of entry (q, j) is ids[q*B + j] when ids (device int32
+ * [Nq, B], values >= 0) is given, else j.  top_idx holds the ids.
+ * -0.0 and +0.0 are equal scores (reported as +0.0).
+ * Requires 1 <= K <= min(B, 1024).  NaN scores are not supported.
+ */
+int maxsim_topk(const float* scores, const int32_t* ids, int32_t Nq, int32_t B, int32_t K, int32_t* top_idx,
+                float* top_score, void* stream);
+
+/* Bytes of device workspace maxsim_two_stage_topk needs (0 on bad sizes). */
+size_t maxsim_two_stage_workspace_bytes(int32_t Nq, int32_t B, int32_t K1);
+
+/*
+ * The two-stage scan (Section 4.1 "Kernel Family"): INT8 x INT8 scores of
+ * every (query, document) pair (maxsim_fwd_i8), each query's K1 best
+ * documents (maxsim_topk), their fp16/bf16 scores from Q16 / D16, the same
+ * rows unquantised (maxsim_fwd_pairs), and the K2 best of those.
+ *   cand [Nq, K1], cand_score8 [Nq, K1] out: the candidates and INT8 scores;
+ *   top_idx [Nq, K2], top_score [Nq, K2] out: the final documents and
+ *   fp16/bf16 scores, best first, equal scores by ascending document index.
+ * workspace: device scratch of maxsim_two_stage_workspace_bytes() bytes,
+ * 256-byte aligned.  Requires 1 <= K2 <= K1 <= min(B, 1024); the other
+ * arguments as for maxsim_fwd_i8 and maxsim_fwd_pairs.
+ */
+int maxsim_two_stage_topk(const int8_t* Q8, const float* q_scale, const int8_t* D8, const float* d_scale,
+                          const void* Q16, const void* D16, const int32_t* cu_seqlens, int32_t dtype16,
+                          int32_t Nq, int32_t Lq, int32_t B, int64_t T, int32_t max_Ld, int32_t d,
+                          int32_t K1, int32_t K2, int32_t* cand, float* cand_score8, int32_t* top_idx,
+                          float* top_score, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* maxsim_status_string(int status);
 

@@ -36,6 +36,11 @@ SIGNATURES = {
     "maxsim_bwd_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "maxsim_bwd": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
+    "maxsim_fwd_pairs": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32, _P, _P, _P]),
+    "maxsim_topk": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, _P]),
+    "maxsim_two_stage_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "maxsim_two_stage_topk": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32, _I32,
+                                             _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "maxsim_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -233,3 +238,91 @@ class MaxSimFunction(torch.autograd.Function):
 def maxsim(Q, D):
     """All-pairs MaxSim scores [Nq, B] with autograd support."""
     return MaxSimFunction.apply(Q, D)
+
+
+def maxsim_fwd_pairs(Q, D_packed, cu_seqlens, pair_q, pair_b, scores=None, argmax=None, with_argmax=False,
+                     stream=None):
+    """Scores [P] (and argmax [P, Lq]) of the listed (query, document) pairs over a packed corpus."""
+    Nq, Lq, d = Q.shape
+    T, d2 = D_packed.shape
+    B = cu_seqlens.shape[0] - 1
+    P = pair_q.shape[0]
+    if d2 != d or Q.dtype != D_packed.dtype:
+        raise ValueError("Q and D_packed must share dtype and width")
+    dev = Q.device
+    _need(Q, "Q")
+    _need(D_packed, "D_packed", device=dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _need(pair_q, "pair_q", torch.int32, dev)
+    _need(pair_b, "pair_b", torch.int32, dev)
+    if pair_b.shape[0] != P:
+        raise ValueError("pair_q and pair_b must have the same length")
+    if scores is None:
+        scores = torch.empty(P, dtype=torch.float32, device=dev)
+    _need(scores, "scores", torch.float32, dev)
+    if argmax is None and with_argmax:
+        argmax = torch.empty((P, Lq), dtype=torch.int32, device=dev)
+    if argmax is not None:
+        _need(argmax, "argmax", torch.int32, dev)
+    st = lib().maxsim_fwd_pairs(_ptr(Q), _ptr(D_packed), _ptr(cu_seqlens), _dtype_code(Q), _ptr(pair_q),
+                                _ptr(pair_b), P, Nq, Lq, B, T, d, _ptr(scores), _ptr(argmax), _stream(Q, stream))
+    _check(st, "maxsim_fwd_pairs")
+    return scores, argmax
+
+
+def maxsim_topk(scores, K, ids=None, top_idx=None, top_score=None, stream=None):
+    """Per row of scores [Nq, B] fp32: (top_idx [Nq, K] int32, top_score [Nq, K]), best first,
+    equal scores by ascending id (ids [Nq, B] int32 if given, else the column)."""
+    Nq, B = scores.shape
+    dev = scores.device
+    _need(scores, "scores", torch.float32)
+    if ids is not None:
+        _need(ids, "ids", torch.int32, dev)
+        if ids.shape != scores.shape:
+            raise ValueError("ids must have the shape of scores")
+    if top_idx is None:
+        top_idx = torch.empty((Nq, K), dtype=torch.int32, device=dev)
+    if top_score is None:
+        top_score = torch.empty((Nq, K), dtype=torch.float32, device=dev)
+    _need(top_idx, "top_idx", torch.int32, dev)
+    _need(top_score, "top_score", torch.float32, dev)
+    st = lib().maxsim_topk(_ptr(scores), _ptr(ids), Nq, B, K, _ptr(top_idx), _ptr(top_score),
+                           _stream(scores, stream))
+    _check(st, "maxsim_topk")
+    return top_idx, top_score
+
+
+def maxsim_two_stage_workspace_bytes(Nq, B, K1):
+    return int(lib().maxsim_two_stage_workspace_bytes(Nq, B, K1))
+
+
+def maxsim_two_stage_topk(Q8, q_scale, D8, d_scale, Q16, D16, cu_seqlens, max_Ld, K1, K2, workspace=None,
+                          stream=None):
+    """INT8 scan of the whole corpus, each query's K1 best re-scored in fp16 / bf16 from Q16 / D16,
+    the K2 best kept.  Returns (cand [Nq, K1], cand_score8, top_idx [Nq, K2], top_score)."""
+    Nq, Lq, d = Q8.shape
+    T = D8.shape[0]
+    B = cu_seqlens.shape[0] - 1
+    dev = Q8.device
+    _need(Q8, "Q8", torch.int8)
+    _need(D8, "D8", torch.int8, dev)
+    _need(q_scale, "q_scale", torch.float32, dev)
+    _need(d_scale, "d_scale", torch.float32, dev)
+    _need(Q16, "Q16", device=dev)
+    _need(D16, "D16", device=dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if Q16.shape != Q8.shape or D16.shape != D8.shape or Q16.dtype != D16.dtype:
+        raise ValueError("Q16 / D16 must be the fp16 or bf16 rows of Q8 / D8")
+    nbytes = maxsim_two_stage_workspace_bytes(Nq, B, K1)
+    if workspace is None:
+        workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=dev)
+    cand = torch.empty((Nq, K1), dtype=torch.int32, device=dev)
+    cand8 = torch.empty((Nq, K1), dtype=torch.float32, device=dev)
+    top_idx = torch.empty((Nq, K2), dtype=torch.int32, device=dev)
+    top_score = torch.empty((Nq, K2), dtype=torch.float32, device=dev)
+    st = lib().maxsim_two_stage_topk(_ptr(Q8), _ptr(q_scale), _ptr(D8), _ptr(d_scale), _ptr(Q16), _ptr(D16),
+                                     _ptr(cu_seqlens), _dtype_code(Q16), Nq, Lq, B, T, int(max_Ld), d, K1, K2,
+                                     _ptr(cand), _ptr(cand8), _ptr(top_idx), _ptr(top_score), _ptr(workspace),
+                                     workspace.numel(), _stream(Q8, stream))
+    _check(st, "maxsim_two_stage_topk")
+    return cand, cand8, top_idx, top_score

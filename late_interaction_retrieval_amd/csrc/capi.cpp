@@ -155,6 +155,84 @@ int maxsim_bwd(const void* Q, const void* D, int32_t dtype, const int32_t* argma
     return hip_status(maxsim::launch_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
+int maxsim_fwd_pairs(const void* Q, const void* D_packed, const int32_t* cu_seqlens, int32_t dtype,
+                     const int32_t* pair_q, const int32_t* pair_b, int32_t P, int32_t Nq, int32_t Lq,
+                     int32_t B, int64_t T, int32_t d, float* scores, int32_t* argmax, void* stream) {
+    if (P < 0 || Nq < 1 || B < 1 || Lq < 1 || T < 0) return MAXSIM_ERR_SHAPE;
+    if (d != kDim || Lq > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_UNSUPPORTED;
+    if (P == 0) return MAXSIM_OK;
+    if (!Q || !cu_seqlens || !pair_q || !pair_b || !scores || (T > 0 && !D_packed)) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D_packed, 16) || !aligned(cu_seqlens, 4) || !aligned(pair_q, 4) ||
+        !aligned(pair_b, 4) || !aligned(scores, 4) || !aligned(argmax, 4))
+        return MAXSIM_ERR_ALIGN;
+    maxsim::FwdArgs a{};
+    a.Q = Q;
+    a.D = D_packed;
+    a.cu = cu_seqlens;
+    a.Nq = Nq;
+    a.Lq = Lq;
+    a.B = B;
+    a.T = T;
+    a.scores = scores;
+    a.argmax = argmax;
+    a.elem = dtype == MAXSIM_BF16 ? maxsim::kBF16 : maxsim::kF16;
+    a.varlen = true;
+    return hip_status(maxsim::launch_fwd_pairs(a, pair_q, pair_b, P, static_cast<hipStream_t>(stream)));
+}
+
+int maxsim_topk(const float* scores, const int32_t* ids, int32_t Nq, int32_t B, int32_t K, int32_t* top_idx,
+                float* top_score, void* stream) {
+    if (Nq < 0 || B < 1 || K < 1 || K > B) return MAXSIM_ERR_SHAPE;
+    if (K > maxsim::kMaxTopK) return MAXSIM_ERR_UNSUPPORTED;
+    if (Nq == 0) return MAXSIM_OK;
+    if (!scores || !top_idx || !top_score) return MAXSIM_ERR_NULL;
+    if (!aligned(scores, 4) || !aligned(ids, 4) || !aligned(top_idx, 4) || !aligned(top_score, 4))
+        return MAXSIM_ERR_ALIGN;
+    return hip_status(maxsim::launch_topk(scores, ids, Nq, B, K, top_idx, top_score, static_cast<hipStream_t>(stream)));
+}
+
+size_t maxsim_two_stage_workspace_bytes(int32_t Nq, int32_t B, int32_t K1) {
+    if (Nq < 1 || B < 1 || K1 < 1) return 0;
+    const size_t s8 = ((size_t)Nq * B * sizeof(float) + 255) / 256 * 256;
+    const size_t pq = ((size_t)Nq * K1 * sizeof(int32_t) + 255) / 256 * 256;
+    const size_t s16 = (size_t)Nq * K1 * sizeof(float);
+    return s8 + pq + s16;
+}
+
+int maxsim_two_stage_topk(const int8_t* Q8, const float* q_scale, const int8_t* D8, const float* d_scale,
+                          const void* Q16, const void* D16, const int32_t* cu_seqlens, int32_t dtype16,
+                          int32_t Nq, int32_t Lq, int32_t B, int64_t T, int32_t max_Ld, int32_t d,
+                          int32_t K1, int32_t K2, int32_t* cand, float* cand_score8, int32_t* top_idx,
+                          float* top_score, void* workspace, size_t workspace_bytes, void* stream) {
+    if (Nq < 1 || B < 1 || K1 < 1 || K1 > B || K2 < 1 || K2 > K1) return MAXSIM_ERR_SHAPE;
+    if ((int64_t)Nq * K1 >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
+    if (K1 > maxsim::kMaxTopK) return MAXSIM_ERR_UNSUPPORTED;
+    if (!workspace || !cand || !cand_score8 || !top_idx || !top_score) return MAXSIM_ERR_NULL;
+    if (!aligned(workspace, 256) || !aligned(cand, 4) || !aligned(cand_score8, 4) || !aligned(top_idx, 4) ||
+        !aligned(top_score, 4))
+        return MAXSIM_ERR_ALIGN;
+    if (workspace_bytes < maxsim_two_stage_workspace_bytes(Nq, B, K1)) return MAXSIM_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    float* s8 = reinterpret_cast<float*>(ws);
+    int32_t* pq = reinterpret_cast<int32_t*>(ws + ((size_t)Nq * B * sizeof(float) + 255) / 256 * 256);
+    float* s16 = reinterpret_cast<float*>(reinterpret_cast<char*>(pq) +
+                                          ((size_t)Nq * K1 * sizeof(int32_t) + 255) / 256 * 256);
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    // 1. INT8 scores of every pair
+    int st = maxsim_fwd_i8(Q8, q_scale, D8, d_scale, cu_seqlens, Nq, Lq, B, T, max_Ld, d, s8, nullptr, stream);
+    if (st != MAXSIM_OK) return st;
+    // 2. each query's K1 best documents
+    st = maxsim_topk(s8, nullptr, Nq, B, K1, cand, cand_score8, stream);
+    if (st != MAXSIM_OK) return st;
+    // 3. fp16 / bf16 scores of the candidates
+    if (maxsim::launch_fill_pair_q(pq, (int64_t)Nq * K1, K1, hs) != hipSuccess) return MAXSIM_ERR_HIP;
+    st = maxsim_fwd_pairs(Q16, D16, cu_seqlens, dtype16, pq, cand, Nq * K1, Nq, Lq, B, T, d, s16, nullptr, stream);
+    if (st != MAXSIM_OK) return st;
+    // 4. their K2 best, ties by document index
+    return maxsim_topk(s16, cand, Nq, K1, K2, top_idx, top_score, stream);
+}
+
 const char* maxsim_status_string(int status) {
     switch (status) {
         case MAXSIM_OK: return "MAXSIM_OK";

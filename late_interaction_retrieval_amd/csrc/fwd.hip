@@ -874,39 +874,35 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     }
 }
 
-// Few query rows in all (Nq * Lq <= 32, e.g. one ColBERT query): the work per
-// document token is tiny and the kernel is bound by reading D.  One workgroup
-// per document; each of its W waves takes SPL 16-token sub-tiles per round
-// and loads them straight from HBM into MFMA operand registers (no LDS
-// staging, no barrier until the end), all of a round's loads in flight at
-// once.  Lane group g reads 16 contiguous bytes at chunk s*4 + g of its row in
-// k-step s, so one load instruction covers 64 contiguous bytes of 16 rows.
-// The argmax is exact (first index on ties).  The waves' row results meet in
-// LDS once at the end.
-template <int ELEM, int W, int SPL, bool ARGMAX, bool VARLEN>
-__global__ __launch_bounds__(64 * W) void fwd_tiny_kernel(FwdParams p) {
+// One workgroup of W waves scores up to 32 query rows (rows 0 .. nr-1 from
+// `qrows`, 256 bytes apart) against one document (first row st, len tokens).
+// The work per document token is tiny, so this is bound by reading D: each
+// wave takes SPL 16-token sub-tiles per round and loads them straight from
+// HBM into MFMA operand registers (no LDS staging, no barrier until the end),
+// all of a round's loads in flight at once.  Lane group g reads 16
+// contiguous bytes at chunk s*4 + g of its row in k-step s, so one load
+// instruction covers 64 contiguous bytes of 16 rows.  The argmax is exact
+// (first index on ties).  On return, lanes r < nr of wave 0 hold row r's
+// maximum and argmax (other waves' values are unspecified); every wave must
+// call it (it contains a workgroup barrier).
+template <int ELEM, int W, int SPL>
+__device__ __forceinline__ void rows_vs_doc(const FwdParams& p, const char* qrows, int nr, int64_t st, int len,
+                                            float (*rowmax_s)[32], int (*rowarg_s)[32], float& mv, int& idx) {
     using MM = Mma<ELEM, 16>;
     using Acc = typename MM::Acc;
     constexpr int M = 16, NG = MM::NG, KS = MM::KS, VPL = MM::VPL, ROWB = 256;
-    __shared__ float rowmax_s[W][2 * M];
-    __shared__ int rowarg_s[W][2 * M];
-    const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane / M, lm = lane % M;
-    int64_t st;
-    int len;
-    doc_info<VARLEN>(p, b, st, len);
-    const int nrows = p.Nq * p.Lq;  // <= 32: two 16-row blocks
     u32x4 bq[2][KS];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
         const int r = cb * M + lm;
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2)
-            bq[cb][s2] = r < nrows ? *reinterpret_cast<const u32x4*>(p.Q + (int64_t)r * ROWB + (s2 * NG + g) * 16)
-                                   : u32x4{0u, 0u, 0u, 0u};
+            bq[cb][s2] = r < nr ? *reinterpret_cast<const u32x4*>(qrows + (int64_t)r * ROWB + (s2 * NG + g) * 16)
+                                : u32x4{0u, 0u, 0u, 0u};
     }
     float m[2] = {-INFINITY, -INFINITY};
     int best[2] = {-1, -1};  // token index of the maximum (first on ties)
@@ -961,10 +957,9 @@ __global__ __launch_bounds__(64 * W) void fwd_tiny_kernel(FwdParams p) {
         }
     }
     __syncthreads();
-    if (wave != 0) return;
-    float mv = -INFINITY;
-    int idx = -1;
-    if (lane < nrows) {
+    mv = -INFINITY;
+    idx = -1;
+    if (wave == 0 && lane < nr) {
 #pragma unroll
         for (int w = 0; w < W; ++w) {  // ties: the lower token index
             const float om = rowmax_s[w][lane];
@@ -974,9 +969,30 @@ __global__ __launch_bounds__(64 * W) void fwd_tiny_kernel(FwdParams p) {
                 idx = oi;
             }
         }
-        rowmax_s[0][lane] = mv;  // only this wave reads it from here on
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the row maxima are in LDS
+    __syncthreads();  // the LDS rows may be reused by the caller
+}
+
+// Few query rows in all (Nq * Lq <= 32, e.g. one ColBERT query): one
+// workgroup per document scores every row (rows_vs_doc); wave 0 writes the
+// argmax and the per-query sums.
+template <int ELEM, int W, int SPL, bool ARGMAX, bool VARLEN>
+__global__ __launch_bounds__(64 * W) void fwd_tiny_kernel(FwdParams p) {
+    __shared__ float rowmax_s[W][32];
+    __shared__ int rowarg_s[W][32];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int64_t st;
+    int len;
+    doc_info<VARLEN>(p, b, st, len);
+    const int nrows = p.Nq * p.Lq;  // <= 32
+    float mv;
+    int idx;
+    rows_vs_doc<ELEM, W, SPL>(p, p.Q, nrows, st, len, rowmax_s, rowarg_s, mv, idx);
+    if (wave != 0) return;
+    if (lane < nrows) rowmax_s[0][lane] = mv;  // only this wave reads it from here on
+    __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): the row maxima are in LDS
     __builtin_amdgcn_wave_barrier();
     const int Lq = p.Lq;
     if (lane < nrows) {
@@ -988,6 +1004,42 @@ __global__ __launch_bounds__(64 * W) void fwd_tiny_kernel(FwdParams p) {
         for (int i = 0; i < Lq; ++i) acc += rowmax_s[0][lane * Lq + i];
         p.scores[(int64_t)lane * p.B + b] = acc;
     }
+}
+
+// An explicit list of (query, document) pairs over the packed corpus (the
+// rescoring pass of the two-stage scan): one workgroup per pair, the query's
+// rows in blocks of 32 (rows_vs_doc each), the block sums added in order.
+// scores[p] and argmax[p, Lq] follow the list.
+template <int ELEM, int W, int SPL, bool ARGMAX>
+__global__ __launch_bounds__(64 * W) void fwd_pairs_kernel(FwdParams p, const int32_t* pq, const int32_t* pb) {
+    __shared__ float rowmax_s[W][32];
+    __shared__ int rowarg_s[W][32];
+    const int pair = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int q = ((cint_ptr)pq)[pair];
+    int b = ((cint_ptr)pb)[pair];
+    q = q < 0 ? 0 : (q >= p.Nq ? p.Nq - 1 : q);  // out-of-range pairs break the contract; keep accesses in bounds
+    b = b < 0 ? 0 : (b >= p.B ? p.B - 1 : b);
+    int64_t st;
+    int len;
+    doc_info<true>(p, b, st, len);
+    const int Lq = p.Lq;
+    float total = 0.f;
+    for (int r0 = 0; r0 < Lq; r0 += 32) {  // uniform
+        const int nr = Lq - r0 < 32 ? Lq - r0 : 32;
+        float mv;
+        int idx;
+        rows_vs_doc<ELEM, W, SPL>(p, p.Q + ((int64_t)q * Lq + r0) * 256, nr, st, len, rowmax_s, rowarg_s, mv, idx);
+        if (wave == 0) {
+            if (ARGMAX && lane < nr) p.argmax[(int64_t)pair * Lq + r0 + lane] = idx;
+            // rows of the block in ascending order: lane 0 gathers them
+            float part = 0.f;
+            for (int i = 0; i < nr; ++i) part += __shfl(mv, i);
+            total += part;
+        }
+    }
+    if (wave == 0 && lane == 0) p.scores[pair] = total;
 }
 
 __global__ __launch_bounds__(256) void zero_fill(float* x, int64_t n) {
@@ -1061,6 +1113,22 @@ hipError_t launch_tiny(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int ELEM, bool ARGMAX>
+hipError_t launch_pairs(const FwdArgs& a, const int32_t* pq, const int32_t* pb, int32_t P, hipStream_t stream) {
+    FwdParams p{};
+    p.Q = static_cast<const char*>(a.Q);
+    p.D = static_cast<const char*>(a.D);
+    p.cu = a.cu;
+    p.T = a.T;
+    p.Nq = a.Nq;
+    p.Lq = a.Lq;
+    p.B = a.B;
+    p.scores = a.scores;
+    p.argmax = a.argmax;
+    hipLaunchKernelGGL((fwd_pairs_kernel<ELEM, 4, 3, ARGMAX>), dim3((unsigned)P), dim3(256), 0, stream, p, pq, pb);
+    return hipGetLastError();
+}
+
 template <int ELEM, bool ARGMAX, bool VARLEN>
 hipError_t dispatch_shape(const FwdArgs& a, hipStream_t stream) {
     // Few query rows in all (single-query reranking): one 32-row slab, four
@@ -1091,6 +1159,19 @@ hipError_t dispatch_argmax(const FwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_fwd_pairs(const FwdArgs& a, const int32_t* pq, const int32_t* pb, int32_t P, hipStream_t stream) {
+    if (P == 0) return hipSuccess;
+    const bool am = a.argmax != nullptr;
+    switch (a.elem) {
+        case kF16:
+            return am ? launch_pairs<kF16, true>(a, pq, pb, P, stream) : launch_pairs<kF16, false>(a, pq, pb, P, stream);
+        case kBF16:
+            return am ? launch_pairs<kBF16, true>(a, pq, pb, P, stream) : launch_pairs<kBF16, false>(a, pq, pb, P, stream);
+        default:
+            return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     if (a.Nq == 0 || a.B == 0) return hipSuccess;

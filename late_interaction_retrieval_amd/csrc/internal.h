@@ -30,6 +30,14 @@ struct FwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// scores of the listed (query, document) pairs over a packed corpus (a.varlen)
+hipError_t launch_fwd_pairs(const FwdArgs& a, const int32_t* pair_q, const int32_t* pair_b, int32_t P,
+                            hipStream_t stream);
+
+constexpr int kMaxTopK = 1024;  // K of one top-K selection (LDS sort)
+hipError_t launch_topk(const float* scores, const int32_t* ids, int Nq, int B, int K, int32_t* idx, float* val,
+                       hipStream_t stream);
+hipError_t launch_fill_pair_q(int32_t* pair_q, int64_t n, int K1, hipStream_t stream);
 
 struct BwdArgs {
     const void* Q;            // [Nq, Lq, 128]

@@ -44,7 +44,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported_with_binding_arity():
     decl = declared_functions()
     assert set(decl) == {"maxsim_fwd", "maxsim_fwd_varlen", "maxsim_fwd_i8", "maxsim_bwd_workspace_bytes",
-                         "maxsim_bwd", "maxsim_status_string"}
+                         "maxsim_bwd", "maxsim_status_string", "maxsim_fwd_pairs", "maxsim_topk",
+                         "maxsim_two_stage_workspace_bytes", "maxsim_two_stage_topk"}
     raw = ctypes.CDLL(LIB)
     for name, nargs in decl.items():
         assert hasattr(raw, name), name
@@ -180,3 +181,34 @@ def test_probe_library_exports_and_validation():
     assert pl.maxsim_probe_mfma(0, A, 0, 1, A, None) == 2
     assert pl.maxsim_probe_mfma(0, A, 1, 0, A, None) == 2
     assert pl.maxsim_probe_mfma(7, A, 1, 1, A, None) == 3
+
+
+def test_pairs_topk_two_stage_validation():
+    ok, NULL, SHAPE, UNSUP, ALIGN, WS = (bd.MAXSIM_OK, bd.MAXSIM_ERR_NULL, bd.MAXSIM_ERR_SHAPE,
+                                         bd.MAXSIM_ERR_UNSUPPORTED, bd.MAXSIM_ERR_ALIGN, bd.MAXSIM_ERR_WORKSPACE)
+    # pairs: Q, D, cu, dtype, pq, pb, P, Nq, Lq, B, T, d, scores, argmax, stream
+    assert L.maxsim_fwd_pairs(A, A, A, 0, A, A, 0, 2, 32, 3, 10, 128, A, None, None) == ok  # P = 0: nothing
+    assert L.maxsim_fwd_pairs(A, A, A, 0, A, A, -1, 2, 32, 3, 10, 128, A, None, None) == SHAPE
+    assert L.maxsim_fwd_pairs(A, A, A, 0, A, A, 4, 2, 1025, 3, 10, 128, A, None, None) == UNSUP
+    assert L.maxsim_fwd_pairs(A, A, A, 0, A, A, 4, 2, 32, 3, 10, 64, A, None, None) == UNSUP
+    assert L.maxsim_fwd_pairs(A, A, A, 2, A, A, 4, 2, 32, 3, 10, 128, A, None, None) == UNSUP
+    assert L.maxsim_fwd_pairs(A, A, A, 0, None, A, 4, 2, 32, 3, 10, 128, A, None, None) == NULL
+    assert L.maxsim_fwd_pairs(M, A, A, 0, A, A, 4, 2, 32, 3, 10, 128, A, None, None) == ALIGN
+    # topk: scores, ids, Nq, B, K, idx, val, stream
+    assert L.maxsim_topk(A, None, 2, 10, 11, A, A, None) == SHAPE
+    assert L.maxsim_topk(A, None, 2, 10, 0, A, A, None) == SHAPE
+    assert L.maxsim_topk(A, None, 2, 5000, 1025, A, A, None) == UNSUP
+    assert L.maxsim_topk(A, None, 0, 10, 3, A, A, None) == ok
+    assert L.maxsim_topk(None, None, 2, 10, 3, A, A, None) == NULL
+    assert L.maxsim_topk(A, M, 2, 10, 3, A, A, None) == ALIGN
+    # two-stage: workspace size and argument checks happen before any launch
+    need = L.maxsim_two_stage_workspace_bytes(2, 10, 4)
+    assert need == 256 + 256 + 2 * 4 * 4
+    assert L.maxsim_two_stage_workspace_bytes(0, 10, 4) == 0
+    args = lambda K1, K2, ws, nbytes: L.maxsim_two_stage_topk(A, A, A, A, A, A, A, 0, 2, 32, 10, 100, 20, 128,
+                                                              K1, K2, A, A, A, A, ws, nbytes, None)
+    assert args(4, 5, A, need) == SHAPE
+    assert args(11, 2, A, need) == SHAPE
+    assert args(4, 2, A, need - 1) == WS
+    assert args(4, 2, ctypes.c_void_p(0x10010), need) == ALIGN
+    assert args(4, 2, None, need) == NULL
