@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="colbert_rerank_varlen",
                     choices=["colbert_rerank_varlen", "colbert_tiny", "colpali_fwd", "contrastive_train",
-                             "int8_varlen"])
+                             "int8_varlen", "two_stage_topk"])
     ap.add_argument("--argmax", choices=["auto", "on", "off"], default="auto",
                     help="save the argmax in inference workloads (auto: as the workload specifies)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -176,6 +176,10 @@ def main():
         return
 
     import torch
+
+    if args.workload == "two_stage_topk":
+        bench_two_stage(args)
+        return
 
     lib_path = os.path.join(ROOT, "late_interaction_retrieval_amd", "libmaxsim.so")
     if not os.path.exists(lib_path):
@@ -424,6 +428,122 @@ def main():
     }
     if extra:
         out["extra"] = extra
+    print(json.dumps(out), flush=True)
+
+
+def bench_two_stage(args, B=30000, K1=100, K2=10):
+    """The two-stage scan (a next step beyond the hot path): 32 ColBERT-length
+    queries against an INT8 corpus shaped like the int8 workload (B documents of
+    32..512 tokens), each query's K1 best re-scored in fp16, K2 kept.  A step is
+    one maxsim_two_stage_topk call.  The roofline is that of its INT8 stage
+    (timed alone on the same data)."""
+    import torch
+    from late_interaction_retrieval_amd import binding as bd
+    from late_interaction_retrieval_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = inputs.make("int8_varlen", B=B)
+    Q16h, D16h = inputs.fp16_of_int8_workload(w)
+    Nq, Lq, d, T = w["Nq"], w["Lq"], w["d"], w["T"]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    Q8, qs, D8, ds, cu = t(w["Q"]), t(w["q_scale"]), t(w["D_packed"]), t(w["d_scale"]), t(w["cu_seqlens"])
+    Q16, D16 = t(Q16h), t(D16h)
+    max_ld = int(w["lens"].max())
+    ws = torch.empty(max(256, bd.maxsim_two_stage_workspace_bytes(Nq, B, K1)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    s8 = torch.empty((Nq, B), dtype=torch.float32, device=dev)
+
+    def step(timed, pool):
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        out = bd.maxsim_two_stage_topk(Q8, qs, D8, ds, Q16, D16, cu, max_ld, K1, K2, workspace=ws)
+        if timed:
+            e1.record(stream)
+            pool.append((e0, e1))
+        return out
+
+    def int8_stage(timed, pool):
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        bd.maxsim_fwd_i8(Q8, qs, D8, ds, cu, max_ld, scores=s8, with_argmax=False)
+        if timed:
+            e1.record(stream)
+            pool.append((e0, e1))
+
+    for _ in range(3):
+        cand = step(False, None)[0]
+    torch.cuda.synchronize()
+    steps = args.steps if args.steps is not None else 100
+    warmup = args.warmup if args.warmup is not None else 10
+    for _ in range(warmup):
+        step(False, None)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    pool, pool8 = [], []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True, pool)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    peak_mem = torch.cuda.max_memory_allocated(dev)
+    for _ in range(steps):
+        int8_stage(True, pool8)
+    torch.cuda.synchronize()
+    step_ms = float(np.mean([a.elapsed_time(b) for a, b in pool]))
+    i8_ms = float(np.mean([a.elapsed_time(b) for a, b in pool8]))
+    lens = np.diff(w["cu_seqlens"])
+    cand_tokens = int(lens[cand.cpu().numpy()].sum())  # doc tokens the rescoring pass reads
+    ops8 = 2.0 * Nq * Lq * d * T
+    ops16 = 2.0 * Lq * d * cand_tokens
+    value = (ops8 + ops16) * steps / elapsed / 1e12
+    i8_bytes = T * (d + 4) + Nq * Lq * (d + 4) + 4 * (B + 1) + 4 * Nq * B
+    achieved = ops8 / (i8_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS["i8"], "unit": "TOP/s",
+                "frac": round(achieved / MFMA_PEAK_TFLOPS["i8"], 4), "traffic": None,
+                "kernel": "fwd_kernel (INT8 stage)", "kernel_avg_ms": round(i8_ms, 5),
+                "algorithmic_flops_per_launch": ops8, "algorithmic_bytes_per_launch": i8_bytes,
+                "stage_share_of_step": round(i8_ms / step_ms, 4)}
+    if not args.no_sustained:
+        sp = sustained_peak("i8")
+        roofline["sustained_peak"] = round(sp, 1)
+        roofline["frac_of_sustained"] = round(achieved / sp, 4)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = 200
+        while True:
+            sub = inputs.make("int8_varlen", B=n)
+            q16s, d16s = inputs.fp16_of_int8_workload(sub)
+            t1 = time.perf_counter()
+            oracle.two_stage_topk(sub["Q"], sub["q_scale"], sub["D_packed"], sub["d_scale"], q16s, d16s,
+                                  sub["cu_seqlens"], oracle.F16, min(K1, n), min(K2, n))
+            tc = time.perf_counter() - t1
+            if tc > 0.5 * args.cpu_seconds or n >= B:
+                break
+            n = int(min(B, n * max(2.0, 0.8 * args.cpu_seconds / max(tc, 1e-3))))
+        ops_c = 2.0 * Nq * Lq * d * int(sub["T"]) + 2.0 * Lq * d * int(np.diff(sub["cu_seqlens"]).mean() * Nq * min(K1, n))
+        cpu = {"value": round(ops_c / tc / 1e12, 6), "unit": "TOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "%d queries x first %d documents of the same corpus, K1=%d, K2=%d, %.1f s" %
+                         (Nq, n, min(K1, n), min(K2, n), tc)}
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(elapsed * 1e3 / steps, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8+f16",
+        "data": "synthetic (seeded N(0,1) rows, l2-normalised; int8 per-token quantised, fp16 of the same rows)",
+        "config": {"workload": "two_stage_topk", "Nq": Nq, "Lq": Lq, "B": B, "T_doc_tokens": T, "d": d,
+                   "Ld_range": [int(lens.min()), int(lens.max())], "K1": K1, "K2": K2,
+                   "rescored_doc_tokens": cand_tokens, "layout": "cu_seqlens"},
+        "queries_per_s": round(Nq * steps / elapsed, 1),
+        "doc_tokens_per_s": round(T * steps / elapsed, 1),
+        "step_event_ms": round(step_ms, 5),
+        "peak_mem_bytes": int(peak_mem),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
     print(json.dumps(out), flush=True)
 
 
