@@ -23,4 +23,6 @@ from .oracle import (  # noqa: F401
     fwd_pairs,
     topk,
     two_stage_topk,
+    csr_build_varlen,
+    bwd_varlen,
 )

@@ -350,7 +350,89 @@ int oracle_bwd(const uint16_t* Q, const uint16_t* D, int dtype, const int32_t* a
     return 0;
 }
 
-/* Number of OpenMP threads a parallel region of the oracle uses. */
+/*
+ * The backward over a packed (cu_seqlens) corpus: Section 4.2 Algorithm 3
+ * with the destination row of source s = (q*B + b)*Lq + i read as
+ * dst(s) = cu_seqlens[b] + argmax[s] (the packed row of the selected token;
+ * Section 4.3 "Padding-Free Variable-Length" keeps only real tokens).  An
+ * empty document (its argmax is -1) has no rows: its sources select nothing,
+ * add nothing to dQ and appear in no CSR row.
+ *   row_ptr [T + 1]: exclusive prefix sum of the per-row counts (row_ptr[T]
+ *                    is the number of sources that select a row),
+ *   col_idx [row_ptr[T]]: stable argsort of dst over those sources.
+ * Returns 0, or -1 if an argmax of a non-empty document is out of range.
+ */
+int oracle_csr_build_varlen(const int32_t* argmax, int Nq, int B, int Lq, const int32_t* cu_seqlens,
+                            int32_t* row_ptr, int32_t* col_idx) {
+    const int64_t nsrc = (int64_t)Nq * B * Lq;
+    const int64_t T = cu_seqlens[B];
+    int64_t* cnt = (int64_t*)calloc((size_t)T + 1, sizeof(int64_t));
+    for (int64_t s = 0; s < nsrc; ++s) {
+        const int64_t b = (s / Lq) % B;
+        const int len = cu_seqlens[b + 1] - cu_seqlens[b];
+        if (len == 0) continue;
+        const int32_t t = argmax[s];
+        if (t < 0 || t >= len) {
+            free(cnt);
+            return -1;
+        }
+        cnt[cu_seqlens[b] + t] += 1;
+    }
+    row_ptr[0] = 0;
+    for (int64_t r = 0; r < T; ++r) row_ptr[r + 1] = (int32_t)(row_ptr[r] + cnt[r]);
+    int64_t* cursor = cnt;
+    for (int64_t r = 0; r < T; ++r) cursor[r] = row_ptr[r];
+    for (int64_t s = 0; s < nsrc; ++s) {
+        const int64_t b = (s / Lq) % B;
+        if (cu_seqlens[b + 1] == cu_seqlens[b]) continue;
+        const int64_t dst = cu_seqlens[b] + argmax[s];
+        col_idx[cursor[dst]] = (int32_t)s;
+        cursor[dst] += 1;
+    }
+    free(cnt);
+    return 0;
+}
+
+/*
+ * Closed-form gradients (Section 4.2, Eqs. (dq), (dd)) over a packed corpus:
+ *   dQ[q, i, :] = sum over non-empty b of g[q, b] * D_packed[cu[b] + t*, :]
+ *   dD[cu[b] + t, :] = sum over (q, i) with t*(q, b, i) = t of g[q, b] * Q[q, i, :]
+ * The plain definition in fp64, as oracle_bwd.  D_packed [T, d], dD [T, d].
+ */
+int oracle_bwd_varlen(const uint16_t* Q, const uint16_t* D, const int32_t* cu_seqlens, int dtype,
+                      const int32_t* argmax, const float* g, int Nq, int Lq, int B, int d, double* dQ,
+                      double* dD) {
+    const int64_t T = cu_seqlens[B];
+    for (int q = 0; q < Nq; ++q)
+        for (int b = 0; b < B; ++b) {
+            const int len = cu_seqlens[b + 1] - cu_seqlens[b];
+            for (int i = 0; i < Lq; ++i) {
+                const int32_t t = argmax[((int64_t)q * B + b) * Lq + i];
+                if (len > 0 && (t < 0 || t >= len)) return -1;
+            }
+        }
+    memset(dQ, 0, sizeof(double) * (size_t)Nq * Lq * d);
+    memset(dD, 0, sizeof(double) * (size_t)T * d);
+    for (int q = 0; q < Nq; ++q) {
+        for (int b = 0; b < B; ++b) {
+            if (cu_seqlens[b + 1] == cu_seqlens[b]) continue;
+            const double gqb = (double)g[(int64_t)q * B + b];
+            for (int i = 0; i < Lq; ++i) {
+                const int64_t row = cu_seqlens[b] + argmax[((int64_t)q * B + b) * Lq + i];
+                const uint16_t* qrow = Q + ((int64_t)q * Lq + i) * d;
+                const uint16_t* drow = D + row * d;
+                double* dq = dQ + ((int64_t)q * Lq + i) * d;
+                double* ddr = dD + row * d;
+                for (int k = 0; k < d; ++k) {
+                    dq[k] += gqb * decode(drow[k], dtype);
+                    ddr[k] += gqb * decode(qrow[k], dtype);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
 /*
  * Scores of an explicit list of (query, document) pairs over the packed
  * corpus: pair p is query pq[p] against document pb[p] (Eq. (1), the same
@@ -414,6 +496,7 @@ int oracle_topk(const float* scores, int Nq, int B, int K, int32_t* idx, float* 
     return 0;
 }
 
+/* Number of OpenMP threads a parallel region of the oracle uses. */
 int oracle_num_threads(void) {
     int n = 1;
 #pragma omp parallel

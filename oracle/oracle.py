@@ -60,9 +60,11 @@ def _load():
         lib.oracle_bwd.argtypes = [P, P, I, P, P, I, I, I, I, I, P, P]
         lib.oracle_fwd_pairs.argtypes = [P, P, P, I, P, P, I, I, I, I, I, P, P]
         lib.oracle_topk.argtypes = [P, I, I, I, P, P]
+        lib.oracle_csr_build_varlen.argtypes = [P, I, I, I, P, P, P]
+        lib.oracle_bwd_varlen.argtypes = [P, P, P, I, P, P, I, I, I, I, P, P]
         for name in ("oracle_fwd_padded", "oracle_fwd_varlen", "oracle_fwd_i8", "oracle_sim_at",
                      "oracle_csr_build", "oracle_bwd", "oracle_num_threads", "oracle_fwd_pairs",
-                     "oracle_topk"):
+                     "oracle_topk", "oracle_csr_build_varlen", "oracle_bwd_varlen"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -237,3 +239,31 @@ def two_stage_topk(Q8, q_scale, D8, d_scale, Q16, D16, cu_seqlens, dtype, K1, K2
         final[q] = cand[q][order]
         fval[q] = s16[q][order]
     return cand, cval, final, fval
+
+
+def csr_build_varlen(argmax, cu_seqlens):
+    """argmax [Nq, B, Lq] over a packed corpus -> (row_ptr [T+1], col_idx [row_ptr[T]])."""
+    A = np.ascontiguousarray(argmax, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    Nq, B, Lq = A.shape
+    T = int(cu[-1])
+    row_ptr = np.empty(T + 1, np.int32)
+    col_idx = np.empty(Nq * B * Lq, np.int32)
+    _check(_load().oracle_csr_build_varlen(_p(A), Nq, B, Lq, _p(cu), _p(row_ptr), _p(col_idx)), "csr_build_varlen")
+    return row_ptr, col_idx[:row_ptr[-1]]
+
+
+def bwd_varlen(Q, D_packed, cu_seqlens, dtype, argmax, g):
+    """Packed-corpus backward -> (dQ [Nq, Lq, d], dD [T, d]) in fp64."""
+    Qb, Db = _bits16(Q), _bits16(D_packed)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    A = np.ascontiguousarray(argmax, dtype=np.int32)
+    gg = np.ascontiguousarray(g, dtype=np.float32)
+    Nq, Lq, d = Qb.shape
+    B = cu.shape[0] - 1
+    T = int(cu[-1])
+    dQ = np.empty((Nq, Lq, d), np.float64)
+    dD = np.empty((T, d), np.float64)
+    _check(_load().oracle_bwd_varlen(_p(Qb), _p(Db), _p(cu), dtype, _p(A), _p(gg), Nq, Lq, B, d, _p(dQ), _p(dD)),
+           "bwd_varlen")
+    return dQ, dD

@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "maxsim_oracle.c")
 PINS = ["tests/test_oracle_fwd.py", "tests/test_oracle_i8.py", "tests/test_oracle_bwd.py",
-        "tests/test_oracle_topk.py"]
+        "tests/test_oracle_topk.py", "tests/test_oracle_bwd_varlen.py"]
 
 MUTANTS = {
     "tie_takes_last_index": ("            if (s > m) {\n                m = s;\n                arg = j;",
@@ -36,6 +36,9 @@ MUTANTS = {
     "topk_ascending_scores": ("    if (si > sj) return -1;\n    if (si < sj) return 1;",
                               "    if (si > sj) return 1;\n    if (si < sj) return -1;"),
     "pairs_wrong_document_start": ("        const int64_t first = cu_seqlens[b];", "        const int64_t first = cu_seqlens[q];"),
+    "varlen_csr_row_of_next_document": ("        cnt[cu_seqlens[b] + t] += 1;", "        cnt[cu_seqlens[b + 1] - 1 - t] += 1;"),
+    "varlen_bwd_empty_doc_not_skipped": ("            if (cu_seqlens[b + 1] == cu_seqlens[b]) continue;\n            const double gqb",
+                                         "            const double gqb"),
     "pairs_wrong_query": ("++e) qd[e] = decode(Q[(int64_t)q * Lq * d + e], dtype);",
                           "++e) qd[e] = decode(Q[(int64_t)(Nq - 1 - q) * Lq * d + e], dtype);"),
 }
