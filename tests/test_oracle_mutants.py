@@ -27,11 +27,23 @@ MUTANTS = {
     "i8_query_scale_dropped": ("float v = m * q_scale[(int64_t)q * Lq + i];", "float v = m;"),
     "i8_doc_scale_of_wrong_token": ("float s = (float)dot * d_scale[first + j];",
                                     "float s = (float)dot * d_scale[first];"),
-    "csr_cursor_not_advanced": ("        cursor[dst] += 1;\n", "\n"),
+    "csr_cursor_not_advanced": ("        int64_t dst = b * Ld + argmax[s];\n        col_idx[cursor[dst]] = (int32_t)s;\n        cursor[dst] += 1;\n",
+                                "        int64_t dst = b * Ld + argmax[s];\n        col_idx[cursor[dst]] = (int32_t)s;\n"),
     "csr_wrong_doc_stride": ("        cnt[b * Ld + t] += 1;", "        cnt[t * B + b] += 1;"),
-    "dD_wrong_operand": ("ddr[k] += gqb * decode(qrow[k], dtype);", "ddr[k] += gqb * decode(drow[k], dtype);"),
-    "dQ_transposed_upstream": ("double gqb = (double)g[(int64_t)q * B + b];",
-                               "double gqb = (double)g[(int64_t)b * Nq + q];"),
+    "dD_wrong_operand": ("double* ddr = dD + ((int64_t)b * Ld + t) * d;\n                for (int k = 0; k < d; ++k) {\n"
+                         "                    dq[k] += gqb * decode(drow[k], dtype);\n"
+                         "                    ddr[k] += gqb * decode(qrow[k], dtype);",
+                         "double* ddr = dD + ((int64_t)b * Ld + t) * d;\n                for (int k = 0; k < d; ++k) {\n"
+                         "                    dq[k] += gqb * decode(drow[k], dtype);\n"
+                         "                    ddr[k] += gqb * decode(drow[k], dtype);"),
+    "dQ_transposed_upstream": ("++b) {\n            double gqb = (double)g[(int64_t)q * B + b];",
+                               "++b) {\n            double gqb = (double)g[(int64_t)b * Nq + q];"),
+    "varlen_dD_wrong_operand": ("double* ddr = dD + row * d;\n                for (int k = 0; k < d; ++k) {\n"
+                                "                    dq[k] += gqb * decode(drow[k], dtype);\n"
+                                "                    ddr[k] += gqb * decode(qrow[k], dtype);",
+                                "double* ddr = dD + row * d;\n                for (int k = 0; k < d; ++k) {\n"
+                                "                    dq[k] += gqb * decode(drow[k], dtype);\n"
+                                "                    ddr[k] += gqb * decode(drow[k], dtype);"),
     "topk_ties_by_descending_index": ("    return (i > j) - (i < j);", "    return (i < j) - (i > j);"),
     "topk_ascending_scores": ("    if (si > sj) return -1;\n    if (si < sj) return 1;",
                               "    if (si > sj) return 1;\n    if (si < sj) return -1;"),
