@@ -136,6 +136,38 @@ int maxsim_bwd(const void* Q, const void* D, int32_t dtype, const int32_t* argma
                float* dQ, float* dD, int32_t* row_ptr, int32_t* col_idx, void* workspace,
                size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace maxsim_bwd_varlen needs (0 on bad sizes). */
+size_t maxsim_bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld);
+
+/*
+ * Backward over padding-free documents (Section 4.2, Algorithm 3, with the
+ * packed layout of Section 4.3 "Padding-Free Variable-Length").
+ *   Q [Nq, Lq, d] and D_packed [T, d] (dtype), cu_seqlens [B+1] as for
+ *   maxsim_fwd_varlen (cu_seqlens[B] = T, every length <= max_Ld), argmax
+ *   [Nq, B, Lq] int32 from maxsim_fwd_varlen (local to the document),
+ *   grad_scores [Nq, B] fp32.
+ * A source s = (q*B + b)*Lq + i selects the packed row cu_seqlens[b] +
+ * argmax[s]; an empty document has no rows and its sources select nothing
+ * (their argmax and grad_scores entries are ignored).
+ *   row_ptr [T + 1] out: exclusive prefix of the per-row counts, so that
+ *           row_ptr[T] = Nq*Lq * (number of non-empty documents);
+ *   col_idx [Nq*B*Lq] out (capacity): the first row_ptr[T] entries hold the
+ *           sources of row r in ascending s at col_idx[row_ptr[r] ..
+ *           row_ptr[r+1]); the rest is left unspecified;
+ *   dD [T, d] fp32 out (Eq. (dd)), rows with no source are 0;
+ *   dQ [Nq, Lq, d] fp32 out (Eq. (dq)), summed over the non-empty documents.
+ * T = 0 is allowed (D_packed and dD may then be NULL; dQ is all zero).
+ * workspace: device scratch of maxsim_bwd_varlen_workspace_bytes() bytes,
+ * 256-byte aligned; its contents on entry do not matter.  Requires Nq, B >= 1,
+ * 1 <= Lq <= 1024, 1 <= max_Ld <= 4096, Nq*B*Lq < 2^31, T < 2^31.  A
+ * malformed cu_seqlens gives unspecified gradients but no access outside
+ * the buffers.
+ */
+int maxsim_bwd_varlen(const void* Q, const void* D_packed, const int32_t* cu_seqlens, int32_t dtype,
+                      const int32_t* argmax, const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B,
+                      int64_t T, int32_t max_Ld, int32_t d, float* dQ, float* dD, int32_t* row_ptr,
+                      int32_t* col_idx, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Scores of an explicit list of (query, document) pairs over a packed corpus
  * (Eq. (1) for each listed pair only).  This is the rescoring pass of the

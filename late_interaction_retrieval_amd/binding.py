@@ -36,6 +36,9 @@ SIGNATURES = {
     "maxsim_bwd_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "maxsim_bwd": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
+    "maxsim_bwd_varlen_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
+    "maxsim_bwd_varlen": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _P, _P,
+                                         _P, _P, _P, ctypes.c_size_t, _P]),
     "maxsim_fwd_pairs": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32, _P, _P, _P]),
     "maxsim_topk": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, _P]),
     "maxsim_two_stage_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
@@ -215,6 +218,46 @@ def maxsim_bwd(Q, D, argmax, grad_scores, dQ=None, dD=None, row_ptr=None, col_id
                           _ptr(dQ), _ptr(dD), _ptr(row_ptr), _ptr(col_idx), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream(Q, stream))
     _check(st, "maxsim_bwd")
+    return dQ, dD, row_ptr, col_idx
+
+
+def maxsim_bwd_varlen_workspace_bytes(Nq, B, Lq, max_Ld):
+    return int(lib().maxsim_bwd_varlen_workspace_bytes(Nq, B, Lq, max_Ld))
+
+
+def maxsim_bwd_varlen(Q, D_packed, cu_seqlens, max_Ld, argmax, grad_scores, dQ=None, dD=None, row_ptr=None,
+                      col_idx=None, workspace=None, stream=None):
+    """Backward over a packed corpus.  Returns (dQ [Nq, Lq, d], dD [T, d], row_ptr [T+1], col_idx
+    [Nq*B*Lq], of which the first row_ptr[T] entries are defined)."""
+    Nq, Lq, d = Q.shape
+    T, d2 = D_packed.shape
+    B = cu_seqlens.shape[0] - 1
+    if d2 != d or Q.dtype != D_packed.dtype:
+        raise ValueError("Q and D_packed must share dtype and width")
+    dev = Q.device
+    _need(Q, "Q")
+    _need(D_packed, "D_packed", device=dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _need(argmax, "argmax", torch.int32, dev)
+    _need(grad_scores, "grad_scores", torch.float32, dev)
+    if dQ is None:
+        dQ = torch.empty((Nq, Lq, d), dtype=torch.float32, device=dev)
+    if dD is None:
+        dD = torch.empty((T, d), dtype=torch.float32, device=dev)
+    if row_ptr is None:
+        row_ptr = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(Nq * B * Lq, dtype=torch.int32, device=dev)
+    nbytes = maxsim_bwd_varlen_workspace_bytes(Nq, B, Lq, int(max_Ld))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    for t, n in ((dQ, "dQ"), (dD, "dD"), (row_ptr, "row_ptr"), (col_idx, "col_idx"), (workspace, "workspace")):
+        _need(t, n, device=dev)
+    st = lib().maxsim_bwd_varlen(_ptr(Q), _ptr(D_packed), _ptr(cu_seqlens), _dtype_code(Q), _ptr(argmax),
+                                 _ptr(grad_scores), Nq, Lq, B, T, int(max_Ld), d, _ptr(dQ), _ptr(dD), _ptr(row_ptr),
+                                 _ptr(col_idx), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(Q, stream))
+    _check(st, "maxsim_bwd_varlen")
     return dQ, dD, row_ptr, col_idx
 
 

@@ -50,9 +50,74 @@ struct BwdParams {
     // floor(n / (B*Lq)) for 0 <= n < 2^31 as (n * magic) >> (32 + shift)
     unsigned long long magic;
     int shift;
+    // floor(n / Lq) likewise
+    unsigned long long magic_lq;
+    int shift_lq;
+    // packed corpus: cu_seqlens [B+1] (nullptr: padded documents of Ld rows),
+    // T rows, and each document's first CSR slot [B+1] (workspace)
+    const int32_t* cu;
+    int64_t T;
+    int32_t* docbase;
 };
 
 __device__ __forceinline__ int clamp_tok(int t, int Ld) { return t < 0 ? 0 : (t >= Ld ? Ld - 1 : t); }
+
+// First row and number of rows of document b.  Packed documents longer than
+// Ld (the stated maximum) are cut to Ld so every LDS index stays in range.
+__device__ __forceinline__ void doc_rows(const BwdParams& p, int b, int64_t& start, int& len) {
+    if (p.cu) {
+        int64_t s0 = p.cu[b], s1 = p.cu[b + 1];
+        s0 = s0 < 0 ? 0 : (s0 > p.T ? p.T : s0);
+        s1 = s1 < s0 ? s0 : (s1 > p.T ? p.T : s1);
+        start = s0;
+        len = (int)(s1 - s0 < p.Ld ? s1 - s0 : p.Ld);
+    } else {
+        start = (int64_t)b * p.Ld;
+        len = p.Ld;
+    }
+}
+
+// First col_idx slot of document b: its sources follow those of the earlier
+// non-empty documents.
+__device__ __forceinline__ int doc_base(const BwdParams& p, int b) {
+    return p.docbase ? p.docbase[b] : b * p.Nq * p.Lq;
+}
+
+// Packed corpus: docbase[b] = Nq*Lq * (number of non-empty documents before b),
+// b = 0 .. B.  One workgroup of 1024 threads scans the documents in order.
+__global__ __launch_bounds__(1024) void csr_docbase(BwdParams p) {
+    __shared__ int wsum[16];
+    __shared__ int carry_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    const int per = p.Nq * p.Lq;
+    for (int b0 = 0; b0 <= p.B; b0 += 1024) {
+        const int b = b0 + tid;
+        int flag = 0;
+        if (b < p.B) {
+            int64_t st;
+            int len;
+            doc_rows(p, b, st, len);
+            flag = len > 0;
+        }
+        int x = flag;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        int wpre = 0;
+        for (int w = 0; w < wave; ++w) wpre += wsum[w];
+        const int carry = carry_s;
+        if (b <= p.B) p.docbase[b] = (carry + wpre + x - flag) * per;
+        __syncthreads();
+        if (tid == 1023) carry_s = carry + wpre + x;
+        __syncthreads();
+    }
+}
 
 __global__ __launch_bounds__(1024) void csr_count(BwdParams p) {
     extern __shared__ int hist[];  // [Ld]
@@ -63,9 +128,12 @@ __global__ __launch_bounds__(1024) void csr_count(BwdParams p) {
     __syncthreads();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int q = qg * p.G + wave;
-    if (q < p.Nq) {
+    int64_t st;
+    int len;
+    doc_rows(p, b, st, len);
+    if (q < p.Nq && len > 0) {  // an empty document has no rows and no sources
         const int32_t* a = p.A + ((int64_t)q * p.B + b) * p.Lq;
-        for (int i = lane; i < p.Lq; i += 64) atomicAdd(&hist[clamp_tok(a[i], p.Ld)], 1);
+        for (int i = lane; i < p.Lq; i += 64) atomicAdd(&hist[clamp_tok(a[i], len)], 1);
     }
     __syncthreads();
     int32_t* out = p.ws + ((int64_t)b * p.NG + qg) * p.Ld;
@@ -80,14 +148,17 @@ __global__ __launch_bounds__(1024) void csr_scan(BwdParams p) {
     __shared__ int carry_s;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t doc_base = (int64_t)b * p.Nq * p.Lq;
+    const int base = doc_base(p, b);
+    int64_t rstart;
+    int len;
+    doc_rows(p, b, rstart, len);
     int32_t* ws = p.ws + (int64_t)b * p.NG * p.Ld;
     if (tid == 0) carry_s = 0;
     __syncthreads();
-    for (int t0 = 0; t0 < p.Ld; t0 += 1024) {
+    for (int t0 = 0; t0 < len; t0 += 1024) {
         const int t = t0 + tid;
         int tot = 0;
-        if (t < p.Ld) {
+        if (t < len) {
             for (int g0 = 0; g0 < p.NG; g0 += 16) {
                 int c[16];
 #pragma unroll
@@ -109,9 +180,9 @@ __global__ __launch_bounds__(1024) void csr_scan(BwdParams p) {
         for (int w = 0; w < wave; ++w) wpre += wsum[w];
         const int carry = carry_s;
         const int excl = carry + wpre + x - tot;
-        if (t < p.Ld) {
-            int run = (int)(doc_base + excl);
-            p.row_ptr[(int64_t)b * p.Ld + t] = run;
+        if (t < len) {
+            int run = base + excl;
+            p.row_ptr[rstart + t] = run;
             for (int g0 = 0; g0 < p.NG; g0 += 16) {
                 int c[16];
 #pragma unroll
@@ -127,7 +198,10 @@ __global__ __launch_bounds__(1024) void csr_scan(BwdParams p) {
         if (tid == 1023) carry_s = carry + wpre + x;
         __syncthreads();
     }
-    if (b == p.B - 1 && tid == 0) p.row_ptr[(int64_t)p.B * p.Ld] = (int)((int64_t)p.B * p.Nq * p.Lq);
+    if (b == p.B - 1 && tid == 0) {  // one past the last row: the number of sources that select a row
+        const int64_t nrows = p.cu ? p.T : (int64_t)p.B * p.Ld;
+        p.row_ptr[nrows] = p.docbase ? p.docbase[p.B] : p.B * p.Nq * p.Lq;
+    }
 }
 
 // One wave per query of the group.  Dynamic LDS: G*Ld int (next slot per
@@ -146,12 +220,16 @@ __global__ __launch_bounds__(1024) void csr_fill(BwdParams p) {
     int* slot = lds;                                            // [G][Ld]
     unsigned* mask = reinterpret_cast<unsigned*>(lds + p.G * Ld);  // [G][Ld][2]
     const int q = qg * p.G + wave;
+    int64_t rstart;
+    int len;
+    doc_rows(p, b, rstart, len);
+    if (len == 0) return;  // uniform: an empty document has no sources
     const int32_t* a = p.A + ((int64_t)q * p.B + b) * p.Lq;
     int tk[kFillIt];  // -1: no source in this lane for step k
 #pragma unroll
     for (int k = 0; k < kFillIt; ++k) {
         const int i = k * 64 + lane;
-        tk[k] = (q < p.Nq && i < p.Lq) ? clamp_tok(a[i], Ld) : -1;
+        tk[k] = (q < p.Nq && i < p.Lq) ? clamp_tok(a[i], len) : -1;
     }
     for (int e = tid; e < p.G * Ld; e += nt) {
         slot[e] = 0;
@@ -257,13 +335,20 @@ __device__ __forceinline__ void store8(float* dst, const float* acc) {
 // groups hold consecutive rows, so index loads of a wave share cache lines).
 // Per query window the index loads of all the group's rows are issued
 // together, then each row's gathers.
-template <int ELEM>
+//
+// Packed corpus (VARLEN): the rows are the T packed rows and a source's
+// document comes from the source itself (s / Lq = q*B + b).  Rows that no
+// document covers hold no meaningful row_ptr entry under a malformed
+// cu_seqlens; their ranges are clamped into col_idx so that no access leaves
+// the buffers.
+template <int ELEM, bool VARLEN>
 __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void dd_owner(BwdParams p, int rows_per_group) {
     const int l16 = threadIdx.x & 15;
     const int64_t ngroups = (int64_t)gridDim.x * kGatherGroups;
     const int64_t gid = (int64_t)blockIdx.x * kGatherGroups + (threadIdx.x >> 4);
-    const int64_t nrows = (int64_t)p.B * p.Ld;
+    const int64_t nrows = VARLEN ? p.T : (int64_t)p.B * p.Ld;
     const int BLq = p.B * p.Lq;
+    const int nsrc = p.Nq * BLq;  // col_idx capacity
     int cur[kRowsPerGroup], end[kRowsPerGroup], bdoc[kRowsPerGroup];
     float acc[kRowsPerGroup][8];
 #pragma unroll
@@ -272,7 +357,13 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
         const bool ok = k < rows_per_group && row < nrows;
         cur[k] = ok ? p.row_ptr[row] : 0;
         end[k] = ok ? p.row_ptr[row + 1] : 0;
-        bdoc[k] = ok ? (int)(row / p.Ld) : 0;
+        if constexpr (VARLEN) {
+            cur[k] = cur[k] < 0 ? 0 : (cur[k] > nsrc ? nsrc : cur[k]);
+            end[k] = end[k] < cur[k] ? cur[k] : (end[k] > nsrc ? nsrc : end[k]);
+            bdoc[k] = 0;
+        } else {
+            bdoc[k] = ok ? (int)(row / p.Ld) : 0;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
     }
@@ -295,11 +386,17 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
                 bool in = false;
                 if (src[k] >= 0) {
                     int q = (int)(((unsigned long long)(unsigned)src[k] * p.magic) >> (32 + p.shift));
-                    int i = src[k] - q * BLq - bdoc[k] * p.Lq;
+                    int b = bdoc[k];
+                    if constexpr (VARLEN) {
+                        const int qb = (int)(((unsigned long long)(unsigned)src[k] * p.magic_lq) >> (32 + p.shift_lq));
+                        b = qb - q * p.B;
+                        b = b < 0 ? 0 : (b >= p.B ? p.B - 1 : b);
+                    }
+                    int i = src[k] - q * BLq - b * p.Lq;
                     q = q < 0 ? 0 : (q >= p.Nq ? p.Nq - 1 : q);  // a consistent map never clamps
                     i = i < 0 ? 0 : (i >= p.Lq ? p.Lq - 1 : i);
                     in = q < qend;
-                    gv = p.g[(int64_t)q * p.B + bdoc[k]];
+                    gv = p.g[(int64_t)q * p.B + b];
                     qi = q * p.Lq + i;
                 }
                 // sources are in ascending q: the ones in this window are a prefix
@@ -333,8 +430,10 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
 }
 
 // Per step of kDocStep documents the gathers of all the group's rows are in
-// flight together.
-template <int ELEM>
+// flight together.  Packed corpus (VARLEN): lane j of a group holds document
+// b0 + j's first row and length; an empty document gives weight 0 and reads
+// a valid row.
+template <int ELEM, bool VARLEN>
 __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void dq_gather(BwdParams p, int rows_per_group) {
     const int l16 = threadIdx.x & 15;
     const int64_t ngroups = (int64_t)gridDim.x * kGatherGroups;
@@ -357,10 +456,14 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
     // Straight-line steps: every load is issued unconditionally from a valid
     // address (a missing row or document reads row 0 / the last document) and
     // its term gets weight 0, so no branch separates a load from the next.
-    for (int b0 = 0; b0 < p.B; b0 += kDocStep) {
+    const int nb_end = (VARLEN && p.T == 0) ? 0 : p.B;  // no rows at all: dQ = 0
+    for (int b0 = 0; b0 < nb_end; b0 += kDocStep) {
         const int nb = min(kDocStep, p.B - b0);
         const bool lane_doc = l16 < nb;
         const int bl = b0 + (lane_doc ? l16 : 0);
+        int64_t dstart = 0;
+        int dlen = p.Ld;
+        if constexpr (VARLEN) doc_rows(p, bl, dstart, dlen);
         int araw[kRowsPerGroup];
         float gv[kRowsPerGroup];
 #pragma unroll
@@ -371,8 +474,16 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
         int tok[kRowsPerGroup];
 #pragma unroll
         for (int k = 0; k < kRowsPerGroup; ++k) {
-            tok[k] = clamp_tok(araw[k], p.Ld);
-            gv[k] = (ok[k] && lane_doc) ? gv[k] : 0.f;
+            if constexpr (VARLEN) {
+                // packed row index (T < 2^31, checked by the host); an empty
+                // document, or one starting at T, reads row T-1 with weight 0
+                const int r = (int)dstart + clamp_tok(araw[k], dlen > 0 ? dlen : 1);
+                tok[k] = r < (int)p.T ? r : (int)p.T - 1;
+                gv[k] = (ok[k] && lane_doc && dlen > 0) ? gv[k] : 0.f;
+            } else {
+                tok[k] = clamp_tok(araw[k], p.Ld);
+                gv[k] = (ok[k] && lane_doc) ? gv[k] : 0.f;
+            }
         }
         u32x4 raw[kRowsPerGroup][kDocStep];
 #pragma unroll
@@ -380,9 +491,13 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int j = 0; j < kDocStep; ++j) {
                 const int tj = __shfl(tok[k], j, 16);
-                // document base is wave-uniform; the row offset fits 32 bits (Ld <= 4096)
-                const char* Db = p.D + (int64_t)min(b0 + j, p.B - 1) * p.Ld * 256;
-                raw[k][j] = *reinterpret_cast<const u32x4*>(Db + (unsigned)(tj * 256 + l16 * 16));
+                if constexpr (VARLEN) {
+                    raw[k][j] = *reinterpret_cast<const u32x4*>(p.D + (int64_t)tj * 256 + l16 * 16);
+                } else {
+                    // document base is wave-uniform; the row offset fits 32 bits (Ld <= 4096)
+                    const char* Db = p.D + (int64_t)min(b0 + j, p.B - 1) * p.Ld * 256;
+                    raw[k][j] = *reinterpret_cast<const u32x4*>(Db + (unsigned)(tj * 256 + l16 * 16));
+                }
             }
         }
 #pragma unroll
@@ -414,25 +529,42 @@ void gather_grid(int64_t nrows, unsigned* blocks, int* rows_per_group) {
     *rows_per_group = r;
 }
 
-template <int ELEM>
+template <int ELEM, bool VARLEN>
 hipError_t launch_bwd_elem(const BwdParams& p, hipStream_t stream) {
     const int nthr = 64 * p.G;
     const unsigned groups = (unsigned)((int64_t)p.B * p.NG);
+    hipError_t e;
+    if (VARLEN) {
+        hipLaunchKernelGGL(csr_docbase, dim3(1), dim3(1024), 0, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(csr_count, dim3(groups), dim3(nthr), p.Ld * sizeof(int), stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(csr_scan, dim3(p.B), dim3(1024), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(csr_fill, dim3(groups), dim3(nthr), (size_t)p.G * p.Ld * 12, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     unsigned blocks;
     int rpg;
-    gather_grid((int64_t)p.B * p.Ld, &blocks, &rpg);
-    hipLaunchKernelGGL((dd_owner<ELEM>), dim3(blocks), dim3(kGatherThreads), 0, stream, p, rpg);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t nrows = VARLEN ? p.T : (int64_t)p.B * p.Ld;
+    if (nrows > 0) {
+        gather_grid(nrows, &blocks, &rpg);
+        hipLaunchKernelGGL((dd_owner<ELEM, VARLEN>), dim3(blocks), dim3(kGatherThreads), 0, stream, p, rpg);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     gather_grid((int64_t)p.Nq * p.Lq, &blocks, &rpg);
-    hipLaunchKernelGGL((dq_gather<ELEM>), dim3(blocks), dim3(kGatherThreads), 0, stream, p, rpg);
+    hipLaunchKernelGGL((dq_gather<ELEM, VARLEN>), dim3(blocks), dim3(kGatherThreads), 0, stream, p, rpg);
     return hipGetLastError();
+}
+
+// ceil-rounded magic multiplier for floor(n / d), 0 <= n < 2^31:
+// shift = ceil(log2 d), magic = ceil(2^(32+shift) / d)
+void magic_div(unsigned long long d, unsigned long long* magic, int* shift) {
+    int s = 0;
+    while ((1ull << s) < d) ++s;
+    const unsigned __int128 num = (unsigned __int128)1 << (32 + s);
+    *magic = (unsigned long long)((num + d - 1) / d);
+    *shift = s;
 }
 
 }  // namespace
@@ -452,8 +584,14 @@ size_t bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld) {
     return (size_t)(B * NG * Ld * (int64_t)sizeof(int32_t));
 }
 
+size_t bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld) {
+    const size_t base = bwd_workspace_bytes(Nq, B, Lq, max_Ld);
+    if (base == 0) return 0;
+    return ((base + 255) & ~(size_t)255) + (size_t)(B + 1) * sizeof(int32_t);
+}
+
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
-    BwdParams p;
+    BwdParams p = {};
     p.Q = static_cast<const char*>(a.Q);
     p.D = static_cast<const char*>(a.D);
     p.A = a.argmax;
@@ -469,14 +607,17 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.row_ptr = a.row_ptr;
     p.col_idx = a.col_idx;
     p.ws = static_cast<int32_t*>(a.workspace);
-    // magic division by B*Lq: shift = ceil(log2 d), magic = ceil(2^(32+shift) / d)
-    const unsigned long long d = (unsigned long long)a.B * a.Lq;
-    int shift = 0;
-    while ((1ull << shift) < d) ++shift;
-    const unsigned __int128 num = (unsigned __int128)1 << (32 + shift);
-    p.magic = (unsigned long long)((num + d - 1) / d);
-    p.shift = shift;
-    return a.elem == kBF16 ? launch_bwd_elem<kBF16>(p, stream) : launch_bwd_elem<kF16>(p, stream);
+    magic_div((unsigned long long)a.B * a.Lq, &p.magic, &p.shift);
+    magic_div((unsigned long long)a.Lq, &p.magic_lq, &p.shift_lq);
+    if (a.cu_seqlens) {
+        // workspace: the [B][NG][Ld] counts, then docbase [B+1] at a 256-byte boundary
+        p.cu = a.cu_seqlens;
+        p.T = a.T;
+        const size_t off = (bwd_workspace_bytes(a.Nq, a.B, a.Lq, a.Ld) + 255) & ~(size_t)255;
+        p.docbase = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + off);
+        return a.elem == kBF16 ? launch_bwd_elem<kBF16, true>(p, stream) : launch_bwd_elem<kF16, true>(p, stream);
+    }
+    return a.elem == kBF16 ? launch_bwd_elem<kBF16, false>(p, stream) : launch_bwd_elem<kF16, false>(p, stream);
 }
 
 }  // namespace maxsim

@@ -155,6 +155,48 @@ int maxsim_bwd(const void* Q, const void* D, int32_t dtype, const int32_t* argma
     return hip_status(maxsim::launch_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t maxsim_bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld) {
+    if (Nq < 1 || B < 1 || Lq < 1 || max_Ld < 1) return 0;
+    return maxsim::bwd_varlen_workspace_bytes(Nq, B, Lq, max_Ld);
+}
+
+int maxsim_bwd_varlen(const void* Q, const void* D_packed, const int32_t* cu_seqlens, int32_t dtype,
+                      const int32_t* argmax, const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B,
+                      int64_t T, int32_t max_Ld, int32_t d, float* dQ, float* dD, int32_t* row_ptr,
+                      int32_t* col_idx, void* workspace, size_t workspace_bytes, void* stream) {
+    if (Nq < 1 || B < 1 || Lq < 1 || max_Ld < 1 || T < 0) return MAXSIM_ERR_SHAPE;
+    if ((int64_t)Nq * B * Lq >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
+    if (T >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
+    if (d != kDim || Lq > kMaxLq || max_Ld > maxsim::kMaxLdBwd) return MAXSIM_ERR_UNSUPPORTED;
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_UNSUPPORTED;
+    if (!Q || !cu_seqlens || !argmax || !grad_scores || !dQ || !row_ptr || !col_idx || !workspace ||
+        (T > 0 && (!D_packed || !dD)))
+        return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D_packed, 16) || !aligned(dQ, 16) || !aligned(dD, 16) ||
+        !aligned(cu_seqlens, 4) || !aligned(argmax, 4) || !aligned(grad_scores, 4) ||
+        !aligned(row_ptr, 4) || !aligned(col_idx, 4) || !aligned(workspace, 256))
+        return MAXSIM_ERR_ALIGN;
+    if (workspace_bytes < maxsim::bwd_varlen_workspace_bytes(Nq, B, Lq, max_Ld)) return MAXSIM_ERR_WORKSPACE;
+    maxsim::BwdArgs a{};
+    a.Q = Q;
+    a.D = D_packed;
+    a.argmax = argmax;
+    a.g = grad_scores;
+    a.Nq = Nq;
+    a.Lq = Lq;
+    a.B = B;
+    a.Ld = max_Ld;
+    a.elem = dtype == MAXSIM_BF16 ? maxsim::kBF16 : maxsim::kF16;
+    a.dQ = dQ;
+    a.dD = dD;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.workspace = workspace;
+    a.cu_seqlens = cu_seqlens;
+    a.T = T;
+    return hip_status(maxsim::launch_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 int maxsim_fwd_pairs(const void* Q, const void* D_packed, const int32_t* cu_seqlens, int32_t dtype,
                      const int32_t* pair_q, const int32_t* pair_b, int32_t P, int32_t Nq, int32_t Lq,
                      int32_t B, int64_t T, int32_t d, float* scores, int32_t* argmax, void* stream) {

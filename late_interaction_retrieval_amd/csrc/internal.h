@@ -51,11 +51,16 @@ struct BwdArgs {
     int32_t* row_ptr;         // [B*Ld + 1]
     int32_t* col_idx;         // [Nq*B*Lq]
     void* workspace;
+    // packed corpus (nullptr: padded): D is [T, 128], dD is [T, 128], row_ptr
+    // is [T + 1] and Ld is the longest document
+    const int32_t* cu_seqlens = nullptr;  // [B + 1]
+    int64_t T = 0;
 };
 
 // Queries per CSR group (one wave each) for a document length; 0 if unsupported.
 int bwd_group(int32_t Ld);
 size_t bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld);
+size_t bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace maxsim

@@ -45,7 +45,8 @@ def test_every_declared_symbol_is_exported_with_binding_arity():
     decl = declared_functions()
     assert set(decl) == {"maxsim_fwd", "maxsim_fwd_varlen", "maxsim_fwd_i8", "maxsim_bwd_workspace_bytes",
                          "maxsim_bwd", "maxsim_status_string", "maxsim_fwd_pairs", "maxsim_topk",
-                         "maxsim_two_stage_workspace_bytes", "maxsim_two_stage_topk"}
+                         "maxsim_two_stage_workspace_bytes", "maxsim_two_stage_topk",
+                         "maxsim_bwd_varlen_workspace_bytes", "maxsim_bwd_varlen"}
     raw = ctypes.CDLL(LIB)
     for name, nargs in decl.items():
         assert hasattr(raw, name), name
@@ -212,3 +213,38 @@ def test_pairs_topk_two_stage_validation():
     assert args(4, 2, A, need - 1) == WS
     assert args(4, 2, ctypes.c_void_p(0x10010), need) == ALIGN
     assert args(4, 2, None, need) == NULL
+
+
+def bwd_varlen(**kw):
+    a = dict(Q=A, D=A, cu=A, dt=1, A=A, g=A, Nq=4, Lq=32, B=5, T=300, maxld=64, d=128, dQ=A, dD=A, rp=A, ci=A,
+             ws=A, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.maxsim_bwd_varlen(a["Q"], a["D"], a["cu"], a["dt"], a["A"], a["g"], a["Nq"], a["Lq"], a["B"],
+                               a["T"], a["maxld"], a["d"], a["dQ"], a["dD"], a["rp"], a["ci"], a["ws"], a["wsb"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), bd.MAXSIM_ERR_NULL), (dict(cu=None), bd.MAXSIM_ERR_NULL), (dict(A=None), bd.MAXSIM_ERR_NULL),
+    (dict(D=None), bd.MAXSIM_ERR_NULL), (dict(dD=None), bd.MAXSIM_ERR_NULL), (dict(ws=None), bd.MAXSIM_ERR_NULL),
+    (dict(Nq=0), bd.MAXSIM_ERR_SHAPE), (dict(B=0), bd.MAXSIM_ERR_SHAPE), (dict(T=-1), bd.MAXSIM_ERR_SHAPE),
+    (dict(maxld=0), bd.MAXSIM_ERR_SHAPE), (dict(T=1 << 31), bd.MAXSIM_ERR_SHAPE),
+    (dict(Nq=1 << 16, B=1 << 10, Lq=32), bd.MAXSIM_ERR_SHAPE),
+    (dict(maxld=4097), bd.MAXSIM_ERR_UNSUPPORTED), (dict(d=64), bd.MAXSIM_ERR_UNSUPPORTED),
+    (dict(Lq=1025), bd.MAXSIM_ERR_UNSUPPORTED), (dict(dt=2), bd.MAXSIM_ERR_UNSUPPORTED),
+    (dict(Q=M), bd.MAXSIM_ERR_ALIGN), (dict(dD=M), bd.MAXSIM_ERR_ALIGN),
+    (dict(ws=ctypes.c_void_p(0x10010)), bd.MAXSIM_ERR_ALIGN),
+    (dict(wsb=0), bd.MAXSIM_ERR_WORKSPACE),
+])
+def test_bwd_varlen_validation(kw, code):
+    assert bwd_varlen(**kw) == code
+
+
+def test_bwd_varlen_workspace_bytes():
+    # the padded counts for max_Ld, then the per-document first slots at a 256-byte boundary
+    base = L.maxsim_bwd_workspace_bytes(10, 7, 32, 100)
+    n = L.maxsim_bwd_varlen_workspace_bytes(10, 7, 32, 100)
+    assert n == ((base + 255) // 256) * 256 + 8 * 4
+    assert L.maxsim_bwd_varlen_workspace_bytes(0, 7, 32, 100) == 0
+    assert L.maxsim_bwd_varlen_workspace_bytes(1, 1, 1, 5000) == 0
+    assert bwd_varlen(wsb=n - 1, Nq=10, B=7, Lq=32, maxld=100) == bd.MAXSIM_ERR_WORKSPACE
