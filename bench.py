@@ -59,6 +59,9 @@ def parse():
                     help="only measure the sustained MFMA rate for f16, bf16 and int8 and exit")
     ap.add_argument("--no-graph", action="store_true",
                     help="tiny workload: time eager launches instead of HIP-graph replays")
+    ap.add_argument("--bwd-dispatch-sweep", action="store_true",
+                    help="instead of the workload, time the CSR and the atomic-scatter backward over a grid "
+                         "of contention levels (sources per dD row) and print one JSON line per shape")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the workload, run 5 device-to-device copies of MIB MiB: the counter "
@@ -177,6 +180,9 @@ def main():
 
     import torch
 
+    if args.bwd_dispatch_sweep:
+        bwd_dispatch_sweep()
+        return
     if args.workload == "two_stage_topk":
         bench_two_stage(args)
         return
@@ -429,6 +435,56 @@ def main():
     if extra:
         out["extra"] = extra
     print(json.dumps(out), flush=True)
+
+
+def bwd_dispatch_sweep(reps=20):
+    """CSR backward (maxsim_bwd) against the atomic-scatter backward
+    (maxsim_bwd_scatter) on padded fp16 documents, seeded uniform argmax and
+    upstream gradient, over shapes whose mean number of sources per dD row
+    (Nq*Lq/Ld) spans 0.03 .. 64.  Each time is the mean of `reps` launches
+    between HIP events on the launch stream, after one warm-up call."""
+    import torch
+    from late_interaction_retrieval_amd import binding as bd
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    shapes = [(nq, 32, 1000, 180) for nq in (1, 2, 4, 8, 16, 32, 64)]
+    shapes += [(nq, 32, 64, 1024) for nq in (1, 8, 32)]
+    shapes += [(nq, 1024, 64, 1024) for nq in (1, 4, 16, 64)]
+    for Nq, Lq, B, Ld in shapes:
+        Q = torch.randn((Nq, Lq, 128), device=dev, generator=gen).to(torch.float16)
+        D = torch.randn((B, Ld, 128), device=dev, generator=gen).to(torch.float16)
+        A = torch.randint(0, Ld, (Nq, B, Lq), device=dev, generator=gen, dtype=torch.int32)
+        g = torch.randn((Nq, B), device=dev, generator=gen)
+        dQ = torch.empty((Nq, Lq, 128), device=dev)
+        dD = torch.empty((B, Ld, 128), device=dev)
+        rp = torch.empty(B * Ld + 1, dtype=torch.int32, device=dev)
+        ci = torch.empty(Nq * B * Lq, dtype=torch.int32, device=dev)
+        ws = torch.empty(max(16, bd.maxsim_bwd_workspace_bytes(Nq, B, Lq, Ld)), dtype=torch.uint8, device=dev)
+        runs = {"csr": lambda: bd.maxsim_bwd(Q, D, A, g, dQ=dQ, dD=dD, row_ptr=rp, col_idx=ci, workspace=ws),
+                "scatter": lambda: bd.maxsim_bwd_scatter(Q, D, A, g, dQ=dQ, dD=dD)}
+        ms = {}
+        for k, fn in runs.items():
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms[k] = e0.elapsed_time(e1) / reps
+        per_row = Nq * Lq / Ld
+        print(json.dumps({"Nq": Nq, "Lq": Lq, "B": B, "Ld": Ld, "sources_per_row": round(per_row, 4),
+                          "csr_ms": round(ms["csr"], 4), "scatter_ms": round(ms["scatter"], 4),
+                          "faster": min(ms, key=ms.get),
+                          "rule_picks": "scatter" if bd.maxsim_bwd_prefer_scatter(Nq, Lq, B, B * Ld) else "csr"}),
+              flush=True)
+        del Q, D, A, g, dQ, dD, rp, ci, ws
 
 
 def bench_two_stage(args, B=30000, K1=100, K2=10):

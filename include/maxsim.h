@@ -126,6 +126,8 @@ size_t maxsim_bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld)
  *     Each row is written once by its owner, no atomics.
  * Step 3, gathered dQ (Eq. (dq)):
  *     dQ [Nq, Lq, d] fp32 out, dQ[q,i] = sum_b grad_scores[q,b] * D[b, argmax[q,b,i]].
+ *     With few query rows the documents are split into chunks whose partial
+ *     sums are added in ascending chunk order (still bit-reproducible).
  * workspace: device scratch of at least maxsim_bwd_workspace_bytes() bytes,
  * 16-byte aligned; its contents on entry do not matter.
  * Requires Nq, B >= 1, 1 <= Lq <= 1024, 1 <= Ld <= 4096, Nq*B*Lq < 2^31,
@@ -167,6 +169,40 @@ int maxsim_bwd_varlen(const void* Q, const void* D_packed, const int32_t* cu_seq
                       const int32_t* argmax, const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B,
                       int64_t T, int32_t max_Ld, int32_t d, float* dQ, float* dD, int32_t* row_ptr,
                       int32_t* col_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace maxsim_bwd_scatter needs (0 on bad sizes). */
+size_t maxsim_bwd_scatter_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq);
+
+/*
+ * Backward with dD by atomic scatter: the low-contention alternative the
+ * pages pair with the destination-owned reduction (Section 4.2,
+ * "Destination-Owned Reduction", the dispatch remark at its end).  dD is
+ * cleared and every source adds grad_scores[q,b] * Q[q,i] into its row with
+ * fp32 atomic adds; dQ is gathered exactly as in maxsim_bwd.  No CSR map is
+ * built and no workspace is needed.  The order of the adds into one row is
+ * not fixed, so dD may differ between runs in the last bits (maxsim_bwd is
+ * bit-reproducible); rows no source selects are exactly 0.
+ *   cu_seqlens NULL: padded, D and dD are [B, Ld, d] and T is ignored;
+ *   otherwise packed as for maxsim_bwd_varlen, D_packed and dD are [T, d]
+ *   and Ld is the longest document.
+ * workspace: device scratch of maxsim_bwd_scatter_workspace_bytes() bytes,
+ * 256-byte aligned (partial dQ sums when the documents are split in chunks).
+ * Other arguments and requirements as maxsim_bwd / maxsim_bwd_varlen.
+ */
+int maxsim_bwd_scatter(const void* Q, const void* D, const int32_t* cu_seqlens, int32_t dtype,
+                       const int32_t* argmax, const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B,
+                       int32_t Ld, int64_t T, int32_t d, float* dQ, float* dD, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * The dispatch rule between the two dD reductions: 1 when the atomic scatter
+ * (maxsim_bwd_scatter) is expected to be faster than the CSR path for Nq
+ * queries of Lq tokens against B documents of `rows` rows in total (B*Ld
+ * padded, T packed), else 0.  The rule compares the mean number of sources
+ * per destination row, Nq*Lq*B / rows, with a threshold measured on MI355X.
+ * Returns 0 for non-positive sizes.  Host-only; launches nothing.
+ */
+int maxsim_bwd_prefer_scatter(int32_t Nq, int32_t Lq, int32_t B, int64_t rows);
 
 /*
  * Scores of an explicit list of (query, document) pairs over a packed corpus

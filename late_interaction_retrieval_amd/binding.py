@@ -39,6 +39,10 @@ SIGNATURES = {
     "maxsim_bwd_varlen_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "maxsim_bwd_varlen": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _P, _P,
                                          _P, _P, _P, ctypes.c_size_t, _P]),
+    "maxsim_bwd_scatter_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "maxsim_bwd_scatter": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32, _P, _P,
+                                          _P, ctypes.c_size_t, _P]),
+    "maxsim_bwd_prefer_scatter": (ctypes.c_int, [_I32, _I32, _I32, _I64]),
     "maxsim_fwd_pairs": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32, _P, _P, _P]),
     "maxsim_topk": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, _P]),
     "maxsim_two_stage_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
@@ -261,26 +265,90 @@ def maxsim_bwd_varlen(Q, D_packed, cu_seqlens, max_Ld, argmax, grad_scores, dQ=N
     return dQ, dD, row_ptr, col_idx
 
 
+def maxsim_bwd_prefer_scatter(Nq, Lq, B, rows):
+    return bool(lib().maxsim_bwd_prefer_scatter(Nq, Lq, B, rows))
+
+
+def maxsim_bwd_scatter_workspace_bytes(Nq, B, Lq):
+    return int(lib().maxsim_bwd_scatter_workspace_bytes(Nq, B, Lq))
+
+
+def maxsim_bwd_scatter(Q, D, argmax, grad_scores, cu_seqlens=None, max_Ld=None, dQ=None, dD=None, workspace=None,
+                       stream=None):
+    """Backward with dD by atomic scatter (no CSR).  D is [B, Ld, d] (padded) or, with cu_seqlens,
+    D_packed [T, d] with max_Ld the longest document.  Returns (dQ, dD)."""
+    Nq, Lq, d = Q.shape
+    dev = Q.device
+    _need(Q, "Q")
+    _need(D, "D", device=dev)
+    _need(argmax, "argmax", torch.int32, dev)
+    _need(grad_scores, "grad_scores", torch.float32, dev)
+    if D.dtype != Q.dtype or D.shape[-1] != d:
+        raise ValueError("Q and D must share dtype and width")
+    if cu_seqlens is None:
+        B, Ld, _ = D.shape
+        T = 0
+    else:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        B = cu_seqlens.shape[0] - 1
+        T = D.shape[0]
+        Ld = int(max_Ld)
+    if dQ is None:
+        dQ = torch.empty((Nq, Lq, d), dtype=torch.float32, device=dev)
+    if dD is None:
+        dD = torch.empty(D.shape, dtype=torch.float32, device=dev)
+    _need(dQ, "dQ", torch.float32, dev)
+    _need(dD, "dD", torch.float32, dev)
+    if workspace is None:
+        workspace = torch.empty(max(256, maxsim_bwd_scatter_workspace_bytes(Nq, B, Lq)), dtype=torch.uint8,
+                                device=dev)
+    _need(workspace, "workspace", device=dev)
+    st = lib().maxsim_bwd_scatter(_ptr(Q), _ptr(D), _ptr(cu_seqlens), _dtype_code(Q), _ptr(argmax),
+                                  _ptr(grad_scores), Nq, Lq, B, Ld, T, d, _ptr(dQ), _ptr(dD), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(Q, stream))
+    _check(st, "maxsim_bwd_scatter")
+    return dQ, dD
+
+
 class MaxSimFunction(torch.autograd.Function):
     """score = MaxSim(Q, D) as an autograd op: the forward saves the argmax and the
-    backward builds the inverse-grid CSR and the gradients (paper Section 4.2)."""
+    backward builds the inverse-grid CSR and the gradients (paper Section 4.2).
+    With deterministic=False the backward may take the atomic-scatter dD instead,
+    where the dispatch rule (maxsim_bwd_prefer_scatter) expects it to be faster."""
 
     @staticmethod
-    def forward(ctx, Q, D):
-        scores, argmax = maxsim_fwd(Q, D)
-        ctx.save_for_backward(Q, D, argmax)
+    def forward(ctx, Q, D, cu_seqlens, max_Ld, deterministic):
+        if cu_seqlens is None:
+            scores, argmax = maxsim_fwd(Q, D)
+        else:
+            scores, argmax = maxsim_fwd_varlen(Q, D, cu_seqlens, max_Ld)
+        ctx.save_for_backward(Q, D, argmax, cu_seqlens)
+        ctx.max_Ld = max_Ld
+        ctx.deterministic = deterministic
         return scores
 
     @staticmethod
     def backward(ctx, grad_scores):
-        Q, D, argmax = ctx.saved_tensors
-        dQ, dD, _, _ = maxsim_bwd(Q, D, argmax, grad_scores.float().contiguous())
-        return dQ.to(Q.dtype), dD.to(D.dtype)
+        Q, D, argmax, cu = ctx.saved_tensors
+        g = grad_scores.float().contiguous()
+        Nq, Lq, _ = Q.shape
+        B = argmax.shape[1]
+        rows = D.shape[0] * D.shape[1] if cu is None else D.shape[0]
+        if not ctx.deterministic and maxsim_bwd_prefer_scatter(Nq, Lq, B, rows):
+            dQ, dD = maxsim_bwd_scatter(Q, D, argmax, g, cu_seqlens=cu, max_Ld=ctx.max_Ld)
+        elif cu is None:
+            dQ, dD, _, _ = maxsim_bwd(Q, D, argmax, g)
+        else:
+            dQ, dD, _, _ = maxsim_bwd_varlen(Q, D, cu, ctx.max_Ld, argmax, g)
+        return dQ.to(Q.dtype), dD.to(D.dtype), None, None, None
 
 
-def maxsim(Q, D):
-    """All-pairs MaxSim scores [Nq, B] with autograd support."""
-    return MaxSimFunction.apply(Q, D)
+def maxsim(Q, D, cu_seqlens=None, max_Ld=None, deterministic=True):
+    """MaxSim scores [Nq, B] of every query against every document, with autograd
+    support.  D is [B, Ld, d], or packed [T, d] with cu_seqlens [B+1] and max_Ld."""
+    if cu_seqlens is not None and max_Ld is None:
+        raise ValueError("max_Ld is required with cu_seqlens")
+    return MaxSimFunction.apply(Q, D, cu_seqlens, max_Ld, deterministic)
 
 
 def maxsim_fwd_pairs(Q, D_packed, cu_seqlens, pair_q, pair_b, scores=None, argmax=None, with_argmax=False,

@@ -27,6 +27,8 @@
 // clamped into range so that no access leaves the buffers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace maxsim {
@@ -58,6 +60,11 @@ struct BwdParams {
     const int32_t* cu;
     int64_t T;
     int32_t* docbase;
+    // dQ over document chunks: with dq_split > 1 chunk c (blockIdx.y) sums
+    // documents [c*dq_docs, (c+1)*dq_docs) into dq_part[c] ([Nq*Lq, 128]),
+    // and dq_reduce adds the chunks in ascending order
+    int dq_split, dq_docs;
+    float* dq_part;
 };
 
 __device__ __forceinline__ int clamp_tok(int t, int Ld) { return t < 0 ? 0 : (t >= Ld ? Ld - 1 : t); }
@@ -316,7 +323,6 @@ constexpr int kGatherThreads = 512;
 constexpr int kGatherGroups = kGatherThreads / 16;  // 16-lane groups per workgroup
 constexpr int kGatherBlocks = 512;                  // 2 per CU on 256 CUs
 constexpr int kRowsPerGroup = 4;
-constexpr int kDocStep = 2;       // documents per dQ step
 constexpr int kQueryWindow = 16;  // queries per dD step
 constexpr int kDdBatch = 12;      // dD sources gathered per round (loads in flight)
 
@@ -429,21 +435,22 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-// Per step of kDocStep documents the gathers of all the group's rows are in
-// flight together.  Packed corpus (VARLEN): lane j of a group holds document
-// b0 + j's first row and length; an empty document gives weight 0 and reads
-// a valid row.
-template <int ELEM, bool VARLEN>
+// Per step of DSTEP documents the gathers of all the group's RPG rows are in
+// flight together (RPG * DSTEP = 8 loads: 4 rows x 2 documents, or 1 row x 8
+// documents when there are few rows).  Packed corpus (VARLEN): lane j of a
+// group holds document b0 + j's first row and length; an empty document gives
+// weight 0 and reads a valid row.  Each row sums its terms in ascending b.
+template <int ELEM, bool VARLEN, int RPG, int DSTEP>
 __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void dq_gather(BwdParams p, int rows_per_group) {
     const int l16 = threadIdx.x & 15;
     const int64_t ngroups = (int64_t)gridDim.x * kGatherGroups;
     const int64_t gid = (int64_t)blockIdx.x * kGatherGroups + (threadIdx.x >> 4);
     const int64_t nrows = (int64_t)p.Nq * p.Lq;
-    int aoff[kRowsPerGroup], goff[kRowsPerGroup];  // Nq*B*Lq < 2^31 (checked by the host)
-    bool ok[kRowsPerGroup];
-    float acc[kRowsPerGroup][8];
+    int aoff[RPG], goff[RPG];  // Nq*B*Lq < 2^31 (checked by the host)
+    bool ok[RPG];
+    float acc[RPG][8];
 #pragma unroll
-    for (int k = 0; k < kRowsPerGroup; ++k) {
+    for (int k = 0; k < RPG; ++k) {
         const int64_t row = gid + k * ngroups;  // q*Lq + i
         ok[k] = k < rows_per_group && row < nrows;
         const int q = ok[k] ? (int)(row / p.Lq) : 0;
@@ -456,24 +463,25 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
     // Straight-line steps: every load is issued unconditionally from a valid
     // address (a missing row or document reads row 0 / the last document) and
     // its term gets weight 0, so no branch separates a load from the next.
-    const int nb_end = (VARLEN && p.T == 0) ? 0 : p.B;  // no rows at all: dQ = 0
-    for (int b0 = 0; b0 < nb_end; b0 += kDocStep) {
-        const int nb = min(kDocStep, p.B - b0);
+    const int b_lo = blockIdx.y * p.dq_docs;
+    const int b_hi = (VARLEN && p.T == 0) ? 0 : min(p.B, b_lo + p.dq_docs);  // no rows at all: dQ = 0
+    for (int b0 = b_lo; b0 < b_hi; b0 += DSTEP) {
+        const int nb = min(DSTEP, b_hi - b0);
         const bool lane_doc = l16 < nb;
         const int bl = b0 + (lane_doc ? l16 : 0);
         int64_t dstart = 0;
         int dlen = p.Ld;
         if constexpr (VARLEN) doc_rows(p, bl, dstart, dlen);
-        int araw[kRowsPerGroup];
-        float gv[kRowsPerGroup];
+        int araw[RPG];
+        float gv[RPG];
 #pragma unroll
-        for (int k = 0; k < kRowsPerGroup; ++k) {
+        for (int k = 0; k < RPG; ++k) {
             araw[k] = p.A[aoff[k] + (int64_t)bl * p.Lq];
             gv[k] = p.g[goff[k] + bl];
         }
-        int tok[kRowsPerGroup];
+        int tok[RPG];
 #pragma unroll
-        for (int k = 0; k < kRowsPerGroup; ++k) {
+        for (int k = 0; k < RPG; ++k) {
             if constexpr (VARLEN) {
                 // packed row index (T < 2^31, checked by the host); an empty
                 // document, or one starting at T, reads row T-1 with weight 0
@@ -485,11 +493,11 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
                 gv[k] = (ok[k] && lane_doc) ? gv[k] : 0.f;
             }
         }
-        u32x4 raw[kRowsPerGroup][kDocStep];
+        u32x4 raw[RPG][DSTEP];
 #pragma unroll
-        for (int k = 0; k < kRowsPerGroup; ++k) {
+        for (int k = 0; k < RPG; ++k) {
 #pragma unroll
-            for (int j = 0; j < kDocStep; ++j) {
+            for (int j = 0; j < DSTEP; ++j) {
                 const int tj = __shfl(tok[k], j, 16);
                 if constexpr (VARLEN) {
                     raw[k][j] = *reinterpret_cast<const u32x4*>(p.D + (int64_t)tj * 256 + l16 * 16);
@@ -501,9 +509,9 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
             }
         }
 #pragma unroll
-        for (int k = 0; k < kRowsPerGroup; ++k) {
+        for (int k = 0; k < RPG; ++k) {
 #pragma unroll
-            for (int j = 0; j < kDocStep; ++j) {
+            for (int j = 0; j < DSTEP; ++j) {
                 const float gj = __shfl(gv[k], j, 16);
                 float v[8];
                 cvt8<ELEM>(raw[k][j], v);
@@ -511,10 +519,93 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
             }
         }
     }
+    float* out = p.dq_split > 1 ? p.dq_part + (int64_t)blockIdx.y * nrows * 128 : p.dQ;
 #pragma unroll
-    for (int k = 0; k < kRowsPerGroup; ++k) {
+    for (int k = 0; k < RPG; ++k) {
         const int64_t row = gid + k * ngroups;
-        if (ok[k]) store8(p.dQ + row * 128 + l16 * 8, acc[k]);
+        if (ok[k]) store8(out + row * 128 + l16 * 8, acc[k]);
+    }
+}
+
+// dQ = sum of the chunks' partial sums in a fixed order: 16 slices of
+// consecutive chunks are summed in ascending order by 16 threads each (one
+// per float4 of 16 consecutive ones), then the slices in ascending order.
+__global__ __launch_bounds__(256) void dq_reduce(BwdParams p) {
+    __shared__ f32x4 slice_sum[16][16];  // [slice][element]
+    const int64_t n4 = (int64_t)p.Nq * p.Lq * 32;
+    const int el = threadIdx.x & 15, sl = threadIdx.x >> 4;
+    const int64_t k = (int64_t)blockIdx.x * 16 + el;
+    const int per = (p.dq_split + 15) / 16;
+    const int c0 = sl * per, c1 = min(p.dq_split, c0 + per);
+    const f32x4* part = reinterpret_cast<const f32x4*>(p.dq_part);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (k < n4) {
+#pragma unroll 8
+        for (int c = c0; c < c1; ++c) {
+            const f32x4 v = part[(int64_t)c * n4 + k];
+            acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
+        }
+    }
+    slice_sum[sl][el] = acc;
+    __syncthreads();
+    if (sl == 0 && k < n4) {
+        f32x4 t = slice_sum[0][el];
+        for (int j = 1; j < 16; ++j) {
+            const f32x4 v = slice_sum[j][el];
+            t = f32x4{t[0] + v[0], t[1] + v[1], t[2] + v[2], t[3] + v[3]};
+        }
+        reinterpret_cast<f32x4*>(p.dQ)[k] = t;
+    }
+}
+
+// Atomic-scatter dD, the low-contention alternative to the CSR path: dD is
+// cleared, then every source adds g[q,b] * Q[q,i] into its destination row
+// with fp32 atomic adds at the device's L2.  A 16-lane group takes one source
+// at a time; lane l owns columns e*16 + l (e < 8), so each atomic instruction
+// of the group covers 64 contiguous bytes of the row.  The order of the adds
+// into one row is not fixed, so results may differ between runs in the last
+// bits; rows no source selects are exactly 0.
+__global__ __launch_bounds__(256) void zero_rows(float* dst, int64_t n4) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n4; k += stride)
+        reinterpret_cast<f32x4*>(dst)[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int ELEM, bool VARLEN>
+__global__ __launch_bounds__(256) void dd_scatter(BwdParams p) {
+    const int l16 = threadIdx.x & 15;
+    const int ngroups = gridDim.x * 16;
+    const int nsrc = p.Nq * p.B * p.Lq;  // < 2^31 (checked by the host)
+    for (int s = blockIdx.x * 16 + (threadIdx.x >> 4); s < nsrc; s += ngroups) {
+        const int qb = s / p.Lq;  // q*B + b
+        const int i = s - qb * p.Lq;
+        const int q = qb / p.B;
+        const int b = qb - q * p.B;
+        int64_t start;
+        int len;
+        if constexpr (VARLEN) {
+            doc_rows(p, b, start, len);
+            if (len == 0) continue;  // uniform per group: an empty document takes no gradient
+        } else {
+            start = (int64_t)b * p.Ld;
+            len = p.Ld;
+        }
+        const int64_t row = start + clamp_tok(p.A[s], len);
+        const float gv = p.g[qb];
+        const unsigned short* qrow = reinterpret_cast<const unsigned short*>(p.Q) + ((int64_t)q * p.Lq + i) * 128;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const unsigned short h = qrow[e * 16 + l16];
+            if constexpr (ELEM == kBF16)
+                v[e] = __uint_as_float((unsigned)h << 16);
+            else
+                v[e] = (float)__builtin_bit_cast(_Float16, h);
+        }
+        float* drow = p.dD + row * 128;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            __hip_atomic_fetch_add(drow + e * 16 + l16, gv * v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -527,6 +618,47 @@ void gather_grid(int64_t nrows, unsigned* blocks, int* rows_per_group) {
     const int64_t groups = (nrows + r - 1) / r;
     *blocks = (unsigned)((groups + kGatherGroups - 1) / kGatherGroups);
     *rows_per_group = r;
+}
+
+// Documents per dQ chunk: enough chunks that the gather fills the chip
+// (kGatherBlocks workgroups) when there are few dQ rows, at least one step of
+// documents each (8 with one row per group, else 2).
+int dq_split_of(int64_t nrows, int B) {
+    unsigned blocks;
+    int rpg;
+    gather_grid(nrows, &blocks, &rpg);
+    int64_t s = ((int64_t)kGatherBlocks + blocks - 1) / blocks;
+    const int64_t smax = B / (rpg == 1 ? 8 : 2);
+    if (s > smax) s = smax;
+    return s < 1 ? 1 : (int)s;
+}
+
+size_t dq_part_bytes(int32_t Nq, int32_t Lq, int32_t B) {
+    const int64_t nrows = (int64_t)Nq * Lq;
+    const int S = dq_split_of(nrows, B);
+    return S > 1 ? (size_t)S * nrows * 128 * sizeof(float) : 0;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+template <int ELEM, bool VARLEN>
+hipError_t launch_dq(BwdParams p, hipStream_t stream) {
+    const int64_t nrows = (int64_t)p.Nq * p.Lq;
+    unsigned blocks;
+    int rpg;
+    gather_grid(nrows, &blocks, &rpg);
+    p.dq_split = dq_split_of(nrows, p.B);
+    p.dq_docs = (p.B + p.dq_split - 1) / p.dq_split;
+    if (rpg == 1)
+        hipLaunchKernelGGL((dq_gather<ELEM, VARLEN, 1, 8>), dim3(blocks, p.dq_split), dim3(kGatherThreads), 0, stream,
+                           p, rpg);
+    else
+        hipLaunchKernelGGL((dq_gather<ELEM, VARLEN, kRowsPerGroup, 2>), dim3(blocks, p.dq_split), dim3(kGatherThreads),
+                           0, stream, p, rpg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.dq_split == 1) return e;
+    hipLaunchKernelGGL(dq_reduce, dim3((unsigned)((nrows * 32 + 15) / 16)), dim3(256), 0, stream, p);
+    return hipGetLastError();
 }
 
 template <int ELEM, bool VARLEN>
@@ -552,9 +684,26 @@ hipError_t launch_bwd_elem(const BwdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL((dd_owner<ELEM, VARLEN>), dim3(blocks), dim3(kGatherThreads), 0, stream, p, rpg);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    gather_grid((int64_t)p.Nq * p.Lq, &blocks, &rpg);
-    hipLaunchKernelGGL((dq_gather<ELEM, VARLEN>), dim3(blocks), dim3(kGatherThreads), 0, stream, p, rpg);
-    return hipGetLastError();
+    return launch_dq<ELEM, VARLEN>(p, stream);
+}
+
+template <int ELEM, bool VARLEN>
+hipError_t launch_scatter_elem(const BwdParams& p, hipStream_t stream) {
+    hipError_t e;
+    const int64_t nrows = VARLEN ? p.T : (int64_t)p.B * p.Ld;
+    if (nrows > 0) {
+        const int64_t n4 = nrows * 32;
+        const unsigned zb = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
+        hipLaunchKernelGGL(zero_rows, dim3(zb), dim3(256), 0, stream, p.dD, n4);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int64_t nsrc = (int64_t)p.Nq * p.B * p.Lq;
+        const unsigned sb = (unsigned)std::min<int64_t>((nsrc + 15) / 16, 8192);
+        hipLaunchKernelGGL((dd_scatter<ELEM, VARLEN>), dim3(sb), dim3(256), 0, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    unsigned blocks;
+    int rpg;
+    return launch_dq<ELEM, VARLEN>(p, stream);
 }
 
 // ceil-rounded magic multiplier for floor(n / d), 0 <= n < 2^31:
@@ -576,18 +725,53 @@ int bwd_group(int32_t Ld) {
     return G;
 }
 
-size_t bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld) {
-    (void)Lq;
+// Workspace layout (each part at a 256-byte boundary): the CSR counts
+// [B][NG][Ld] int32, the packed corpus' document bases [B+1] int32, then the
+// dQ chunk partial sums [S][Nq*Lq][128] fp32 when dQ is split (S > 1).
+namespace {
+size_t counts_bytes(int32_t Nq, int32_t B, int32_t Ld) {
     const int G = bwd_group(Ld);
     if (G == 0 || Nq < 1 || B < 1) return 0;
     const int64_t NG = (Nq + G - 1) / G;
     return (size_t)(B * NG * Ld * (int64_t)sizeof(int32_t));
 }
+}  // namespace
+
+size_t bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld) {
+    const size_t c = counts_bytes(Nq, B, Ld);
+    if (c == 0 || Lq < 1) return 0;
+    return align256(c) + dq_part_bytes(Nq, Lq, B);
+}
 
 size_t bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld) {
-    const size_t base = bwd_workspace_bytes(Nq, B, Lq, max_Ld);
-    if (base == 0) return 0;
-    return ((base + 255) & ~(size_t)255) + (size_t)(B + 1) * sizeof(int32_t);
+    const size_t c = counts_bytes(Nq, B, max_Ld);
+    if (c == 0 || Lq < 1) return 0;
+    return align256(c) + align256((size_t)(B + 1) * sizeof(int32_t)) + dq_part_bytes(Nq, Lq, B);
+}
+
+size_t bwd_scatter_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq) {
+    if (Nq < 1 || B < 1 || Lq < 1) return 0;
+    return std::max<size_t>(256, dq_part_bytes(Nq, Lq, B));
+}
+
+hipError_t launch_bwd_scatter(const BwdArgs& a, hipStream_t stream) {
+    BwdParams p = {};
+    p.Q = static_cast<const char*>(a.Q);
+    p.D = static_cast<const char*>(a.D);
+    p.A = a.argmax;
+    p.g = a.g;
+    p.Nq = a.Nq;
+    p.Lq = a.Lq;
+    p.B = a.B;
+    p.Ld = a.Ld;
+    p.dQ = a.dQ;
+    p.dD = a.dD;
+    p.cu = a.cu_seqlens;
+    p.T = a.T;
+    p.dq_part = static_cast<float*>(a.workspace);
+    if (a.cu_seqlens)
+        return a.elem == kBF16 ? launch_scatter_elem<kBF16, true>(p, stream) : launch_scatter_elem<kF16, true>(p, stream);
+    return a.elem == kBF16 ? launch_scatter_elem<kBF16, false>(p, stream) : launch_scatter_elem<kF16, false>(p, stream);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
@@ -606,17 +790,20 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.dD = a.dD;
     p.row_ptr = a.row_ptr;
     p.col_idx = a.col_idx;
-    p.ws = static_cast<int32_t*>(a.workspace);
+    char* ws = static_cast<char*>(a.workspace);
+    p.ws = reinterpret_cast<int32_t*>(ws);
+    size_t off = align256(counts_bytes(a.Nq, a.B, a.Ld));
     magic_div((unsigned long long)a.B * a.Lq, &p.magic, &p.shift);
     magic_div((unsigned long long)a.Lq, &p.magic_lq, &p.shift_lq);
     if (a.cu_seqlens) {
-        // workspace: the [B][NG][Ld] counts, then docbase [B+1] at a 256-byte boundary
         p.cu = a.cu_seqlens;
         p.T = a.T;
-        const size_t off = (bwd_workspace_bytes(a.Nq, a.B, a.Lq, a.Ld) + 255) & ~(size_t)255;
-        p.docbase = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + off);
+        p.docbase = reinterpret_cast<int32_t*>(ws + off);
+        off += align256((size_t)(a.B + 1) * sizeof(int32_t));
+        p.dq_part = reinterpret_cast<float*>(ws + off);
         return a.elem == kBF16 ? launch_bwd_elem<kBF16, true>(p, stream) : launch_bwd_elem<kF16, true>(p, stream);
     }
+    p.dq_part = reinterpret_cast<float*>(ws + off);
     return a.elem == kBF16 ? launch_bwd_elem<kBF16, false>(p, stream) : launch_bwd_elem<kF16, false>(p, stream);
 }
 

@@ -197,6 +197,50 @@ int maxsim_bwd_varlen(const void* Q, const void* D_packed, const int32_t* cu_seq
     return hip_status(maxsim::launch_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t maxsim_bwd_scatter_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq) {
+    return maxsim::bwd_scatter_workspace_bytes(Nq, B, Lq);
+}
+
+int maxsim_bwd_scatter(const void* Q, const void* D, const int32_t* cu_seqlens, int32_t dtype,
+                       const int32_t* argmax, const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B,
+                       int32_t Ld, int64_t T, int32_t d, float* dQ, float* dD, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (Nq < 1 || B < 1 || Lq < 1 || Ld < 1) return MAXSIM_ERR_SHAPE;
+    if ((int64_t)Nq * B * Lq >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
+    const int64_t rows = cu_seqlens ? T : (int64_t)B * Ld;
+    if (rows < 0 || rows >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
+    if (d != kDim || Lq > kMaxLq || Ld > maxsim::kMaxLdBwd) return MAXSIM_ERR_UNSUPPORTED;
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_UNSUPPORTED;
+    if (!Q || !argmax || !grad_scores || !dQ || !workspace || (rows > 0 && (!D || !dD))) return MAXSIM_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(dQ, 16) || !aligned(dD, 16) ||
+        !aligned(cu_seqlens, 4) || !aligned(argmax, 4) || !aligned(grad_scores, 4) || !aligned(workspace, 256))
+        return MAXSIM_ERR_ALIGN;
+    if (workspace_bytes < maxsim::bwd_scatter_workspace_bytes(Nq, B, Lq)) return MAXSIM_ERR_WORKSPACE;
+    maxsim::BwdArgs a{};
+    a.Q = Q;
+    a.D = D;
+    a.argmax = argmax;
+    a.g = grad_scores;
+    a.Nq = Nq;
+    a.Lq = Lq;
+    a.B = B;
+    a.Ld = Ld;
+    a.elem = dtype == MAXSIM_BF16 ? maxsim::kBF16 : maxsim::kF16;
+    a.dQ = dQ;
+    a.dD = dD;
+    a.cu_seqlens = cu_seqlens;
+    a.T = cu_seqlens ? T : 0;
+    a.workspace = workspace;
+    return hip_status(maxsim::launch_bwd_scatter(a, static_cast<hipStream_t>(stream)));
+}
+
+int maxsim_bwd_prefer_scatter(int32_t Nq, int32_t Lq, int32_t B, int64_t rows) {
+    if (Nq < 1 || Lq < 1 || B < 1 || rows < 1) return 0;
+    // mean number of sources (query tokens) per destination row
+    const double per_row = (double)Nq * Lq * B / (double)rows;
+    return per_row < maxsim::kScatterMaxSourcesPerRow ? 1 : 0;
+}
+
 int maxsim_fwd_pairs(const void* Q, const void* D_packed, const int32_t* cu_seqlens, int32_t dtype,
                      const int32_t* pair_q, const int32_t* pair_b, int32_t P, int32_t Nq, int32_t Lq,
                      int32_t B, int64_t T, int32_t d, float* scores, int32_t* argmax, void* stream) {

@@ -13,6 +13,9 @@ enum ElemType { kF16 = 0, kBF16 = 1, kI8 = 2 };
 constexpr int kDim = 128;        // embedding width every kernel is built for
 constexpr int kMaxLq = 1024;     // query tokens one workgroup keeps on chip
 constexpr int kMaxLdBwd = 4096;  // document tokens the CSR fill kernel keeps in LDS
+// Below this mean number of sources per dD row the atomic scatter is faster
+// than building the CSR map (measured on MI355X).
+constexpr double kScatterMaxSourcesPerRow = 0.5;
 
 struct FwdArgs {
     const void* Q;            // [Nq, Lq, 128]
@@ -61,6 +64,9 @@ struct BwdArgs {
 int bwd_group(int32_t Ld);
 size_t bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld);
 size_t bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld);
+size_t bwd_scatter_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+// dD by atomic scatter (no CSR, no workspace), dQ gathered as in launch_bwd
+hipError_t launch_bwd_scatter(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace maxsim

@@ -46,7 +46,8 @@ def test_every_declared_symbol_is_exported_with_binding_arity():
     assert set(decl) == {"maxsim_fwd", "maxsim_fwd_varlen", "maxsim_fwd_i8", "maxsim_bwd_workspace_bytes",
                          "maxsim_bwd", "maxsim_status_string", "maxsim_fwd_pairs", "maxsim_topk",
                          "maxsim_two_stage_workspace_bytes", "maxsim_two_stage_topk",
-                         "maxsim_bwd_varlen_workspace_bytes", "maxsim_bwd_varlen"}
+                         "maxsim_bwd_varlen_workspace_bytes", "maxsim_bwd_varlen", "maxsim_bwd_scatter",
+                         "maxsim_bwd_prefer_scatter", "maxsim_bwd_scatter_workspace_bytes"}
     raw = ctypes.CDLL(LIB)
     for name, nargs in decl.items():
         assert hasattr(raw, name), name
@@ -241,10 +242,51 @@ def test_bwd_varlen_validation(kw, code):
 
 
 def test_bwd_varlen_workspace_bytes():
-    # the padded counts for max_Ld, then the per-document first slots at a 256-byte boundary
-    base = L.maxsim_bwd_workspace_bytes(10, 7, 32, 100)
-    n = L.maxsim_bwd_varlen_workspace_bytes(10, 7, 32, 100)
-    assert n == ((base + 255) // 256) * 256 + 8 * 4
+    # the counts for max_Ld, the per-document first slots, then the dQ chunk sums, each at a
+    # 256-byte boundary.  320 query rows fill 10 gather workgroups, so the 100 documents are
+    # split into min(ceil(512 / 10), 100 // 8) = 12 chunks for dQ.
+    counts = 100 * 1 * 100 * 4  # 10 queries form one group of 16 at Ld = 100
+    part = 12 * 320 * 128 * 4
+    assert L.maxsim_bwd_workspace_bytes(10, 100, 32, 100) == 40192 + part
+    assert L.maxsim_bwd_varlen_workspace_bytes(10, 100, 32, 100) == 40192 + 512 + part
+    assert counts <= 40192 < counts + 256
+    assert L.maxsim_bwd_scatter_workspace_bytes(10, 100, 32) == part
+    assert L.maxsim_bwd_scatter_workspace_bytes(10, 7, 32) == 256  # too few documents to split
+    assert L.maxsim_bwd_scatter_workspace_bytes(64, 64, 1024) == 256  # 65536 rows fill the chip: no split
     assert L.maxsim_bwd_varlen_workspace_bytes(0, 7, 32, 100) == 0
     assert L.maxsim_bwd_varlen_workspace_bytes(1, 1, 1, 5000) == 0
+    n = L.maxsim_bwd_varlen_workspace_bytes(10, 7, 32, 100)
     assert bwd_varlen(wsb=n - 1, Nq=10, B=7, Lq=32, maxld=100) == bd.MAXSIM_ERR_WORKSPACE
+
+
+def bwd_scatter(**kw):
+    a = dict(Q=A, D=A, cu=None, dt=0, A=A, g=A, Nq=4, Lq=32, B=5, Ld=64, T=0, d=128, dQ=A, dD=A, ws=A,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.maxsim_bwd_scatter(a["Q"], a["D"], a["cu"], a["dt"], a["A"], a["g"], a["Nq"], a["Lq"], a["B"],
+                                a["Ld"], a["T"], a["d"], a["dQ"], a["dD"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), bd.MAXSIM_ERR_NULL), (dict(D=None), bd.MAXSIM_ERR_NULL), (dict(dD=None), bd.MAXSIM_ERR_NULL),
+    (dict(A=None), bd.MAXSIM_ERR_NULL), (dict(g=None), bd.MAXSIM_ERR_NULL), (dict(dQ=None), bd.MAXSIM_ERR_NULL),
+    (dict(Nq=0), bd.MAXSIM_ERR_SHAPE), (dict(Ld=0), bd.MAXSIM_ERR_SHAPE), (dict(cu=A, T=-1), bd.MAXSIM_ERR_SHAPE),
+    (dict(cu=A, T=1 << 31), bd.MAXSIM_ERR_SHAPE), (dict(Nq=1 << 16, B=1 << 10, Lq=32), bd.MAXSIM_ERR_SHAPE),
+    (dict(Ld=4097), bd.MAXSIM_ERR_UNSUPPORTED), (dict(d=64), bd.MAXSIM_ERR_UNSUPPORTED),
+    (dict(dt=5), bd.MAXSIM_ERR_UNSUPPORTED), (dict(Lq=2000), bd.MAXSIM_ERR_UNSUPPORTED),
+    (dict(D=M), bd.MAXSIM_ERR_ALIGN), (dict(cu=M, T=10), bd.MAXSIM_ERR_ALIGN), (dict(g=M), bd.MAXSIM_ERR_ALIGN),
+    (dict(ws=None), bd.MAXSIM_ERR_NULL), (dict(ws=ctypes.c_void_p(0x10010)), bd.MAXSIM_ERR_ALIGN),
+    (dict(wsb=255), bd.MAXSIM_ERR_WORKSPACE),
+])
+def test_bwd_scatter_validation(kw, code):
+    assert bwd_scatter(**kw) == code
+
+
+def test_bwd_dispatch_rule():
+    """Scatter below the measured sources-per-row threshold, CSR above it."""
+    assert L.maxsim_bwd_prefer_scatter(1, 32, 1000, 1000 * 180) == 1      # 0.18 sources per row
+    assert L.maxsim_bwd_prefer_scatter(2, 32, 1000, 1000 * 180) == 1      # 0.36: scatter measured faster
+    assert L.maxsim_bwd_prefer_scatter(4, 32, 1000, 1000 * 180) == 0      # 0.71: CSR measured faster
+    assert L.maxsim_bwd_prefer_scatter(64, 1024, 64, 64 * 1024) == 0      # 64 per row (training)
+    assert L.maxsim_bwd_prefer_scatter(0, 32, 10, 100) == 0
+    assert L.maxsim_bwd_prefer_scatter(1, 32, 10, 0) == 0
