@@ -204,6 +204,39 @@ int maxsim_bwd_scatter(const void* Q, const void* D, const int32_t* cu_seqlens, 
  */
 int maxsim_bwd_prefer_scatter(int32_t Nq, int32_t Lq, int32_t B, int64_t rows);
 
+/* Bytes of device staging maxsim_fwd_host_stream needs (0 on bad sizes). */
+size_t maxsim_fwd_host_stream_staging_bytes(int32_t Nq, int32_t Lq, int32_t Ld, int32_t block_docs,
+                                            int32_t with_argmax);
+
+/*
+ * Out-of-core forward (Section 5 "Out-of-Core Corpus Scaling", Table 4): the
+ * corpus stays in host memory and is streamed to the GPU in blocks of
+ * block_docs documents; each block is scored by the fused forward while the
+ * next one is copied, so device memory holds two blocks, not the corpus.
+ *   Q [Nq, Lq, d] device (dtype).
+ *   D_host: the corpus in host memory, padded [B, Ld, d] (cu_seqlens_host
+ *     NULL; d_lens device [B] or NULL as for maxsim_fwd) or packed [T, d]
+ *     with cu_seqlens_host (host [B+1], read during this call; cu[0] = 0,
+ *     every length <= Ld) and cu_seqlens (the same on the device).  Ld is the
+ *     padded row stride, or the longest packed document (D_host may be NULL
+ *     for a packed corpus without rows).  Pinned memory
+ *     (hipHostMalloc) is needed for full copy speed; any host memory works.
+ *   scores [Nq, B] fp32 out (device), argmax [Nq, B, Lq] int32 out or NULL.
+ *   staging: device memory of maxsim_fwd_host_stream_staging_bytes() bytes,
+ *     256-byte aligned: two document blocks, the block's scores, cu_seqlens
+ *     and argmax.
+ * The call enqueues all work and returns: the copies run on a stream the
+ * library creates once per device, the forward on `stream`, which is ordered
+ * after the last block.  D_host and staging must stay valid until `stream`
+ * has finished.  Calls on one device are serialised while they enqueue.  Not
+ * for HIP graph capture.  Results equal maxsim_fwd / maxsim_fwd_varlen on the
+ * same documents.  Requires block_docs >= 1; other arguments as maxsim_fwd.
+ */
+int maxsim_fwd_host_stream(const void* Q, const void* D_host, const int32_t* cu_seqlens_host,
+                           const int32_t* cu_seqlens, const int32_t* d_lens, int32_t Nq, int32_t Lq, int32_t B,
+                           int32_t Ld, int32_t d, int32_t dtype, int32_t block_docs, void* staging,
+                           size_t staging_bytes, float* scores, int32_t* argmax, void* stream);
+
 /*
  * Scores of an explicit list of (query, document) pairs over a packed corpus
  * (Eq. (1) for each listed pair only).  This is the rescoring pass of the

@@ -43,6 +43,9 @@ SIGNATURES = {
     "maxsim_bwd_scatter": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32, _P, _P,
                                           _P, ctypes.c_size_t, _P]),
     "maxsim_bwd_prefer_scatter": (ctypes.c_int, [_I32, _I32, _I32, _I64]),
+    "maxsim_fwd_host_stream_staging_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
+    "maxsim_fwd_host_stream": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
+                                              ctypes.c_size_t, _P, _P, _P]),
     "maxsim_fwd_pairs": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32, _P, _P, _P]),
     "maxsim_topk": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, _P]),
     "maxsim_two_stage_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
@@ -349,6 +352,55 @@ def maxsim(Q, D, cu_seqlens=None, max_Ld=None, deterministic=True):
     if cu_seqlens is not None and max_Ld is None:
         raise ValueError("max_Ld is required with cu_seqlens")
     return MaxSimFunction.apply(Q, D, cu_seqlens, max_Ld, deterministic)
+
+
+def maxsim_fwd_host_stream_staging_bytes(Nq, Lq, Ld, block_docs, with_argmax):
+    return int(lib().maxsim_fwd_host_stream_staging_bytes(Nq, Lq, Ld, block_docs, int(bool(with_argmax))))
+
+
+def maxsim_fwd_host_stream(Q, D_host, block_docs, cu_seqlens_host=None, cu_seqlens=None, max_Ld=None, d_lens=None,
+                           scores=None, argmax=None, with_argmax=False, staging=None, stream=None):
+    """Score a corpus held in host memory (a CPU tensor, pinned for full speed) block by block.
+    Padded: D_host [B, Ld, 128].  Packed: D_host [T, 128], cu_seqlens_host (CPU int32 [B+1]),
+    cu_seqlens (the same on the device) and max_Ld.  Returns (scores [Nq, B], argmax or None).
+    The copies run after this returns: keep D_host alive until the stream has finished."""
+    Nq, Lq, d = Q.shape
+    dev = Q.device
+    _need(Q, "Q")
+    if D_host.is_cuda or not D_host.is_contiguous():
+        raise ValueError("D_host must be a contiguous host tensor")
+    if D_host.dtype != Q.dtype or D_host.shape[-1] != d:
+        raise ValueError("Q and D_host must share dtype and width")
+    if cu_seqlens_host is None:
+        B, Ld, _ = D_host.shape
+    else:
+        if cu_seqlens_host.is_cuda or cu_seqlens_host.dtype != torch.int32 or not cu_seqlens_host.is_contiguous():
+            raise ValueError("cu_seqlens_host must be a contiguous host int32 tensor")
+        if cu_seqlens is None or max_Ld is None:
+            raise ValueError("a packed corpus needs cu_seqlens on the device and max_Ld")
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        B = cu_seqlens_host.shape[0] - 1
+        Ld = int(max_Ld)
+    if d_lens is not None:
+        _need(d_lens, "d_lens", torch.int32, dev)
+    if scores is None:
+        scores = torch.empty((Nq, B), dtype=torch.float32, device=dev)
+    _need(scores, "scores", torch.float32, dev)
+    if argmax is None and with_argmax:
+        argmax = torch.empty((Nq, B, Lq), dtype=torch.int32, device=dev)
+    if argmax is not None:
+        _need(argmax, "argmax", torch.int32, dev)
+    nbytes = maxsim_fwd_host_stream_staging_bytes(Nq, Lq, Ld, block_docs, argmax is not None)
+    if staging is None:
+        staging = torch.empty(max(256, nbytes), dtype=torch.uint8, device=dev)
+    _need(staging, "staging", device=dev)
+    st = lib().maxsim_fwd_host_stream(_ptr(Q), ctypes.c_void_p(D_host.data_ptr()),
+                                      None if cu_seqlens_host is None else ctypes.c_void_p(cu_seqlens_host.data_ptr()),
+                                      _ptr(cu_seqlens), _ptr(d_lens), Nq, Lq, B, Ld, d, _dtype_code(Q),
+                                      int(block_docs), _ptr(staging), staging.numel(), _ptr(scores), _ptr(argmax),
+                                      _stream(Q, stream))
+    _check(st, "maxsim_fwd_host_stream")
+    return scores, argmax
 
 
 def maxsim_fwd_pairs(Q, D_packed, cu_seqlens, pair_q, pair_b, scores=None, argmax=None, with_argmax=False,

@@ -241,6 +241,55 @@ int maxsim_bwd_prefer_scatter(int32_t Nq, int32_t Lq, int32_t B, int64_t rows) {
     return per_row < maxsim::kScatterMaxSourcesPerRow ? 1 : 0;
 }
 
+size_t maxsim_fwd_host_stream_staging_bytes(int32_t Nq, int32_t Lq, int32_t Ld, int32_t block_docs,
+                                            int32_t with_argmax) {
+    if (Lq > kMaxLq) return 0;
+    return maxsim::host_stream_staging_bytes(Nq, Lq, Ld, block_docs, with_argmax != 0);
+}
+
+int maxsim_fwd_host_stream(const void* Q, const void* D_host, const int32_t* cu_seqlens_host,
+                           const int32_t* cu_seqlens, const int32_t* d_lens, int32_t Nq, int32_t Lq, int32_t B,
+                           int32_t Ld, int32_t d, int32_t dtype, int32_t block_docs, void* staging,
+                           size_t staging_bytes, float* scores, int32_t* argmax, void* stream) {
+    int st = check_common(Nq, Lq, B, d);
+    if (st != MAXSIM_OK) return st;
+    if (Ld < 1 || block_docs < 1) return MAXSIM_ERR_SHAPE;
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_UNSUPPORTED;
+    if (Nq == 0 || B == 0) return MAXSIM_OK;
+    const bool packed = cu_seqlens_host != nullptr;
+    if (!Q || !scores || !staging || (packed && !cu_seqlens)) return MAXSIM_ERR_NULL;
+    if (!D_host && (!packed || cu_seqlens_host[B] != 0)) return MAXSIM_ERR_NULL;  // only an empty corpus has none
+    if (packed && d_lens) return MAXSIM_ERR_SHAPE;  // lengths come from cu_seqlens
+    if (!aligned(Q, 16) || !aligned(D_host, 16) || !aligned(scores, 4) || !aligned(argmax, 4) ||
+        !aligned(d_lens, 4) || !aligned(cu_seqlens, 4) || !aligned(cu_seqlens_host, 4) || !aligned(staging, 256))
+        return MAXSIM_ERR_ALIGN;
+    if (staging_bytes < maxsim::host_stream_staging_bytes(Nq, Lq, Ld, block_docs, argmax != nullptr))
+        return MAXSIM_ERR_WORKSPACE;
+    if (packed) {  // the host offsets are read here: every block must fit its buffer
+        if (cu_seqlens_host[0] != 0) return MAXSIM_ERR_SHAPE;
+        for (int32_t b = 0; b < B; ++b) {
+            const int64_t len = (int64_t)cu_seqlens_host[b + 1] - cu_seqlens_host[b];
+            if (len < 0 || len > Ld) return MAXSIM_ERR_SHAPE;
+        }
+    }
+    maxsim::HostStreamArgs a{};
+    a.Q = Q;
+    a.D_host = D_host;
+    a.cu_host = cu_seqlens_host;
+    a.cu_dev = cu_seqlens;
+    a.d_lens = d_lens;
+    a.Nq = Nq;
+    a.Lq = Lq;
+    a.B = B;
+    a.Ld = Ld;
+    a.block_docs = block_docs;
+    a.elem = dtype == MAXSIM_BF16 ? maxsim::kBF16 : maxsim::kF16;
+    a.staging = staging;
+    a.scores = scores;
+    a.argmax = argmax;
+    return hip_status(maxsim::launch_fwd_host_stream(a, static_cast<hipStream_t>(stream)));
+}
+
 int maxsim_fwd_pairs(const void* Q, const void* D_packed, const int32_t* cu_seqlens, int32_t dtype,
                      const int32_t* pair_q, const int32_t* pair_b, int32_t P, int32_t Nq, int32_t Lq,
                      int32_t B, int64_t T, int32_t d, float* scores, int32_t* argmax, void* stream) {

@@ -42,6 +42,24 @@ hipError_t launch_topk(const float* scores, const int32_t* ids, int Nq, int B, i
                        hipStream_t stream);
 hipError_t launch_fill_pair_q(int32_t* pair_q, int64_t n, int K1, hipStream_t stream);
 
+// Out-of-core forward: the corpus is in host memory (pinned for full speed)
+// and is streamed through two device buffers in blocks of block_docs documents.
+struct HostStreamArgs {
+    const void* Q;               // device [Nq, Lq, 128]
+    const void* D_host;          // host: padded [B, Ld, 128] or packed [T, 128]
+    const int32_t* cu_host;      // packed: host [B+1] (nullptr: padded)
+    const int32_t* cu_dev;       // packed: the same on the device
+    const int32_t* d_lens;       // padded: device [B] or nullptr
+    int32_t Nq, Lq, B, Ld;       // Ld: padded row stride, or the longest packed document
+    int32_t block_docs;
+    int elem;
+    void* staging;               // host_stream_staging_bytes() bytes of device memory
+    float* scores;               // device [Nq, B]
+    int32_t* argmax;             // device [Nq, B, Lq] or nullptr
+};
+size_t host_stream_staging_bytes(int32_t Nq, int32_t Lq, int32_t Ld, int32_t block_docs, bool with_argmax);
+hipError_t launch_fwd_host_stream(const HostStreamArgs& a, hipStream_t stream);
+
 struct BwdArgs {
     const void* Q;            // [Nq, Lq, 128]
     const void* D;            // [B, Ld, 128]

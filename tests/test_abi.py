@@ -47,7 +47,8 @@ def test_every_declared_symbol_is_exported_with_binding_arity():
                          "maxsim_bwd", "maxsim_status_string", "maxsim_fwd_pairs", "maxsim_topk",
                          "maxsim_two_stage_workspace_bytes", "maxsim_two_stage_topk",
                          "maxsim_bwd_varlen_workspace_bytes", "maxsim_bwd_varlen", "maxsim_bwd_scatter",
-                         "maxsim_bwd_prefer_scatter", "maxsim_bwd_scatter_workspace_bytes"}
+                         "maxsim_bwd_prefer_scatter", "maxsim_bwd_scatter_workspace_bytes",
+                         "maxsim_fwd_host_stream_staging_bytes", "maxsim_fwd_host_stream"}
     raw = ctypes.CDLL(LIB)
     for name, nargs in decl.items():
         assert hasattr(raw, name), name
@@ -290,3 +291,50 @@ def test_bwd_dispatch_rule():
     assert L.maxsim_bwd_prefer_scatter(64, 1024, 64, 64 * 1024) == 0      # 64 per row (training)
     assert L.maxsim_bwd_prefer_scatter(0, 32, 10, 100) == 0
     assert L.maxsim_bwd_prefer_scatter(1, 32, 10, 0) == 0
+
+
+def host_stream(**kw):
+    a = dict(Q=A, D=A, cuh=None, cu=None, lens=None, Nq=2, Lq=32, B=10, Ld=64, d=128, dt=0, blk=4, st=A,
+             stb=1 << 40, scores=A, argmax=None, stream=None)
+    a.update(kw)
+    return L.maxsim_fwd_host_stream(a["Q"], a["D"], a["cuh"], a["cu"], a["lens"], a["Nq"], a["Lq"], a["B"],
+                                    a["Ld"], a["d"], a["dt"], a["blk"], a["st"], a["stb"], a["scores"],
+                                    a["argmax"], a["stream"])
+
+
+def test_host_stream_staging_bytes():
+    # two D blocks, the block's scores, its cu_seqlens [+ its argmax], each at a 256-byte boundary
+    n = L.maxsim_fwd_host_stream_staging_bytes(2, 32, 64, 4, 0)
+    assert n == 2 * (4 * 64 * 256) + 256 + 256
+    assert L.maxsim_fwd_host_stream_staging_bytes(2, 32, 64, 4, 1) == n + 1024
+    assert L.maxsim_fwd_host_stream_staging_bytes(0, 32, 64, 4, 0) == 0
+    assert L.maxsim_fwd_host_stream_staging_bytes(2, 32, 64, 0, 0) == 0
+    assert L.maxsim_fwd_host_stream_staging_bytes(2, 1025, 64, 4, 0) == 0
+
+
+def test_host_stream_validation():
+    """Every rejection happens on the host before any HIP call (the host
+    cu_seqlens is read here, so it is a real array)."""
+    cu_ok = (ctypes.c_int32 * 4)(0, 10, 10, 70)
+    cu_long = (ctypes.c_int32 * 4)(0, 10, 75, 80)   # a document longer than Ld = 64
+    cu_off = (ctypes.c_int32 * 4)(5, 10, 20, 30)    # does not start at 0
+    cu_empty = (ctypes.c_int32 * 4)(0, 0, 0, 0)
+    assert host_stream(Q=None) == bd.MAXSIM_ERR_NULL
+    assert host_stream(D=None) == bd.MAXSIM_ERR_NULL
+    assert host_stream(st=None) == bd.MAXSIM_ERR_NULL
+    assert host_stream(cuh=cu_ok, B=3) == bd.MAXSIM_ERR_NULL  # device cu_seqlens missing
+    assert host_stream(blk=0) == bd.MAXSIM_ERR_SHAPE
+    assert host_stream(Ld=0) == bd.MAXSIM_ERR_SHAPE
+    assert host_stream(cuh=cu_long, cu=A, B=3) == bd.MAXSIM_ERR_SHAPE
+    assert host_stream(cuh=cu_off, cu=A, B=3) == bd.MAXSIM_ERR_SHAPE
+    assert host_stream(cuh=cu_ok, cu=A, B=3, lens=A) == bd.MAXSIM_ERR_SHAPE
+    assert host_stream(cuh=cu_ok, cu=A, B=3, D=None) == bd.MAXSIM_ERR_NULL
+    assert host_stream(d=64) == bd.MAXSIM_ERR_UNSUPPORTED
+    assert host_stream(dt=2) == bd.MAXSIM_ERR_UNSUPPORTED
+    assert host_stream(st=ctypes.c_void_p(0x10010)) == bd.MAXSIM_ERR_ALIGN
+    assert host_stream(D=M) == bd.MAXSIM_ERR_ALIGN
+    assert host_stream(stb=1000) == bd.MAXSIM_ERR_WORKSPACE
+    assert host_stream(Nq=0) == bd.MAXSIM_OK
+    assert host_stream(B=0) == bd.MAXSIM_OK
+    # an empty packed corpus may pass no host rows; this still needs staging
+    assert host_stream(cuh=cu_empty, cu=A, B=3, D=None, stb=0) == bd.MAXSIM_ERR_WORKSPACE
