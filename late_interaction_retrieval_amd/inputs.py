@@ -199,3 +199,44 @@ def fp16_of_int8_workload(w, seed=0):
 def random_rows(seed, n, d, dtype, workload_id=99, stream=STREAM_EXTRA):
     """Small helper for tests: n unit rows under an arbitrary id/stream."""
     return unit_rows(seed, workload_id, stream, n, d, dtype)
+
+
+# Point clouds for the Chamfer distance (paper Section 4.2 "Generalization to
+# Chamfer Distance": two point sets in R^3, up to 100K points).  Recipe: each
+# cloud is a noisy sample of the unit sphere, the shape-matching setting the
+# page names: directions x ~ N(0, I_3) divided by their fp32 norm, then
+# per-coordinate N(0, sigma^2) noise, all fp32, drawn with
+# ``default_rng([seed, CHAMFER_ID, stream, item])`` (stream 0 = P, 1 = Q).
+CHAMFER_ID = 6
+CHAMFER_WORKLOADS = {
+    "chamfer_100k": dict(Bt=1, N=100000, M=100000),
+    "chamfer_batch": dict(Bt=32, N=2048, M=2048),
+}
+
+
+def sphere_cloud(seed, stream, item, n, sigma=0.01):
+    """n points near the unit sphere, fp32 [n, 3]."""
+    rng = np.random.default_rng([seed, CHAMFER_ID, stream, item])
+    x = np.empty((n, 3), np.float32)
+    rng.standard_normal(out=x, dtype=np.float32)
+    nrm = np.sqrt((x * x).sum(axis=1, dtype=np.float32))
+    x /= np.where(nrm > 0, nrm, np.float32(1))[:, None]
+    noise = np.empty((n, 3), np.float32)
+    rng.standard_normal(out=noise, dtype=np.float32)
+    x += np.float32(sigma) * noise
+    return x
+
+
+def point_clouds(seed=0, Bt=1, N=1000, M=1000, sigma=0.01):
+    """(P [Bt, N, 3], Q [Bt, M, 3]) fp32: batch item b of P and of Q are two
+    independent noisy samples of the unit sphere."""
+    P = np.stack([sphere_cloud(seed, 0, b, N, sigma) for b in range(Bt)]) if Bt else np.zeros((0, N, 3), np.float32)
+    Q = np.stack([sphere_cloud(seed, 1, b, M, sigma) for b in range(Bt)]) if Bt else np.zeros((0, M, 3), np.float32)
+    return P, Q
+
+
+def make_chamfer(name, seed=0, **over):
+    w = dict(CHAMFER_WORKLOADS[name])
+    w.update({k: v for k, v in over.items() if v is not None})
+    P, Q = point_clouds(seed, w["Bt"], w["N"], w["M"])
+    return dict(name=name, P=P, Q=Q, **w)

@@ -25,4 +25,9 @@ from .oracle import (  # noqa: F401
     two_stage_topk,
     csr_build_varlen,
     bwd_varlen,
+    chamfer_nn,
+    chamfer,
+    chamfer_loss,
+    chamfer_csr,
+    chamfer_bwd,
 )

@@ -1,5 +1,6 @@
 /*
- * maxsim_oracle.c -- plain, slow, CPU reference for the fused MaxSim path.
+ * maxsim_oracle.c -- plain, slow, CPU reference for the fused MaxSim path
+ * and its Chamfer-distance generalisation.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
  * calls this file: only the tests, the smoke check and the CPU-baseline leg
@@ -510,4 +511,122 @@ int oracle_num_threads(void) {
         }
     }
     return n;
+}
+
+/* ------------------------------------------------------------------ */
+/* Chamfer distance (Section 4.2, "Generalization to Chamfer Distance"). */
+/* ------------------------------------------------------------------ */
+/*
+ * The same hard-selection structure with a minimum of squared Euclidean
+ * distances in place of the maximum of inner products, between two point
+ * sets in R^3.  Clouds come in batches: A [Bt, Na, 3] and B [Bt, Nb, 3]
+ * (fp32), and batch item b of A is only compared with item b of B.
+ */
+
+/* For every point s of A[b]: dist = min over t of |A[b,s] - B[b,t]|^2 and
+ * idx = the first t attaining it (fp64 from the fp32 coordinates, the three
+ * squares added in x, y, z order).  An empty B gives +inf and -1. */
+int oracle_chamfer_nn(const float* A, const float* B, int Bt, int Na, int Nb, double* dist, int32_t* idx) {
+    if (Bt < 0 || Na < 0 || Nb < 0) return 1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t s = 0; s < (int64_t)Bt * Na; ++s) {
+        const int64_t b = s / Na;
+        const float* a = A + s * 3;
+        double best = INFINITY;
+        int32_t arg = -1;
+        for (int t = 0; t < Nb; ++t) {
+            const float* p = B + (b * Nb + t) * 3;
+            const double dx = (double)a[0] - (double)p[0];
+            const double dy = (double)a[1] - (double)p[1];
+            const double dz = (double)a[2] - (double)p[2];
+            const double dd = dx * dx + dy * dy + dz * dz;
+            if (dd < best) {
+                best = dd;
+                arg = t;
+            }
+        }
+        dist[s] = best;
+        idx[s] = arg;
+    }
+    return 0;
+}
+
+/* The inverse map of a nearest-neighbour selection (Section 4.2
+ * "Runtime Inverse-Grid Construction" applied to the argmin): source
+ * s = b*Na + i selects destination b*Nb + idx[b,i]; row_ptr [Bt*Nb + 1] is
+ * the exclusive prefix of the per-destination counts and col_idx lists each
+ * destination's sources in ascending s.  Sources with idx = -1 select
+ * nothing; col_idx has row_ptr[Bt*Nb] entries. */
+int oracle_chamfer_csr(const int32_t* idx, int Bt, int Na, int Nb, int32_t* row_ptr, int32_t* col_idx) {
+    if (Bt < 0 || Na < 0 || Nb < 0) return 1;
+    const int64_t nd = (int64_t)Bt * Nb;
+    int64_t* cnt = calloc(nd + 1, sizeof(int64_t));
+    if (!cnt) return 2;
+    for (int64_t s = 0; s < (int64_t)Bt * Na; ++s) {
+        if (idx[s] < 0) continue;
+        if (idx[s] >= Nb) { free(cnt); return 3; }
+        cnt[(s / Na) * Nb + idx[s]] += 1;
+    }
+    int64_t run = 0;
+    for (int64_t r = 0; r < nd; ++r) {
+        row_ptr[r] = (int32_t)run;
+        run += cnt[r];
+        cnt[r] = row_ptr[r];  /* now the fill cursor of row r */
+    }
+    row_ptr[nd] = (int32_t)run;
+    for (int64_t s = 0; s < (int64_t)Bt * Na; ++s) {  /* ascending s: a stable fill */
+        if (idx[s] < 0) continue;
+        const int64_t r = (s / Na) * Nb + idx[s];
+        col_idx[cnt[r]] = (int32_t)s;
+        cnt[r] += 1;
+    }
+    free(cnt);
+    return 0;
+}
+
+/* Gradients of L = sum_i gp[b,i] * distP[b,i] + sum_j gq[b,j] * distQ[b,j]
+ * with the selections fixed (the saved argmins), distP from P to its nearest
+ * point of Q and distQ from Q to its nearest point of P:
+ *   dP[b,i] = 2 gp[b,i] (P[b,i] - Q[b,idx_p[b,i]])
+ *           + sum over j with idx_q[b,j] = i of 2 gq[b,j] (P[b,i] - Q[b,j])
+ *   dQ[b,j] = 2 gq[b,j] (Q[b,j] - P[b,idx_q[b,j]])
+ *           + sum over i with idx_p[b,i] = j of 2 gp[b,i] (Q[b,j] - P[b,i])
+ * The sums run over the selecting points in ascending order.  The Chamfer
+ * loss of the page is gp = 1/N, gq = 1/M.  Selections of -1 add nothing. */
+int oracle_chamfer_bwd(const float* P, const float* Q, int Bt, int N, int M, const int32_t* idx_p,
+                       const int32_t* idx_q, const float* gp, const float* gq, double* dP, double* dQ) {
+    if (Bt < 0 || N < 0 || M < 0) return 1;
+    memset(dP, 0, sizeof(double) * (size_t)Bt * N * 3);
+    memset(dQ, 0, sizeof(double) * (size_t)Bt * M * 3);
+    for (int b = 0; b < Bt; ++b) {
+        /* P's own terms, and what each P point adds to the Q point it selects */
+        for (int i = 0; i < N; ++i) {
+            const int64_t pi = (int64_t)b * N + i;
+            const int32_t j = idx_p[pi];
+            if (j < 0) continue;
+            if (j >= M) return 3;
+            const int64_t qj = (int64_t)b * M + j;
+            const double w = 2.0 * (double)gp[pi];
+            for (int k = 0; k < 3; ++k) {
+                const double diff = (double)P[pi * 3 + k] - (double)Q[qj * 3 + k];
+                dP[pi * 3 + k] += w * diff;
+                dQ[qj * 3 + k] -= w * diff;
+            }
+        }
+        /* Q's own terms, and what each Q point adds to the P point it selects */
+        for (int j = 0; j < M; ++j) {
+            const int64_t qj = (int64_t)b * M + j;
+            const int32_t i = idx_q[qj];
+            if (i < 0) continue;
+            if (i >= N) return 3;
+            const int64_t pi = (int64_t)b * N + i;
+            const double w = 2.0 * (double)gq[qj];
+            for (int k = 0; k < 3; ++k) {
+                const double diff = (double)Q[qj * 3 + k] - (double)P[pi * 3 + k];
+                dQ[qj * 3 + k] += w * diff;
+                dP[pi * 3 + k] -= w * diff;
+            }
+        }
+    }
+    return 0;
 }

@@ -62,9 +62,13 @@ def _load():
         lib.oracle_topk.argtypes = [P, I, I, I, P, P]
         lib.oracle_csr_build_varlen.argtypes = [P, I, I, I, P, P, P]
         lib.oracle_bwd_varlen.argtypes = [P, P, P, I, P, P, I, I, I, I, P, P]
+        lib.oracle_chamfer_nn.argtypes = [P, P, I, I, I, P, P]
+        lib.oracle_chamfer_csr.argtypes = [P, I, I, I, P, P]
+        lib.oracle_chamfer_bwd.argtypes = [P, P, I, I, I, P, P, P, P, P, P]
         for name in ("oracle_fwd_padded", "oracle_fwd_varlen", "oracle_fwd_i8", "oracle_sim_at",
                      "oracle_csr_build", "oracle_bwd", "oracle_num_threads", "oracle_fwd_pairs",
-                     "oracle_topk", "oracle_csr_build_varlen", "oracle_bwd_varlen"):
+                     "oracle_topk", "oracle_csr_build_varlen", "oracle_bwd_varlen", "oracle_chamfer_nn",
+                     "oracle_chamfer_csr", "oracle_chamfer_bwd"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -267,3 +271,67 @@ def bwd_varlen(Q, D_packed, cu_seqlens, dtype, argmax, g):
     _check(_load().oracle_bwd_varlen(_p(Qb), _p(Db), _p(cu), dtype, _p(A), _p(gg), Nq, Lq, B, d, _p(dQ), _p(dD)),
            "bwd_varlen")
     return dQ, dD
+
+
+def _points(X):
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    if X.ndim == 2:
+        X = X[None]
+    assert X.ndim == 3 and X.shape[2] == 3
+    return X
+
+
+def chamfer_nn(A, B):
+    """For every point of A [Bt, Na, 3]: (squared distance to the nearest point of
+    B [Bt, Nb, 3] in fp64 [Bt, Na], its first index int32 [Bt, Na]); batch items pair up."""
+    A, B = _points(A), _points(B)
+    Bt, Na, _ = A.shape
+    assert B.shape[0] == Bt
+    Nb = B.shape[1]
+    dist = np.empty((Bt, Na), np.float64)
+    idx = np.empty((Bt, Na), np.int32)
+    _check(_load().oracle_chamfer_nn(_p(A), _p(B), Bt, Na, Nb, _p(dist), _p(idx)), "chamfer_nn")
+    return dist, idx
+
+
+def chamfer(P, Q):
+    """Both directions: (dist_p, idx_p, dist_q, idx_q)."""
+    dp, ip = chamfer_nn(P, Q)
+    dq, iq = chamfer_nn(Q, P)
+    return dp, ip, dq, iq
+
+
+def chamfer_loss(P, Q):
+    """The page's Chamfer distance per batch item: mean_p min_q |p-q|^2 + mean_q min_p |q-p|^2."""
+    dp, _, dq, _ = chamfer(P, Q)
+    return dp.mean(axis=1) + dq.mean(axis=1)
+
+
+def chamfer_csr(idx, Nb):
+    """Inverse map of a selection idx [Bt, Na] into Nb destinations per item:
+    (row_ptr [Bt*Nb + 1], col_idx [row_ptr[-1]]) with global source ids b*Na + i."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    if idx.ndim == 1:
+        idx = idx[None]
+    Bt, Na = idx.shape
+    row_ptr = np.empty(Bt * Nb + 1, np.int32)
+    col_idx = np.empty(max(1, Bt * Na), np.int32)
+    _check(_load().oracle_chamfer_csr(_p(idx), Bt, Na, Nb, _p(row_ptr), _p(col_idx)), "chamfer_csr")
+    return row_ptr, col_idx[:row_ptr[-1]]
+
+
+def chamfer_bwd(P, Q, idx_p, idx_q, gp, gq):
+    """Gradients (dP [Bt, N, 3], dQ [Bt, M, 3], fp64) of sum gp*dist_p + sum gq*dist_q
+    with the selections fixed."""
+    P, Q = _points(P), _points(Q)
+    Bt, N, _ = P.shape
+    M = Q.shape[1]
+    ip = np.ascontiguousarray(idx_p, dtype=np.int32).reshape(Bt, N)
+    iq = np.ascontiguousarray(idx_q, dtype=np.int32).reshape(Bt, M)
+    gp = np.ascontiguousarray(gp, dtype=np.float32).reshape(Bt, N)
+    gq = np.ascontiguousarray(gq, dtype=np.float32).reshape(Bt, M)
+    dP = np.empty((Bt, N, 3), np.float64)
+    dQ = np.empty((Bt, M, 3), np.float64)
+    _check(_load().oracle_chamfer_bwd(_p(P), _p(Q), Bt, N, M, _p(ip), _p(iq), _p(gp), _p(gq), _p(dP), _p(dQ)),
+           "chamfer_bwd")
+    return dP, dQ

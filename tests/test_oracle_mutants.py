@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "maxsim_oracle.c")
 PINS = ["tests/test_oracle_fwd.py", "tests/test_oracle_i8.py", "tests/test_oracle_bwd.py",
-        "tests/test_oracle_topk.py", "tests/test_oracle_bwd_varlen.py"]
+        "tests/test_oracle_topk.py", "tests/test_oracle_bwd_varlen.py", "tests/test_oracle_chamfer.py"]
 
 MUTANTS = {
     "tie_takes_last_index": ("            if (s > m) {\n                m = s;\n                arg = j;",
@@ -53,6 +53,16 @@ MUTANTS = {
                                          "            const double gqb"),
     "pairs_wrong_query": ("++e) qd[e] = decode(Q[(int64_t)q * Lq * d + e], dtype);",
                           "++e) qd[e] = decode(Q[(int64_t)(Nq - 1 - q) * Lq * d + e], dtype);"),
+    "chamfer_tie_takes_last": ("            if (dd < best) {", "            if (dd <= best) {"),
+    "chamfer_dropped_z": ("const double dd = dx * dx + dy * dy + dz * dz;", "const double dd = dx * dx + dy * dy;"),
+    "chamfer_wrong_batch_stride": ("const float* p = B + (b * Nb + t) * 3;", "const float* p = B + (b * Na + t) * 3;"),
+    "chamfer_csr_unstable": ("    for (int64_t s = 0; s < (int64_t)Bt * Na; ++s) {  /* ascending s: a stable fill */",
+                             "    for (int64_t s = (int64_t)Bt * Na - 1; s >= 0; --s) {  /* ascending s: a stable fill */"),
+    "chamfer_reverse_term_dropped": ("                dQ[qj * 3 + k] += w * diff;\n                dP[pi * 3 + k] -= w * diff;",
+                                     "                dQ[qj * 3 + k] += w * diff;"),
+    "chamfer_own_term_sign": ("                dP[pi * 3 + k] += w * diff;\n                dQ[qj * 3 + k] -= w * diff;",
+                              "                dP[pi * 3 + k] -= w * diff;\n                dQ[qj * 3 + k] -= w * diff;"),
+    "chamfer_factor_two_dropped": ("            const double w = 2.0 * (double)gq[qj];", "            const double w = (double)gq[qj];"),
 }
 
 
