@@ -237,6 +237,51 @@ int maxsim_fwd_host_stream(const void* Q, const void* D_host, const int32_t* cu_
                            int32_t Ld, int32_t d, int32_t dtype, int32_t block_docs, void* staging,
                            size_t staging_bytes, float* scores, int32_t* argmax, void* stream);
 
+/* Bytes of device workspace maxsim_chamfer_fwd needs (0 on bad sizes). */
+size_t maxsim_chamfer_fwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M);
+
+/*
+ * Chamfer forward (Section 4.2 "Generalization to Chamfer Distance"): the
+ * same hard selection with the minimum of squared Euclidean distances in
+ * place of the maximum of inner products, between point clouds
+ * P [Bt, N, 3] and Q [Bt, M, 3] (fp32, device; item b of P is compared with
+ * item b of Q only).  No [N, M] matrix is formed.
+ *   dist_p [Bt, N] fp32 out: min over j of |P[b,i] - Q[b,j]|^2 (fp32,
+ *     (dx*dx + dy*dy) + dz*dz with fused multiply-adds);
+ *   idx_p [Bt, N] int32 out: the first j attaining it (-1 when M = 0, with
+ *     dist +inf);
+ *   dist_q, idx_q [Bt, M]: the same from Q to P.
+ * The page's loss is mean(dist_p) + mean(dist_q) per item.
+ * workspace: maxsim_chamfer_fwd_workspace_bytes() bytes, 256-byte aligned.
+ * Requires Bt, N, M >= 0, Bt*N and Bt*M < 2^31.
+ */
+int maxsim_chamfer_fwd(const float* P, const float* Q, int32_t Bt, int32_t N, int32_t M, float* dist_p,
+                       int32_t* idx_p, float* dist_q, int32_t* idx_q, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Bytes of device workspace maxsim_chamfer_bwd needs (0 on bad sizes). */
+size_t maxsim_chamfer_bwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M);
+
+/*
+ * Chamfer backward through the saved selections (Section 4.2: the same
+ * inverse-grid CSR and destination-owned rows as the MaxSim backward).
+ * With grad_p [Bt, N] = dL/d dist_p and grad_q [Bt, M] = dL/d dist_q:
+ *   dP[b,i] = 2 grad_p[b,i] (P[b,i] - Q[b,idx_p[b,i]])
+ *           + sum over j with idx_q[b,j] = i of 2 grad_q[b,j] (P[b,i] - Q[b,j])
+ *   dQ[b,j] likewise with the roles of the clouds swapped (fp32 out).
+ * CSR maps (deterministic, sources in ascending order):
+ *   row_ptr_p [Bt*N + 1], col_idx_p [Bt*M]: for P point r = b*N + i, the Q
+ *     points (global index b*M + j) that select it;
+ *   row_ptr_q [Bt*M + 1], col_idx_q [Bt*N]: the same for the Q points.
+ *   Entries past row_ptr[last] (sources with idx -1) are unspecified.
+ * Selections of -1 add nothing.  workspace: maxsim_chamfer_bwd_workspace_bytes()
+ * bytes, 256-byte aligned.  Requirements as maxsim_chamfer_fwd.
+ */
+int maxsim_chamfer_bwd(const float* P, const float* Q, const int32_t* idx_p, const int32_t* idx_q,
+                       const float* grad_p, const float* grad_q, int32_t Bt, int32_t N, int32_t M, float* dP,
+                       float* dQ, int32_t* row_ptr_p, int32_t* col_idx_p, int32_t* row_ptr_q, int32_t* col_idx_q,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Scores of an explicit list of (query, document) pairs over a packed corpus
  * (Eq. (1) for each listed pair only).  This is the rescoring pass of the

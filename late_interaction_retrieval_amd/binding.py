@@ -46,6 +46,11 @@ SIGNATURES = {
     "maxsim_fwd_host_stream_staging_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
     "maxsim_fwd_host_stream": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                               ctypes.c_size_t, _P, _P, _P]),
+    "maxsim_chamfer_fwd_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "maxsim_chamfer_fwd": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "maxsim_chamfer_bwd_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "maxsim_chamfer_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
     "maxsim_fwd_pairs": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32, _P, _P, _P]),
     "maxsim_topk": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, _P]),
     "maxsim_two_stage_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
@@ -401,6 +406,90 @@ def maxsim_fwd_host_stream(Q, D_host, block_docs, cu_seqlens_host=None, cu_seqle
                                       _stream(Q, stream))
     _check(st, "maxsim_fwd_host_stream")
     return scores, argmax
+
+
+def _clouds(P, Q):
+    if P.dim() == 2:
+        P = P.unsqueeze(0)
+    if Q.dim() == 2:
+        Q = Q.unsqueeze(0)
+    _need(P, "P", torch.float32)
+    _need(Q, "Q", torch.float32, P.device)
+    if P.shape[0] != Q.shape[0] or P.shape[2] != 3 or Q.shape[2] != 3:
+        raise ValueError("P [Bt, N, 3] and Q [Bt, M, 3] must share Bt")
+    return P, Q
+
+
+def maxsim_chamfer_fwd(P, Q, workspace=None, stream=None):
+    """Nearest neighbours both ways between P [Bt, N, 3] and Q [Bt, M, 3] (fp32):
+    (dist_p [Bt, N], idx_p, dist_q [Bt, M], idx_q); squared distances."""
+    P, Q = _clouds(P, Q)
+    Bt, N, _ = P.shape
+    M = Q.shape[1]
+    dev = P.device
+    dist_p = torch.empty((Bt, N), dtype=torch.float32, device=dev)
+    idx_p = torch.empty((Bt, N), dtype=torch.int32, device=dev)
+    dist_q = torch.empty((Bt, M), dtype=torch.float32, device=dev)
+    idx_q = torch.empty((Bt, M), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(256, int(lib().maxsim_chamfer_fwd_workspace_bytes(Bt, N, M))), dtype=torch.uint8,
+                                device=dev)
+    st = lib().maxsim_chamfer_fwd(_ptr(P), _ptr(Q), Bt, N, M, _ptr(dist_p), _ptr(idx_p), _ptr(dist_q), _ptr(idx_q),
+                                  _ptr(workspace), workspace.numel(), _stream(P, stream))
+    _check(st, "maxsim_chamfer_fwd")
+    return dist_p, idx_p, dist_q, idx_q
+
+
+def maxsim_chamfer_bwd(P, Q, idx_p, idx_q, grad_p, grad_q, workspace=None, stream=None):
+    """Gradients of sum grad_p*dist_p + sum grad_q*dist_q through the saved selections:
+    (dP, dQ, row_ptr_p, col_idx_p, row_ptr_q, col_idx_q)."""
+    P, Q = _clouds(P, Q)
+    Bt, N, _ = P.shape
+    M = Q.shape[1]
+    dev = P.device
+    for t, n in ((idx_p, "idx_p"), (idx_q, "idx_q")):
+        _need(t, n, torch.int32, dev)
+    for t, n in ((grad_p, "grad_p"), (grad_q, "grad_q")):
+        _need(t, n, torch.float32, dev)
+    dP = torch.empty((Bt, N, 3), dtype=torch.float32, device=dev)
+    dQ = torch.empty((Bt, M, 3), dtype=torch.float32, device=dev)
+    rp_p = torch.empty(Bt * N + 1, dtype=torch.int32, device=dev)
+    ci_p = torch.empty(max(1, Bt * M), dtype=torch.int32, device=dev)
+    rp_q = torch.empty(Bt * M + 1, dtype=torch.int32, device=dev)
+    ci_q = torch.empty(max(1, Bt * N), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(256, int(lib().maxsim_chamfer_bwd_workspace_bytes(Bt, N, M))), dtype=torch.uint8,
+                                device=dev)
+    st = lib().maxsim_chamfer_bwd(_ptr(P), _ptr(Q), _ptr(idx_p), _ptr(idx_q), _ptr(grad_p), _ptr(grad_q), Bt, N, M,
+                                  _ptr(dP), _ptr(dQ), _ptr(rp_p), _ptr(ci_p), _ptr(rp_q), _ptr(ci_q),
+                                  _ptr(workspace), workspace.numel(), _stream(P, stream))
+    _check(st, "maxsim_chamfer_bwd")
+    return dP, dQ, rp_p, ci_p, rp_q, ci_q
+
+
+class ChamferFunction(torch.autograd.Function):
+    """(dist_p, dist_q) with autograd: the forward saves the nearest-neighbour
+    indices, the backward inverts them (paper Section 4.2, Chamfer distance)."""
+
+    @staticmethod
+    def forward(ctx, P, Q):
+        dist_p, idx_p, dist_q, idx_q = maxsim_chamfer_fwd(P, Q)
+        ctx.save_for_backward(P, Q, idx_p, idx_q)
+        return dist_p, dist_q
+
+    @staticmethod
+    def backward(ctx, grad_p, grad_q):
+        P, Q, idx_p, idx_q = ctx.saved_tensors
+        dP, dQ, _, _, _, _ = maxsim_chamfer_bwd(P, Q, idx_p, idx_q, grad_p.float().contiguous(),
+                                                grad_q.float().contiguous())
+        return dP.reshape(P.shape), dQ.reshape(Q.shape)
+
+
+def chamfer_distance(P, Q):
+    """The page's Chamfer distance per batch item, mean_p min_q |p-q|^2 +
+    mean_q min_p |q-p|^2, for P [Bt, N, 3] and Q [Bt, M, 3] fp32, with autograd."""
+    dist_p, dist_q = ChamferFunction.apply(P, Q)
+    return dist_p.mean(dim=-1) + dist_q.mean(dim=-1)
 
 
 def maxsim_fwd_pairs(Q, D_packed, cu_seqlens, pair_q, pair_b, scores=None, argmax=None, with_argmax=False,

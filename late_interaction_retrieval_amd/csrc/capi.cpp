@@ -290,6 +290,85 @@ int maxsim_fwd_host_stream(const void* Q, const void* D_host, const int32_t* cu_
     return hip_status(maxsim::launch_fwd_host_stream(a, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+int check_chamfer(int32_t Bt, int32_t N, int32_t M) {
+    if (Bt < 0 || N < 0 || M < 0) return MAXSIM_ERR_SHAPE;
+    if ((int64_t)Bt * N >= ((int64_t)1 << 31) || (int64_t)Bt * M >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
+    return MAXSIM_OK;
+}
+}  // namespace
+
+size_t maxsim_chamfer_fwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M) {
+    if (check_chamfer(Bt, N, M) != MAXSIM_OK) return 0;
+    return maxsim::chamfer_fwd_workspace_bytes(Bt, N, M);
+}
+
+int maxsim_chamfer_fwd(const float* P, const float* Q, int32_t Bt, int32_t N, int32_t M, float* dist_p,
+                       int32_t* idx_p, float* dist_q, int32_t* idx_q, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    int st = check_chamfer(Bt, N, M);
+    if (st != MAXSIM_OK) return st;
+    if (Bt == 0 || (N == 0 && M == 0)) return MAXSIM_OK;
+    if (!workspace || (N > 0 && (!P || !dist_p || !idx_p)) || (M > 0 && (!Q || !dist_q || !idx_q)))
+        return MAXSIM_ERR_NULL;
+    if (!aligned(P, 4) || !aligned(Q, 4) || !aligned(dist_p, 4) || !aligned(idx_p, 4) || !aligned(dist_q, 4) ||
+        !aligned(idx_q, 4) || !aligned(workspace, 256))
+        return MAXSIM_ERR_ALIGN;
+    if (workspace_bytes < maxsim::chamfer_fwd_workspace_bytes(Bt, N, M)) return MAXSIM_ERR_WORKSPACE;
+    maxsim::ChamferArgs a{};
+    a.P = P;
+    a.Q = Q;
+    a.Bt = Bt;
+    a.N = N;
+    a.M = M;
+    a.dist_p = dist_p;
+    a.idx_p = idx_p;
+    a.dist_q = dist_q;
+    a.idx_q = idx_q;
+    a.workspace = workspace;
+    return hip_status(maxsim::launch_chamfer_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t maxsim_chamfer_bwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M) {
+    if (check_chamfer(Bt, N, M) != MAXSIM_OK) return 0;
+    return maxsim::chamfer_bwd_workspace_bytes(Bt, N, M);
+}
+
+int maxsim_chamfer_bwd(const float* P, const float* Q, const int32_t* idx_p, const int32_t* idx_q,
+                       const float* grad_p, const float* grad_q, int32_t Bt, int32_t N, int32_t M, float* dP,
+                       float* dQ, int32_t* row_ptr_p, int32_t* col_idx_p, int32_t* row_ptr_q, int32_t* col_idx_q,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_chamfer(Bt, N, M);
+    if (st != MAXSIM_OK) return st;
+    if (Bt == 0) return MAXSIM_OK;
+    if (!workspace || !row_ptr_p || !row_ptr_q) return MAXSIM_ERR_NULL;
+    if (N > 0 && (!P || !idx_p || !grad_p || !dP || !col_idx_q)) return MAXSIM_ERR_NULL;
+    if (M > 0 && (!Q || !idx_q || !grad_q || !dQ || !col_idx_p)) return MAXSIM_ERR_NULL;
+    if (!aligned(P, 4) || !aligned(Q, 4) || !aligned(idx_p, 4) || !aligned(idx_q, 4) || !aligned(grad_p, 4) ||
+        !aligned(grad_q, 4) || !aligned(dP, 4) || !aligned(dQ, 4) || !aligned(row_ptr_p, 4) ||
+        !aligned(col_idx_p, 4) || !aligned(row_ptr_q, 4) || !aligned(col_idx_q, 4) || !aligned(workspace, 256))
+        return MAXSIM_ERR_ALIGN;
+    if (workspace_bytes < maxsim::chamfer_bwd_workspace_bytes(Bt, N, M)) return MAXSIM_ERR_WORKSPACE;
+    maxsim::ChamferArgs a{};
+    a.P = P;
+    a.Q = Q;
+    a.Bt = Bt;
+    a.N = N;
+    a.M = M;
+    a.idx_p = const_cast<int32_t*>(idx_p);
+    a.idx_q = const_cast<int32_t*>(idx_q);
+    a.grad_p = grad_p;
+    a.grad_q = grad_q;
+    a.dP = dP;
+    a.dQ = dQ;
+    a.row_ptr_p = row_ptr_p;
+    a.col_idx_p = col_idx_p;
+    a.row_ptr_q = row_ptr_q;
+    a.col_idx_q = col_idx_q;
+    a.workspace = workspace;
+    return hip_status(maxsim::launch_chamfer_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 int maxsim_fwd_pairs(const void* Q, const void* D_packed, const int32_t* cu_seqlens, int32_t dtype,
                      const int32_t* pair_q, const int32_t* pair_b, int32_t P, int32_t Nq, int32_t Lq,
                      int32_t B, int64_t T, int32_t d, float* scores, int32_t* argmax, void* stream) {

@@ -1,0 +1,463 @@
+// chamfer.hip -- Chamfer distance on gfx950 (MI355X): the MaxSim machinery
+// with a minimum of squared Euclidean distances in place of the maximum of
+// inner products (Flash-MaxSim Section 4.2, "Generalization to Chamfer
+// Distance").  Forward: for every point of one cloud, the nearest point of
+// the other and its index, without the [N, M] distance matrix.  Backward:
+// the saved indices inverted into CSR maps (a stable sort of the
+// destinations), then one owner per gradient row.
+//
+// Forward layout.  A 3-float point is too small for the matrix cores, and
+// the expanded form |a|^2 + |b|^2 - 2<a, b> loses the small distances that
+// decide a nearest neighbour to cancellation, so the distance is formed
+// directly on the vector ALU: 3 subtractions, 1 multiply and 2 fused
+// multiply-adds, then a compare and two selects.  Each lane keeps kPts
+// source points in registers; the target points are uniform across the
+// wave and arrive by scalar loads, so one load feeds 64 x kPts distances.
+// The targets of a batch item are split into chunks over workgroups when
+// there are too few source tiles to fill the chip; the chunks' minima are
+// merged in ascending chunk order.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "internal.h"
+
+namespace maxsim {
+namespace {
+
+constexpr int kPts = 8;            // source points per lane
+constexpr int kNnThreads = 256;    // 4 waves
+constexpr int kSrcTile = kNnThreads * kPts;
+constexpr int kTgtStep = 16;       // targets per scalar-load step
+constexpr int kMinChunk = 512;     // targets per chunk, at least
+
+struct NnParams {
+    const float* A;  // [Bt, Na, 3] sources
+    const float* B;  // [Bt, Nb, 3] targets
+    int Bt, Na, Nb;
+    int tiles;       // source tiles per batch item
+    int chunks;      // target chunks per batch item
+    int chunk_len;   // targets per chunk
+    float* dist;     // [Bt, Na]  (chunks == 1)
+    int32_t* idx;
+    float* part_d;   // [chunks][Bt * Na]  (chunks > 1)
+    int32_t* part_i;
+};
+
+// grid: Bt * tiles * chunks workgroups; chunk-major inside a batch item so
+// that the workgroups sharing a target chunk are launched together.
+__global__ __launch_bounds__(kNnThreads) void nn_kernel(NnParams p) {
+    const int per_item = p.tiles * p.chunks;
+    const int b = blockIdx.x / per_item;
+    const int rem = blockIdx.x - b * per_item;
+    const int c = rem / p.tiles;
+    const int tile = rem - c * p.tiles;
+    const int s0 = tile * kSrcTile + threadIdx.x;  // this lane's first source; then +kNnThreads
+    const float* __restrict__ A = p.A + (int64_t)b * p.Na * 3;
+    const float* __restrict__ T = p.B + (int64_t)b * p.Nb * 3;
+    float ax[kPts], ay[kPts], az[kPts], best[kPts];
+    int arg[kPts];
+#pragma unroll
+    for (int r = 0; r < kPts; ++r) {
+        const int s = min(s0 + r * kNnThreads, p.Na - 1);  // a lane past the end repeats a valid point
+        ax[r] = A[(int64_t)s * 3 + 0];
+        ay[r] = A[(int64_t)s * 3 + 1];
+        az[r] = A[(int64_t)s * 3 + 2];
+        best[r] = __builtin_inff();
+        arg[r] = -1;
+    }
+    const int t_lo = c * p.chunk_len;
+    const int t_hi = min(p.Nb, t_lo + p.chunk_len);
+    int t = t_lo;
+    // full steps: 16 targets (48 floats) by scalar loads, in ascending order
+    for (; t + kTgtStep <= t_hi; t += kTgtStep) {
+        float tx[kTgtStep], ty[kTgtStep], tz[kTgtStep];
+        const float* q = T + (int64_t)t * 3;
+#pragma unroll
+        for (int k = 0; k < kTgtStep; ++k) {
+            tx[k] = q[3 * k];
+            ty[k] = q[3 * k + 1];
+            tz[k] = q[3 * k + 2];
+        }
+#pragma unroll
+        for (int k = 0; k < kTgtStep; ++k) {
+#pragma unroll
+            for (int r = 0; r < kPts; ++r) {
+                const float dx = ax[r] - tx[k];
+                const float dy = ay[r] - ty[k];
+                const float dz = az[r] - tz[k];
+                const float d = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
+                if (d < best[r]) {
+                    best[r] = d;
+                    arg[r] = t + k;
+                }
+            }
+        }
+    }
+    for (; t < t_hi; ++t) {  // the chunk's ragged end
+        const float tx = T[(int64_t)t * 3], ty = T[(int64_t)t * 3 + 1], tz = T[(int64_t)t * 3 + 2];
+#pragma unroll
+        for (int r = 0; r < kPts; ++r) {
+            const float dx = ax[r] - tx;
+            const float dy = ay[r] - ty;
+            const float dz = az[r] - tz;
+            const float d = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
+            if (d < best[r]) {
+                best[r] = d;
+                arg[r] = t;
+            }
+        }
+    }
+    const int64_t base = (int64_t)b * p.Na;
+    float* od = p.chunks > 1 ? p.part_d + (int64_t)c * p.Bt * p.Na : p.dist;
+    int32_t* oi = p.chunks > 1 ? p.part_i + (int64_t)c * p.Bt * p.Na : p.idx;
+#pragma unroll
+    for (int r = 0; r < kPts; ++r) {
+        const int s = s0 + r * kNnThreads;
+        if (s < p.Na) {
+            od[base + s] = best[r];
+            oi[base + s] = arg[r];
+        }
+    }
+}
+
+// Merge of the chunks' minima in ascending chunk order; a strict compare
+// keeps the first index among equal distances.
+__global__ __launch_bounds__(256) void nn_merge(NnParams p) {
+    const int64_t n = (int64_t)p.Bt * p.Na;
+    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (int64_t)gridDim.x * blockDim.x) {
+        float best = p.part_d[s];
+        int arg = p.part_i[s];
+        for (int c = 1; c < p.chunks; ++c) {
+            const float d = p.part_d[(int64_t)c * n + s];
+            if (d < best) {
+                best = d;
+                arg = p.part_i[(int64_t)c * n + s];
+            }
+        }
+        p.dist[s] = best;
+        p.idx[s] = arg;
+    }
+}
+
+// an empty target cloud: +inf and -1 for every source point
+__global__ __launch_bounds__(256) void nn_empty(float* dist, int32_t* idx, int64_t n) {
+    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (int64_t)gridDim.x * blockDim.x) {
+        dist[s] = __builtin_inff();
+        idx[s] = -1;
+    }
+}
+
+void nn_plan(int Bt, int Na, int Nb, int* tiles, int* chunks, int* chunk_len) {
+    *tiles = (Na + kSrcTile - 1) / kSrcTile;
+    const int64_t blocks = (int64_t)Bt * *tiles;
+    int c = (int)std::min<int64_t>((1024 + blocks - 1) / blocks, (Nb + kMinChunk - 1) / kMinChunk);
+    if (c < 1) c = 1;
+    int len = (Nb + c - 1) / c;
+    len = (len + kTgtStep - 1) / kTgtStep * kTgtStep;  // whole scalar-load steps except at the very end
+    *chunks = (Nb + len - 1) / len;
+    if (*chunks < 1) *chunks = 1;
+    *chunk_len = len;
+}
+
+size_t nn_part_bytes(int Bt, int Na, int Nb) {
+    if (Bt < 1 || Na < 1 || Nb < 1) return 0;
+    int tiles, chunks, len;
+    nn_plan(Bt, Na, Nb, &tiles, &chunks, &len);
+    return chunks > 1 ? (size_t)chunks * Bt * Na * 8 : 0;
+}
+
+hipError_t launch_nn(const float* A, const float* B, int Bt, int Na, int Nb, float* dist, int32_t* idx, void* ws,
+                     hipStream_t stream) {
+    if (Bt == 0 || Na == 0) return hipSuccess;
+    if (Nb == 0) {
+        const int64_t n = (int64_t)Bt * Na;
+        hipLaunchKernelGGL(nn_empty, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
+                           stream, dist, idx, n);
+        return hipGetLastError();
+    }
+    NnParams p{};
+    p.A = A;
+    p.B = B;
+    p.Bt = Bt;
+    p.Na = Na;
+    p.Nb = Nb;
+    nn_plan(Bt, Na, Nb, &p.tiles, &p.chunks, &p.chunk_len);
+    p.dist = dist;
+    p.idx = idx;
+    const int64_t n = (int64_t)Bt * Na;
+    p.part_d = static_cast<float*>(ws);
+    p.part_i = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + (size_t)p.chunks * n * 4);
+    hipLaunchKernelGGL(nn_kernel, dim3((unsigned)((int64_t)Bt * p.tiles * p.chunks)), dim3(kNnThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.chunks == 1) return e;
+    hipLaunchKernelGGL(nn_merge, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 8192)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Backward.  Source s (a point of one cloud, global index b*Na + i) selects
+// destination b*Nb + idx[s] of the other cloud.  The CSR map of a direction
+// is a stable sort of the sources by destination: an LSD radix sort, 8 bits
+// per pass, of (destination, source) pairs, in a fixed order, so the map is
+// the same on every run.  Unselected sources (idx = -1) get the key nd (one
+// past the last destination) and sort to the end.  row_ptr[r] is then the
+// lower bound of r in the sorted keys.
+// ---------------------------------------------------------------------------
+constexpr int kSortThreads = 256;
+constexpr int kSortItems = 8;  // per thread per pass
+constexpr int kSortTile = kSortThreads * kSortItems;
+
+__global__ __launch_bounds__(256) void sort_init(const int32_t* idx, int Na, int Nb, int64_t n, int64_t nd,
+                                                 uint32_t* key, int32_t* val) {
+    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t t = idx[s];
+        const int64_t b = s / Na;
+        key[s] = (t < 0 || t >= Nb) ? (uint32_t)nd : (uint32_t)(b * Nb + t);
+        val[s] = (int32_t)s;
+    }
+}
+
+// per tile: histogram of the pass's digit -> hist[digit * ntiles + tile]
+__global__ __launch_bounds__(kSortThreads) void sort_hist(const uint32_t* key, int64_t n, int shift, int ntiles,
+                                                          int32_t* hist) {
+    __shared__ int h[256];
+    h[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t e0 = (int64_t)blockIdx.x * kSortTile;
+#pragma unroll
+    for (int k = 0; k < kSortItems; ++k) {
+        const int64_t e = e0 + k * kSortThreads + threadIdx.x;
+        if (e < n) atomicAdd(&h[(key[e] >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    hist[(int64_t)threadIdx.x * ntiles + blockIdx.x] = h[threadIdx.x];
+}
+
+// exclusive scan of hist [256 * ntiles] in place (one workgroup, in order)
+__global__ __launch_bounds__(1024) void sort_scan(int32_t* hist, int64_t len) {
+    __shared__ int wsum[16];
+    __shared__ int carry_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    for (int64_t i0 = 0; i0 < len; i0 += 1024) {
+        const int64_t i = i0 + tid;
+        const int v = i < len ? hist[i] : 0;
+        int x = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        int wpre = 0;
+        for (int w = 0; w < wave; ++w) wpre += wsum[w];
+        const int carry = carry_s;
+        if (i < len) hist[i] = carry + wpre + x - v;
+        __syncthreads();
+        if (tid == 1023) carry_s = carry + wpre + x;
+        __syncthreads();
+    }
+}
+
+// Stable scatter: a tile's elements are placed in ascending element order.
+// Per round of 256 elements (one per thread, thread order = element order):
+// a lane's rank among the lanes of its wave with the same digit comes from
+// eight ballots; the waves before it add their counts of that digit; the
+// earlier rounds of the tile add theirs (running[]).
+__global__ __launch_bounds__(kSortThreads) void sort_scatter(const uint32_t* key, const int32_t* val, int64_t n,
+                                                             int shift, int ntiles, const int32_t* offs,
+                                                             uint32_t* key_out, int32_t* val_out) {
+    __shared__ int running[256];
+    __shared__ int wcount[kSortThreads / 64][256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    running[tid] = offs[(int64_t)tid * ntiles + blockIdx.x];
+    const int64_t e0 = (int64_t)blockIdx.x * kSortTile;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int k = 0; k < kSortItems; ++k) {
+#pragma unroll
+        for (int w = 0; w < kSortThreads / 64; ++w) wcount[w][tid] = 0;
+        __syncthreads();  // also orders running[] after the previous round's update
+        const int64_t e = e0 + k * kSortThreads + tid;
+        const bool valid = e < n;
+        const uint32_t kv = valid ? key[e] : 0u;
+        const int dg = (int)((kv >> shift) & 255u);
+        unsigned long long m = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const unsigned long long vote = __ballot((dg >> bit) & 1);
+            m &= ((dg >> bit) & 1) ? vote : ~vote;
+        }
+        const int rank = __popcll(m & below);
+        if (valid && rank == 0) wcount[wave][dg] = __popcll(m);
+        __syncthreads();
+        if (valid) {
+            int pre = running[dg];
+            for (int w = 0; w < wave; ++w) pre += wcount[w][dg];
+            key_out[pre + rank] = kv;
+            val_out[pre + rank] = val[e];
+        }
+        __syncthreads();
+        int add = 0;
+#pragma unroll
+        for (int w = 0; w < kSortThreads / 64; ++w) add += wcount[w][tid];
+        running[tid] += add;
+    }
+}
+
+// row_ptr[r] = first position of a key >= r in the sorted keys, r = 0 .. nd
+__global__ __launch_bounds__(256) void csr_bounds(const uint32_t* key, int64_t n, int64_t nd, int32_t* row_ptr) {
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r <= nd; r += (int64_t)gridDim.x * blockDim.x) {
+        int64_t lo = 0, hi = n;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (key[mid] < (uint32_t)r) lo = mid + 1; else hi = mid;
+        }
+        row_ptr[r] = (int32_t)lo;
+    }
+}
+
+// Destination-owned gradient rows.  Row r of cloud X (b*Nx + i) owns
+//   2 gx[r] (X[r] - Y[b, idx_x[r]])  +  sum over its CSR sources s of 2 gy[s] (X[r] - Y[s]).
+// 16 lanes per row: lane l sums the row's sources l, l+16, ... in ascending
+// order, the lanes are added by a fixed butterfly, then the row's own term.
+__global__ __launch_bounds__(256) void chamfer_rows(const float* X, const float* Y, const int32_t* idx_x,
+                                                    const float* gx, const float* gy, const int32_t* row_ptr,
+                                                    const int32_t* col_idx, int Nx, int Ny, int64_t nrows,
+                                                    float* dX) {
+    const int l16 = threadIdx.x & 15;
+    const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+    const bool ok = r < nrows;
+    const int64_t rr = ok ? r : 0;
+    const float x0 = X[rr * 3], x1 = X[rr * 3 + 1], x2 = X[rr * 3 + 2];
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+    if (ok) {
+        const int beg = row_ptr[rr], end = row_ptr[rr + 1];
+        for (int e = beg + l16; e < end; e += 16) {
+            const int64_t s = col_idx[e];
+            const float w = 2.0f * gy[s];
+            a0 = __builtin_fmaf(w, x0 - Y[s * 3], a0);
+            a1 = __builtin_fmaf(w, x1 - Y[s * 3 + 1], a1);
+            a2 = __builtin_fmaf(w, x2 - Y[s * 3 + 2], a2);
+        }
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+        a0 += __shfl_xor(a0, off, 16);
+        a1 += __shfl_xor(a1, off, 16);
+        a2 += __shfl_xor(a2, off, 16);
+    }
+    if (ok && l16 == 0) {
+        const int32_t t = idx_x[rr];
+        if (t >= 0 && t < Ny) {
+            const int64_t b = rr / Nx;
+            const float* y = Y + (b * Ny + t) * 3;
+            const float w = 2.0f * gx[rr];
+            a0 = __builtin_fmaf(w, x0 - y[0], a0);
+            a1 = __builtin_fmaf(w, x1 - y[1], a1);
+            a2 = __builtin_fmaf(w, x2 - y[2], a2);
+        }
+        dX[rr * 3] = a0;
+        dX[rr * 3 + 1] = a1;
+        dX[rr * 3 + 2] = a2;
+    }
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// workspace of one sort of n elements: keys and values twice, the histogram
+size_t sort_bytes(int64_t n) {
+    const int64_t ntiles = (n + kSortTile - 1) / kSortTile;
+    return 2 * align256((size_t)n * 4) + 2 * align256((size_t)n * 4) + align256((size_t)ntiles * 256 * 4);
+}
+
+int key_bits(int64_t nd) {
+    int bits = 1;
+    while (bits < 32 && ((int64_t)1 << bits) <= nd) ++bits;  // keys take values 0 .. nd
+    return bits;
+}
+
+// CSR of the selection idx [Bt, Na] into Bt*Nb destinations
+hipError_t build_csr(const int32_t* idx, int Bt, int Na, int Nb, int32_t* row_ptr, int32_t* col_idx, void* ws,
+                     hipStream_t stream) {
+    const int64_t n = (int64_t)Bt * Na, nd = (int64_t)Bt * Nb;
+    hipError_t e;
+    if (n == 0) {
+        hipLaunchKernelGGL(csr_bounds, dim3((unsigned)std::min<int64_t>((nd + 256) / 256, 4096)), dim3(256), 0,
+                           stream, static_cast<const uint32_t*>(nullptr), (int64_t)0, nd, row_ptr);
+        return hipGetLastError();
+    }
+    char* w = static_cast<char*>(ws);
+    uint32_t* k0 = reinterpret_cast<uint32_t*>(w);
+    uint32_t* k1 = reinterpret_cast<uint32_t*>(w + align256((size_t)n * 4));
+    int32_t* v0 = reinterpret_cast<int32_t*>(w + 2 * align256((size_t)n * 4));
+    int32_t* v1 = reinterpret_cast<int32_t*>(w + 3 * align256((size_t)n * 4));
+    int32_t* hist = reinterpret_cast<int32_t*>(w + 4 * align256((size_t)n * 4));
+    const int ntiles = (int)((n + kSortTile - 1) / kSortTile);
+    const unsigned gb = (unsigned)std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(sort_init, dim3(gb), dim3(256), 0, stream, idx, Na, Nb, n, nd, k0, v0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int passes = (key_bits(nd) + 7) / 8;
+    for (int ps = 0; ps < passes; ++ps) {
+        // the last pass writes the values straight into col_idx
+        int32_t* vout = ps == passes - 1 ? col_idx : v1;
+        hipLaunchKernelGGL(sort_hist, dim3(ntiles), dim3(kSortThreads), 0, stream, k0, n, 8 * ps, ntiles, hist);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(sort_scan, dim3(1), dim3(1024), 0, stream, hist, (int64_t)ntiles * 256);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(sort_scatter, dim3(ntiles), dim3(kSortThreads), 0, stream, k0, v0, n, 8 * ps, ntiles,
+                           hist, k1, vout);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        std::swap(k0, k1);
+        std::swap(v0, v1);
+    }
+    hipLaunchKernelGGL(csr_bounds, dim3((unsigned)std::min<int64_t>((nd + 256) / 256, 4096)), dim3(256), 0, stream,
+                       k0, n, nd, row_ptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_rows(const float* X, const float* Y, const int32_t* idx_x, const float* gx, const float* gy,
+                       const int32_t* row_ptr, const int32_t* col_idx, int Bt, int Nx, int Ny, float* dX,
+                       hipStream_t stream) {
+    const int64_t nrows = (int64_t)Bt * Nx;
+    if (nrows == 0) return hipSuccess;
+    hipLaunchKernelGGL(chamfer_rows, dim3((unsigned)((nrows * 16 + 255) / 256)), dim3(256), 0, stream, X, Y, idx_x,
+                       gx, gy, row_ptr, col_idx, Nx, Ny, nrows, dX);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t chamfer_fwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M) {
+    return std::max<size_t>(256, std::max(nn_part_bytes(Bt, N, M), nn_part_bytes(Bt, M, N)));
+}
+
+hipError_t launch_chamfer_fwd(const ChamferArgs& a, hipStream_t stream) {
+    // the two directions share the workspace: stream order keeps them apart
+    hipError_t e = launch_nn(a.P, a.Q, a.Bt, a.N, a.M, a.dist_p, a.idx_p, a.workspace, stream);
+    if (e != hipSuccess) return e;
+    return launch_nn(a.Q, a.P, a.Bt, a.M, a.N, a.dist_q, a.idx_q, a.workspace, stream);
+}
+
+}  // namespace maxsim
+
+namespace maxsim {
+
+size_t chamfer_bwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M) {
+    return std::max<size_t>(256, std::max(sort_bytes((int64_t)Bt * N), sort_bytes((int64_t)Bt * M)));
+}
+
+hipError_t launch_chamfer_bwd(const ChamferArgs& a, hipStream_t stream) {
+    // destinations P: the Q points' selections; destinations Q: the P points'
+    hipError_t e = build_csr(a.idx_q, a.Bt, a.M, a.N, a.row_ptr_p, a.col_idx_p, a.workspace, stream);
+    if (e != hipSuccess) return e;
+    e = build_csr(a.idx_p, a.Bt, a.N, a.M, a.row_ptr_q, a.col_idx_q, a.workspace, stream);
+    if (e != hipSuccess) return e;
+    e = launch_rows(a.P, a.Q, a.idx_p, a.grad_p, a.grad_q, a.row_ptr_p, a.col_idx_p, a.Bt, a.N, a.M, a.dP, stream);
+    if (e != hipSuccess) return e;
+    return launch_rows(a.Q, a.P, a.idx_q, a.grad_q, a.grad_p, a.row_ptr_q, a.col_idx_q, a.Bt, a.M, a.N, a.dQ, stream);
+}
+
+}  // namespace maxsim

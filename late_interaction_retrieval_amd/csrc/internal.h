@@ -60,6 +60,30 @@ struct HostStreamArgs {
 size_t host_stream_staging_bytes(int32_t Nq, int32_t Lq, int32_t Ld, int32_t block_docs, bool with_argmax);
 hipError_t launch_fwd_host_stream(const HostStreamArgs& a, hipStream_t stream);
 
+// Chamfer distance between batched point clouds P [Bt, N, 3] and Q [Bt, M, 3] (fp32).
+struct ChamferArgs {
+    const float* P;
+    const float* Q;
+    int32_t Bt, N, M;
+    float* dist_p;       // [Bt, N]  squared distance to the nearest point of Q
+    int32_t* idx_p;      // [Bt, N]  its index
+    float* dist_q;       // [Bt, M]
+    int32_t* idx_q;      // [Bt, M]
+    const float* grad_p; // [Bt, N]  backward: upstream gradient of dist_p
+    const float* grad_q; // [Bt, M]
+    float* dP;           // [Bt, N, 3]
+    float* dQ;           // [Bt, M, 3]
+    int32_t* row_ptr_p;  // [Bt*N + 1]  the Q points selecting each P point
+    int32_t* col_idx_p;  // [Bt*M]
+    int32_t* row_ptr_q;  // [Bt*M + 1]  the P points selecting each Q point
+    int32_t* col_idx_q;  // [Bt*N]
+    void* workspace;
+};
+size_t chamfer_fwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M);
+hipError_t launch_chamfer_fwd(const ChamferArgs& a, hipStream_t stream);
+size_t chamfer_bwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M);
+hipError_t launch_chamfer_bwd(const ChamferArgs& a, hipStream_t stream);
+
 struct BwdArgs {
     const void* Q;            // [Nq, Lq, 128]
     const void* D;            // [B, Ld, 128]

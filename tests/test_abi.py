@@ -48,7 +48,9 @@ def test_every_declared_symbol_is_exported_with_binding_arity():
                          "maxsim_two_stage_workspace_bytes", "maxsim_two_stage_topk",
                          "maxsim_bwd_varlen_workspace_bytes", "maxsim_bwd_varlen", "maxsim_bwd_scatter",
                          "maxsim_bwd_prefer_scatter", "maxsim_bwd_scatter_workspace_bytes",
-                         "maxsim_fwd_host_stream_staging_bytes", "maxsim_fwd_host_stream"}
+                         "maxsim_fwd_host_stream_staging_bytes", "maxsim_fwd_host_stream",
+                         "maxsim_chamfer_fwd_workspace_bytes", "maxsim_chamfer_fwd",
+                         "maxsim_chamfer_bwd_workspace_bytes", "maxsim_chamfer_bwd"}
     raw = ctypes.CDLL(LIB)
     for name, nargs in decl.items():
         assert hasattr(raw, name), name
@@ -338,3 +340,41 @@ def test_host_stream_validation():
     assert host_stream(B=0) == bd.MAXSIM_OK
     # an empty packed corpus may pass no host rows; this still needs staging
     assert host_stream(cuh=cu_empty, cu=A, B=3, D=None, stb=0) == bd.MAXSIM_ERR_WORKSPACE
+
+
+def test_chamfer_validation():
+    big = 1 << 40
+    fwd = lambda **kw: L.maxsim_chamfer_fwd(*[kw.get(k, v) for k, v in (
+        ("P", A), ("Q", A), ("Bt", 2), ("N", 10), ("M", 20), ("dp", A), ("ip", A), ("dq", A), ("iq", A),
+        ("ws", A), ("wsb", big), ("stream", None))])
+    assert fwd(Bt=-1) == bd.MAXSIM_ERR_SHAPE
+    assert fwd(Bt=1 << 16, N=1 << 15) == bd.MAXSIM_ERR_SHAPE
+    assert fwd(P=None) == bd.MAXSIM_ERR_NULL
+    assert fwd(iq=None) == bd.MAXSIM_ERR_NULL
+    assert fwd(ws=None) == bd.MAXSIM_ERR_NULL
+    assert fwd(P=M) == bd.MAXSIM_ERR_ALIGN
+    assert fwd(ws=ctypes.c_void_p(0x10010)) == bd.MAXSIM_ERR_ALIGN
+    assert fwd(wsb=0, N=100000, M=100000, Bt=1) == bd.MAXSIM_ERR_WORKSPACE
+    assert fwd(Bt=0) == bd.MAXSIM_OK
+    assert fwd(N=0, M=0) == bd.MAXSIM_OK
+    bwd_ = lambda **kw: L.maxsim_chamfer_bwd(*[kw.get(k, v) for k, v in (
+        ("P", A), ("Q", A), ("ip", A), ("iq", A), ("gp", A), ("gq", A), ("Bt", 2), ("N", 10), ("M", 20),
+        ("dP", A), ("dQ", A), ("rpp", A), ("cip", A), ("rpq", A), ("ciq", A), ("ws", A), ("wsb", big),
+        ("stream", None))])
+    assert bwd_(N=-1) == bd.MAXSIM_ERR_SHAPE
+    assert bwd_(gq=None) == bd.MAXSIM_ERR_NULL
+    assert bwd_(rpq=None) == bd.MAXSIM_ERR_NULL
+    assert bwd_(cip=None) == bd.MAXSIM_ERR_NULL
+    assert bwd_(dP=M) == bd.MAXSIM_ERR_ALIGN
+    assert bwd_(wsb=0) == bd.MAXSIM_ERR_WORKSPACE
+    assert bwd_(Bt=0) == bd.MAXSIM_OK
+
+
+def test_chamfer_workspace_bytes():
+    # forward: chunk minima (fp32 + int32) when the targets are split; 100K x 100K splits into 21 chunks
+    assert L.maxsim_chamfer_fwd_workspace_bytes(1, 100000, 100000) == 21 * 100000 * 8
+    assert L.maxsim_chamfer_fwd_workspace_bytes(1, 10, 20) == 256  # one chunk: no partials
+    assert L.maxsim_chamfer_fwd_workspace_bytes(-1, 10, 20) == 0
+    # backward: keys and values twice plus 256 counters per 2048-element tile, for the larger cloud
+    n = 3000
+    assert L.maxsim_chamfer_bwd_workspace_bytes(1, 10, n) == 4 * ((n * 4 + 255) // 256 * 256) + 2 * 256 * 4
