@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="colbert_rerank_varlen",
                     choices=["colbert_rerank_varlen", "colbert_tiny", "colpali_fwd", "contrastive_train",
-                             "int8_varlen", "two_stage_topk", "ooc_colpali"])
+                             "int8_varlen", "two_stage_topk", "ooc_colpali", "chamfer_100k", "chamfer_batch"])
     ap.add_argument("--argmax", choices=["auto", "on", "off"], default="auto",
                     help="save the argmax in inference workloads (auto: as the workload specifies)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -130,6 +130,41 @@ def sustained_peak(el, seconds=0.04):
     return lib.maxsim_probe_ops_per_launch(kind, blocks, iters) / t / 1e12
 
 
+def valu_issue_rate(seconds=0.04):
+    """Plain fp32 vector-ALU lane-instructions per second this GPU issues
+    (libmaxsim_probe.so: 8 independent v_fmac chains per thread, 512
+    workgroups of 8 waves)."""
+    import ctypes
+    import torch
+    from late_interaction_retrieval_amd import build
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    lib.maxsim_probe_valu_lane_ops_per_launch.restype = ctypes.c_double
+    lib.maxsim_probe_valu_lane_ops_per_launch.argtypes = [ctypes.c_int32] * 2
+    lib.maxsim_probe_valu.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    blocks = 512
+    ops = torch.from_numpy(np.random.default_rng(7).uniform(0.5, 1.0, 1024).astype(np.float32)).to("cuda:0")
+    ops[512:] *= -0.5  # x -> x*a + b with |a| < 1 stays bounded
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def run(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = lib.maxsim_probe_valu(ctypes.c_void_p(ops.data_ptr()), blocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                   ctypes.c_void_p(stream.cuda_stream))
+        assert rc == 0, "probe launch failed (%d)" % rc
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+    t = run(200)
+    iters = int(max(200, min(2000000, 200 * seconds / max(t, 1e-6))))
+    run(iters)
+    t = run(iters)
+    return lib.maxsim_probe_valu_lane_ops_per_launch(blocks, iters) / t
+
+
 def inputs_bf16_bits(x):
     from late_interaction_retrieval_amd import inputs
     return inputs.f32_to_bf16_bits(x)
@@ -175,7 +210,9 @@ def main():
     if args.mfma_ceiling:
         out = {el: round(sustained_peak(el, 0.1), 1) for el in ("f16", "bf16", "i8")}
         print(json.dumps({"sustained_mfma_random_operands": out, "unit": "TFLOP/s (TOP/s for i8)",
-                          "published_dense_peak": {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0}}), flush=True)
+                          "published_dense_peak": {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0},
+                          "valu_fp32_lane_instr_per_s": round(valu_issue_rate(0.1), 1),
+                          "valu_lane_instr_per_s_at_2p4ghz": VALU_LANE_OPS}), flush=True)
         return
 
     import torch
@@ -188,6 +225,9 @@ def main():
         return
     if args.workload == "ooc_colpali":
         bench_ooc(args)
+        return
+    if args.workload.startswith("chamfer"):
+        bench_chamfer(args)
         return
 
     lib_path = os.path.join(ROOT, "late_interaction_retrieval_amd", "libmaxsim.so")
@@ -488,6 +528,110 @@ def bwd_dispatch_sweep(reps=20):
                           "rule_picks": "scatter" if bd.maxsim_bwd_prefer_scatter(Nq, Lq, B, B * Ld) else "csr"}),
               flush=True)
         del Q, D, A, g, dQ, dD, rp, ci, ws
+
+
+# Vector ALU issue rate of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# lane-instructions per second (packed fp32 instructions are not used).
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+CHAMFER_VALU_PER_PAIR = 9  # 3 sub, 1 mul, 2 fma, 1 compare, 2 select (inner loop of nn_kernel)
+CHAMFER_FLOP_PER_PAIR = 8  # 3 sub, 3 mul, 2 add
+
+
+def bench_chamfer(args):
+    """Chamfer distance (a next step beyond the hot path): forward (nearest
+    neighbours both ways, saved indices) and backward (two CSR maps and the
+    gradient rows) of the page's loss on two noisy unit-sphere clouds.  A step
+    is one forward + backward.  The forward is bound by the vector ALU: the
+    roofline counts its inner-loop VALU instructions per point pair against
+    the chip's issue rate."""
+    import torch
+    from late_interaction_retrieval_amd import binding as bd
+    from late_interaction_retrieval_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = inputs.make_chamfer(args.workload)
+    Bt, N, M = w["Bt"], w["N"], w["M"]
+    P = torch.from_numpy(w["P"]).to(dev)
+    Q = torch.from_numpy(w["Q"]).to(dev)
+    gp = torch.full((Bt, N), 1.0 / N, dtype=torch.float32, device=dev)
+    gq = torch.full((Bt, M), 1.0 / M, dtype=torch.float32, device=dev)
+    wsf = torch.empty(max(256, bd.lib().maxsim_chamfer_fwd_workspace_bytes(Bt, N, M)), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(256, bd.lib().maxsim_chamfer_bwd_workspace_bytes(Bt, N, M)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    pool = []
+
+    def step(timed):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
+        if timed:
+            ev[0].record(stream)
+        dp, ip, dq, iq = bd.maxsim_chamfer_fwd(P, Q, workspace=wsf)
+        if timed:
+            ev[1].record(stream)
+        bd.maxsim_chamfer_bwd(P, Q, ip, iq, gp, gq, workspace=wsb)
+        if timed:
+            ev[2].record(stream)
+            pool.append(ev)
+
+    steps = args.steps if args.steps is not None else (20 if N >= 50000 else 200)
+    warmup = args.warmup if args.warmup is not None else 3
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    peak_mem = torch.cuda.max_memory_allocated(dev)
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pool]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in pool]))
+    pairs = 2.0 * Bt * N * M  # both directions
+    flops = CHAMFER_FLOP_PER_PAIR * pairs
+    valu = CHAMFER_VALU_PER_PAIR * pairs / (fwd_ms * 1e-3)
+    achieved = flops / (fwd_ms * 1e-3) / 1e12
+    roofline = {"bound": "alu", "achieved": round(achieved, 2), "peak": 157.3, "unit": "TFLOP/s",
+                "frac": round(achieved / 157.3, 4), "traffic": None,
+                "kernel": "nn_kernel (both directions, with the chunk merge)", "kernel_avg_ms": round(fwd_ms, 4),
+                "flop_per_pair": CHAMFER_FLOP_PER_PAIR, "valu_instr_per_pair": CHAMFER_VALU_PER_PAIR,
+                "valu_lane_instr_per_s_implied": round(valu, 1),
+                "valu_lane_instr_per_s_at_2p4ghz": VALU_LANE_OPS,
+                "peak_note": "published fp32 vector peak (it counts packed fp32 instructions, which this build "
+                             "does not emit)",
+                "bwd_ms": round(bwd_ms, 4)}
+    if not args.no_sustained:
+        vr = valu_issue_rate()
+        roofline["valu_fma_probe_lane_instr_per_s"] = round(vr, 1)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = 64
+        while True:
+            t1 = time.perf_counter()
+            oracle.chamfer_nn(w["P"][:, :n], w["Q"])
+            tc = time.perf_counter() - t1
+            if tc > 0.5 * args.cpu_seconds or n >= N:
+                break
+            n = int(min(N, n * max(2.0, 0.8 * args.cpu_seconds / max(tc, 1e-3))))
+        cpu = {"value": round(CHAMFER_FLOP_PER_PAIR * Bt * n * M / tc / 1e12, 6), "unit": "TFLOP/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "nearest neighbours of the first %d points of P in all of Q (per item), %.1f s" % (n, tc),
+               "pairs_per_s": round(Bt * n * M / tc, 1)}
+    out = {
+        "metric": METRIC, "value": round(flops * steps / elapsed / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(elapsed * 1e3 / steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded noisy samples of the unit sphere, sigma 0.01)",
+        "config": {"workload": args.workload, "Bt": Bt, "N": N, "M": M, "loss": "mean dist_p + mean dist_q"},
+        "point_pairs_per_s": round(pairs * steps / elapsed, 1),
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "peak_mem_bytes": int(peak_mem),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
 
 
 PCIE5_X16_GBS = 64.0  # PCIe 5.0 x16, one direction, published (32 GT/s x 16 lanes, 128b/130b)

@@ -1,6 +1,6 @@
 /*
  * maxsim_probe.h -- a measurement aid shipped beside libmaxsim.so, in its own
- * library (libmaxsim_probe.so).  It is not part of the MaxSim operation: it
+ * library (libmaxsim_probe.so); it also measures the vector-ALU issue rate.  It is not part of the MaxSim operation: it
  * measures the matrix-core rate this GPU sustains for the instructions the
  * MaxSim kernels use (v_mfma_f32_32x32x16_{f16,bf16}, v_mfma_i32_16x16x64_i8),
  * on operand data the caller supplies.  The data matters: with random
@@ -37,6 +37,17 @@ double maxsim_probe_ops_per_launch(int32_t kind, int32_t blocks, int32_t iters);
  * Returns 0, or 1 (NULL pointer), 2 (blocks or iters < 1), 3 (unknown kind),
  * 6 (launch failed). */
 int maxsim_probe_mfma(int32_t kind, const void* operands, int32_t blocks, int32_t iters, float* sink, void* stream);
+
+/* Vector-ALU lane-instructions one maxsim_probe_valu launch issues. */
+double maxsim_probe_valu_lane_ops_per_launch(int32_t blocks, int32_t iters);
+
+/* Launch `blocks` workgroups of 512 threads; each thread runs 8 independent
+ * chains of fp32 fused multiply-adds (v_fmac_f32, one lane-instruction each)
+ * for iters x 8 steps, on values read from `operands` (1024 floats), and
+ * writes one float per thread to `sink` (blocks x 512 floats): the rate the
+ * vector ALU issues plain (not packed) fp32 instructions.
+ * Returns 0, or 1 (NULL pointer), 2 (blocks or iters < 1), 6 (launch failed). */
+int maxsim_probe_valu(const float* operands, int32_t blocks, int32_t iters, float* sink, void* stream);
 
 #ifdef __cplusplus
 }

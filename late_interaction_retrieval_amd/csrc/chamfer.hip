@@ -29,7 +29,7 @@ constexpr int kPts = 8;            // source points per lane
 constexpr int kNnThreads = 256;    // 4 waves
 constexpr int kSrcTile = kNnThreads * kPts;
 constexpr int kTgtStep = 16;       // targets per scalar-load step
-constexpr int kMinChunk = 512;     // targets per chunk, at least
+constexpr int kMinChunk = 128;     // targets per chunk, at least
 
 struct NnParams {
     const float* A;  // [Bt, Na, 3] sources
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void nn_empty(float* dist, int32_t* idx, int64
 void nn_plan(int Bt, int Na, int Nb, int* tiles, int* chunks, int* chunk_len) {
     *tiles = (Na + kSrcTile - 1) / kSrcTile;
     const int64_t blocks = (int64_t)Bt * *tiles;
-    int c = (int)std::min<int64_t>((1024 + blocks - 1) / blocks, (Nb + kMinChunk - 1) / kMinChunk);
+    int c = (int)std::min<int64_t>((2048 + blocks - 1) / blocks, (Nb + kMinChunk - 1) / kMinChunk);
     if (c < 1) c = 1;
     int len = (Nb + c - 1) / c;
     len = (len + kTgtStep - 1) / kTgtStep * kTgtStep;  // whole scalar-load steps except at the very end

@@ -1,4 +1,5 @@
-// probe.hip -- sustained MFMA rate on this GPU with given operand data.
+// probe.hip -- sustained MFMA rate on this GPU with given operand data, and
+// the vector-ALU issue rate.
 //
 // A measurement aid, not part of MaxSim: every wave of every workgroup runs
 // four independent accumulation chains of the same MFMA instruction the
@@ -66,9 +67,43 @@ __global__ __launch_bounds__(kThreads) void mfma_loop(const u32x4* ops, float* s
     sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = out;
 }
 
+// Vector-ALU issue rate: every thread runs kValuChains independent chains of
+// fp32 fused multiply-adds (one v_fmac_f32 each, no packed instructions).
+constexpr int kValuChains = 8;
+
+__global__ __launch_bounds__(kThreads) void valu_loop(const float* ops, float* sink, int iters) {
+    const size_t t = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    const float a = ops[t & 1023], b = ops[(t + 512) & 1023];
+    float x[kValuChains];
+#pragma unroll
+    for (int c = 0; c < kValuChains; ++c) x[c] = ops[(t + 64 * c) & 1023];
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+            for (int c = 0; c < kValuChains; ++c) x[c] = __builtin_fmaf(x[c], a, b);
+    float out = 0.f;
+#pragma unroll
+    for (int c = 0; c < kValuChains; ++c) out += x[c];
+    sink[t] = out;
+}
+
 }  // namespace
 
 extern "C" {
+
+double maxsim_probe_valu_lane_ops_per_launch(int32_t blocks, int32_t iters) {
+    if (blocks < 1 || iters < 1) return 0.0;
+    return (double)blocks * kThreads * iters * kSteps * kValuChains;
+}
+
+int maxsim_probe_valu(const float* operands, int32_t blocks, int32_t iters, float* sink, void* stream) {
+    if (!operands || !sink) return 1;
+    if (blocks < 1 || iters < 1) return 2;
+    hipLaunchKernelGGL(valu_loop, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), operands, sink,
+                       iters);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
 
 size_t maxsim_probe_operand_bytes(int32_t blocks) {
     if (blocks < 1) return 0;

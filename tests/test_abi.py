@@ -169,7 +169,8 @@ def test_probe_library_exports_and_validation():
         build.build()
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = set(re.findall(r"\b(maxsim_probe_\w+)\s*\(", text))
-    assert names == {"maxsim_probe_operand_bytes", "maxsim_probe_ops_per_launch", "maxsim_probe_mfma"}
+    assert names == {"maxsim_probe_operand_bytes", "maxsim_probe_ops_per_launch", "maxsim_probe_mfma",
+                     "maxsim_probe_valu_lane_ops_per_launch", "maxsim_probe_valu"}
     pl = ctypes.CDLL(PROBE_LIB)
     for n in names:
         assert hasattr(pl, n), n
@@ -186,6 +187,13 @@ def test_probe_library_exports_and_validation():
     assert pl.maxsim_probe_mfma(0, A, 0, 1, A, None) == 2
     assert pl.maxsim_probe_mfma(0, A, 1, 0, A, None) == 2
     assert pl.maxsim_probe_mfma(7, A, 1, 1, A, None) == 3
+    pl.maxsim_probe_valu_lane_ops_per_launch.restype = ctypes.c_double
+    pl.maxsim_probe_valu_lane_ops_per_launch.argtypes = [ctypes.c_int32] * 2
+    assert pl.maxsim_probe_valu_lane_ops_per_launch(2, 3) == 2 * 512 * 3 * 8 * 8
+    pl.maxsim_probe_valu.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    assert pl.maxsim_probe_valu(None, 1, 1, A, None) == 1
+    assert pl.maxsim_probe_valu(A, 0, 1, A, None) == 2
 
 
 def test_pairs_topk_two_stage_validation():
@@ -371,8 +379,8 @@ def test_chamfer_validation():
 
 
 def test_chamfer_workspace_bytes():
-    # forward: chunk minima (fp32 + int32) when the targets are split; 100K x 100K splits into 21 chunks
-    assert L.maxsim_chamfer_fwd_workspace_bytes(1, 100000, 100000) == 21 * 100000 * 8
+    # forward: chunk minima (fp32 + int32) when the targets are split; 100K x 100K splits into 42 chunks
+    assert L.maxsim_chamfer_fwd_workspace_bytes(1, 100000, 100000) == 42 * 100000 * 8
     assert L.maxsim_chamfer_fwd_workspace_bytes(1, 10, 20) == 256  # one chunk: no partials
     assert L.maxsim_chamfer_fwd_workspace_bytes(-1, 10, 20) == 0
     # backward: keys and values twice plus 256 counters per 2048-element tile, for the larger cloud
