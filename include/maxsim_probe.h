@@ -49,6 +49,13 @@ double maxsim_probe_valu_lane_ops_per_launch(int32_t blocks, int32_t iters);
  * Returns 0, or 1 (NULL pointer), 2 (blocks or iters < 1), 6 (launch failed). */
 int maxsim_probe_valu(const float* operands, int32_t blocks, int32_t iters, float* sink, void* stream);
 
+/* Plain streaming read of `bytes` (a multiple of 16, >= 16) of device memory
+ * at `buf` by `blocks` workgroups of 256 threads, 16 bytes per load, grid-
+ * stride; every thread writes one word to `sink` (blocks x 256 words): the
+ * HBM read rate a simple kernel of the same size reaches.
+ * Returns 0, or 1 (NULL pointer), 2 (bad blocks or bytes), 6 (launch failed). */
+int maxsim_probe_read(const void* buf, size_t bytes, int32_t blocks, unsigned* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

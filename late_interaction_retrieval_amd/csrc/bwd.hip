@@ -126,10 +126,23 @@ __global__ __launch_bounds__(1024) void csr_docbase(BwdParams p) {
     }
 }
 
+// Workgroup k of the count and fill grids runs on XCD k % 8; all of document
+// b's query groups go to XCD b % 8 (the XCD csr_scan's workgroup b runs on),
+// so its counts and its part of col_idx are written through one L2, where the
+// short scattered writes of the fill combine into whole lines.  The grid has
+// 8 * ceil(B / 8) * NG workgroups; those past the last document do nothing.
+__device__ __forceinline__ bool doc_group(const BwdParams& p, int& b, int& qg) {
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int d = j / p.NG;
+    qg = j - d * p.NG;
+    b = d * 8 + x;
+    return b < p.B;
+}
+
 __global__ __launch_bounds__(1024) void csr_count(BwdParams p) {
     extern __shared__ int hist[];  // [Ld]
-    const int qg = blockIdx.x % p.NG;
-    const int b = blockIdx.x / p.NG;
+    int b, qg;
+    if (!doc_group(p, b, qg)) return;  // uniform
     const int nt = blockDim.x;
     for (int t = threadIdx.x; t < p.Ld; t += nt) hist[t] = 0;
     __syncthreads();
@@ -219,8 +232,8 @@ constexpr int kFillIt = kMaxLq / 64;
 
 __global__ __launch_bounds__(1024) void csr_fill(BwdParams p) {
     extern __shared__ int lds[];
-    const int qg = blockIdx.x % p.NG;
-    const int b = blockIdx.x / p.NG;
+    int b, qg;
+    if (!doc_group(p, b, qg)) return;  // uniform
     const int tid = threadIdx.x, nt = blockDim.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int Ld = p.Ld;
@@ -664,7 +677,7 @@ hipError_t launch_dq(BwdParams p, hipStream_t stream) {
 template <int ELEM, bool VARLEN>
 hipError_t launch_bwd_elem(const BwdParams& p, hipStream_t stream) {
     const int nthr = 64 * p.G;
-    const unsigned groups = (unsigned)((int64_t)p.B * p.NG);
+    const unsigned groups = (unsigned)(8 * (((int64_t)p.B + 7) / 8) * p.NG);
     hipError_t e;
     if (VARLEN) {
         hipLaunchKernelGGL(csr_docbase, dim3(1), dim3(1024), 0, stream, p);

@@ -878,45 +878,83 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
 // `qrows`, 256 bytes apart) against one document (first row st, len tokens).
 // The work per document token is tiny, so this is bound by reading D: each
 // wave takes SPL 16-token sub-tiles per round and loads them straight from
-// HBM into MFMA operand registers (no LDS staging, no barrier until the end),
-// all of a round's loads in flight at once.  Lane group g reads 16
-// contiguous bytes at chunk s*4 + g of its row in k-step s, so one load
-// instruction covers 64 contiguous bytes of 16 rows.  The argmax is exact
-// (first index on ties).  On return, lanes r < nr of wave 0 hold row r's
-// maximum and argmax (other waves' values are unspecified); every wave must
-// call it (it contains a workgroup barrier).
+// HBM into MFMA operand registers (no LDS staging of D), all of a round's
+// loads in flight at once.  Lane group g reads 16 contiguous bytes at chunk
+// s*4 + g of its row in k-step s, so one load instruction covers 64
+// contiguous bytes of 16 rows.  The query rows are read once per workgroup
+// into LDS (q_s, 32 rows x 16 chunks, XOR-swizzled by row) and every wave
+// takes its MFMA fragments from there: reading them from global memory in
+// every wave makes the few cache lines of Q a hot spot that delays the
+// document stream.  The first round's document loads are issued before the
+// Q barrier.  The argmax is exact (first index on ties).  On return, lanes
+// r < nr of wave 0 hold row r's maximum and argmax (other waves' values are
+// unspecified); every wave must call it (it contains workgroup barriers).
 template <int ELEM, int W, int SPL>
 __device__ __forceinline__ void rows_vs_doc(const FwdParams& p, const char* qrows, int nr, int64_t st, int len,
-                                            float (*rowmax_s)[32], int (*rowarg_s)[32], float& mv, int& idx) {
+                                            u32x4* q_s, float (*rowmax_s)[32], int (*rowarg_s)[32], float& mv,
+                                            int& idx) {
     using MM = Mma<ELEM, 16>;
     using Acc = typename MM::Acc;
     constexpr int M = 16, NG = MM::NG, KS = MM::KS, VPL = MM::VPL, ROWB = 256;
+    constexpr int QCH = 32 * 16 / (64 * W);  // query chunks each thread stages
+    static_assert(QCH * 64 * W == 32 * 16, "query staging");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane / M, lm = lane % M;
+    u32x4 qv[QCH];
+#pragma unroll
+    for (int k = 0; k < QCH; ++k) {
+        const int e = tid + k * 64 * W;
+        const int r = e >> 4, c = e & 15;
+        qv[k] = r < nr ? *reinterpret_cast<const u32x4*>(qrows + (int64_t)r * ROWB + c * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const int nsub = (len + M - 1) / M;
+    // rows past the document read its first row; an empty document (which
+    // may have no rows at all) reads the query rows instead
+    const char* fallback = len > 0 ? p.D + st * ROWB : qrows;
+    auto load_round = [&](int base, u32x4 (&a)[SPL][KS]) {
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            const int tok = (base + j) * M + lm;
+            const char* src = tok < len ? p.D + (st + tok) * ROWB : fallback;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) a[j][s2] = *reinterpret_cast<const u32x4*>(src + (s2 * NG + g) * 16);
+        }
+    };
+    // Keep every load of a round in flight together: without this the
+    // compiler sinks each sub-tile's loads into the branch that uses them and
+    // the round becomes a chain of dependent memory round trips.  (The empty
+    // asm reads the registers, so it also waits for the loads.)
+    auto pin_round = [&](u32x4 (&a)[SPL][KS]) {
+#pragma unroll
+        for (int j = 0; j < SPL; ++j)
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) asm volatile("" : "+v"(a[j][s2]));
+    };
+    u32x4 a[SPL][KS];
+    load_round(wave * SPL, a);  // every wave, so the Q write below waits for the Q loads only
+#pragma unroll
+    for (int k = 0; k < QCH; ++k) {
+        const int e = tid + k * 64 * W;
+        const int r = e >> 4, c = e & 15;
+        q_s[r * 16 + (c ^ (r & 15))] = qv[k];
+    }
+    __syncthreads();
     u32x4 bq[2][KS];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
         const int r = cb * M + lm;
 #pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2)
-            bq[cb][s2] = r < nr ? *reinterpret_cast<const u32x4*>(qrows + (int64_t)r * ROWB + (s2 * NG + g) * 16)
-                                : u32x4{0u, 0u, 0u, 0u};
+        for (int s2 = 0; s2 < KS; ++s2) bq[cb][s2] = q_s[r * 16 + ((s2 * NG + g) ^ (r & 15))];
     }
+    pin_round(a);  // the first round was issued before the Q barrier
     float m[2] = {-INFINITY, -INFINITY};
     int best[2] = {-1, -1};  // token index of the maximum (first on ties)
-    const int nsub = (len + M - 1) / M;
-    const int64_t safe = len > 0 ? st : 0;
     for (int base = wave * SPL; base < nsub; base += W * SPL) {  // uniform
-        u32x4 a[SPL][KS];
-#pragma unroll
-        for (int j = 0; j < SPL; ++j) {
-            const int tok = (base + j) * M + lm;
-            const int64_t row = tok < len ? st + tok : safe;
-#pragma unroll
-            for (int s2 = 0; s2 < KS; ++s2)
-                a[j][s2] = *reinterpret_cast<const u32x4*>(p.D + row * ROWB + (s2 * NG + g) * 16);
+        if (base != wave * SPL) {  // later rounds of a long document
+            load_round(base, a);
+            pin_round(a);
         }
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
@@ -970,7 +1008,7 @@ __device__ __forceinline__ void rows_vs_doc(const FwdParams& p, const char* qrow
             }
         }
     }
-    __syncthreads();  // the LDS rows may be reused by the caller
+    __syncthreads();  // the LDS rows (and q_s) may be reused by the caller
 }
 
 // Few query rows in all (Nq * Lq <= 32, e.g. one ColBERT query): one
@@ -978,6 +1016,7 @@ __device__ __forceinline__ void rows_vs_doc(const FwdParams& p, const char* qrow
 // argmax and the per-query sums.
 template <int ELEM, int W, int SPL, bool ARGMAX, bool VARLEN>
 __global__ __launch_bounds__(64 * W) void fwd_tiny_kernel(FwdParams p) {
+    __shared__ u32x4 q_s[32 * 16];
     __shared__ float rowmax_s[W][32];
     __shared__ int rowarg_s[W][32];
     const int b = blockIdx.x;
@@ -989,7 +1028,7 @@ __global__ __launch_bounds__(64 * W) void fwd_tiny_kernel(FwdParams p) {
     const int nrows = p.Nq * p.Lq;  // <= 32
     float mv;
     int idx;
-    rows_vs_doc<ELEM, W, SPL>(p, p.Q, nrows, st, len, rowmax_s, rowarg_s, mv, idx);
+    rows_vs_doc<ELEM, W, SPL>(p, p.Q, nrows, st, len, q_s, rowmax_s, rowarg_s, mv, idx);
     if (wave != 0) return;
     if (lane < nrows) rowmax_s[0][lane] = mv;  // only this wave reads it from here on
     __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): the row maxima are in LDS
@@ -999,9 +1038,14 @@ __global__ __launch_bounds__(64 * W) void fwd_tiny_kernel(FwdParams p) {
         const int q = lane / Lq, i = lane - q * Lq;
         if (ARGMAX) p.argmax[((int64_t)q * p.B + b) * Lq + i] = idx;
     }
-    if (lane < p.Nq) {  // query lane: its Lq row maxima in ascending order
+    if (lane < p.Nq) {  // query lane: its Lq (<= 32) row maxima in ascending order
+        float v[32];  // all loads issued before the first add
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = i < Lq ? rowmax_s[0][lane * Lq + i] : 0.f;
         float acc = 0.f;
-        for (int i = 0; i < Lq; ++i) acc += rowmax_s[0][lane * Lq + i];
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            if (i < Lq) acc += v[i];
         p.scores[(int64_t)lane * p.B + b] = acc;
     }
 }
@@ -1012,6 +1056,7 @@ __global__ __launch_bounds__(64 * W) void fwd_tiny_kernel(FwdParams p) {
 // scores[p] and argmax[p, Lq] follow the list.
 template <int ELEM, int W, int SPL, bool ARGMAX>
 __global__ __launch_bounds__(64 * W) void fwd_pairs_kernel(FwdParams p, const int32_t* pq, const int32_t* pb) {
+    __shared__ u32x4 q_s[32 * 16];
     __shared__ float rowmax_s[W][32];
     __shared__ int rowarg_s[W][32];
     const int pair = blockIdx.x;
@@ -1030,12 +1075,19 @@ __global__ __launch_bounds__(64 * W) void fwd_pairs_kernel(FwdParams p, const in
         const int nr = Lq - r0 < 32 ? Lq - r0 : 32;
         float mv;
         int idx;
-        rows_vs_doc<ELEM, W, SPL>(p, p.Q + ((int64_t)q * Lq + r0) * 256, nr, st, len, rowmax_s, rowarg_s, mv, idx);
+        rows_vs_doc<ELEM, W, SPL>(p, p.Q + ((int64_t)q * Lq + r0) * 256, nr, st, len, q_s, rowmax_s, rowarg_s, mv,
+                                  idx);
         if (wave == 0) {
             if (ARGMAX && lane < nr) p.argmax[(int64_t)pair * Lq + r0 + lane] = idx;
-            // rows of the block in ascending order: lane 0 gathers them
+            // rows of the block in ascending order: every lane gathers them
+            // (all shuffles issued before the first add)
+            float v[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) v[i] = __shfl(mv, i);
             float part = 0.f;
-            for (int i = 0; i < nr; ++i) part += __shfl(mv, i);
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                if (i < nr) part += v[i];
             total += part;
         }
     }

@@ -88,9 +88,28 @@ __global__ __launch_bounds__(kThreads) void valu_loop(const float* ops, float* s
     sink[t] = out;
 }
 
+// Plain streaming read: every thread reads 16-byte chunks t, t + nthreads, ...
+// of the buffer and writes the XOR of what it read to `sink` (so no load is
+// dropped).
+__global__ __launch_bounds__(256) void read_loop(const u32x4* buf, long long n16, unsigned* sink) {
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long stride = (long long)gridDim.x * 256;
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    for (long long k = t; k < n16; k += stride) x ^= buf[k];
+    sink[t] = x[0] ^ x[1] ^ x[2] ^ x[3];
+}
+
 }  // namespace
 
 extern "C" {
+
+int maxsim_probe_read(const void* buf, size_t bytes, int32_t blocks, unsigned* sink, void* stream) {
+    if (!buf || !sink) return 1;
+    if (blocks < 1 || bytes < 16 || (bytes & 15)) return 2;
+    hipLaunchKernelGGL(read_loop, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4*>(buf), (long long)(bytes / 16), sink);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
 
 double maxsim_probe_valu_lane_ops_per_launch(int32_t blocks, int32_t iters) {
     if (blocks < 1 || iters < 1) return 0.0;

@@ -170,7 +170,7 @@ def test_probe_library_exports_and_validation():
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = set(re.findall(r"\b(maxsim_probe_\w+)\s*\(", text))
     assert names == {"maxsim_probe_operand_bytes", "maxsim_probe_ops_per_launch", "maxsim_probe_mfma",
-                     "maxsim_probe_valu_lane_ops_per_launch", "maxsim_probe_valu"}
+                     "maxsim_probe_valu_lane_ops_per_launch", "maxsim_probe_valu", "maxsim_probe_read"}
     pl = ctypes.CDLL(PROBE_LIB)
     for n in names:
         assert hasattr(pl, n), n
@@ -194,6 +194,11 @@ def test_probe_library_exports_and_validation():
                                      ctypes.c_void_p]
     assert pl.maxsim_probe_valu(None, 1, 1, A, None) == 1
     assert pl.maxsim_probe_valu(A, 0, 1, A, None) == 2
+    pl.maxsim_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    assert pl.maxsim_probe_read(None, 1024, 1, A, None) == 1
+    assert pl.maxsim_probe_read(A, 1000, 1, A, None) == 2
+    assert pl.maxsim_probe_read(A, 1024, 0, A, None) == 2
 
 
 def test_pairs_topk_two_stage_validation():
