@@ -10,6 +10,8 @@ seeded synthetic input already resident in HBM:
       fp16 -> scores [64, 10000] (maxsim_fwd_varlen);
   colbert_tiny:  1 query x 1,000 documents of 180 tokens, fp16, scores+argmax;
   colpali_fwd:   4 queries x 10,000 documents, Lq = Ld = 1024, bf16, scores+argmax;
+  contrastive_train_varlen: the same step over 64 packed documents of
+      256..1024 tokens (cu_seqlens forward and packed backward);
   contrastive_train: 64 x 64 in-batch pairs, Lq = Ld = 1024, bf16: forward
       with argmax, InfoNCE gradient (tau = 0.02), backward (CSR, dD, dQ);
   int8_varlen:   32 queries x 32 tokens against 100,000 int8 documents,
@@ -49,6 +51,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="colbert_rerank_varlen",
                     choices=["colbert_rerank_varlen", "colbert_tiny", "colpali_fwd", "contrastive_train",
+                             "contrastive_train_varlen",
                              "int8_varlen", "two_stage_topk", "ooc_colpali", "chamfer_100k", "chamfer_batch"])
     ap.add_argument("--argmax", choices=["auto", "on", "off"], default="auto",
                     help="save the argmax in inference workloads (auto: as the workload specifies)")
@@ -245,7 +248,7 @@ def main():
     Nq, Lq, B, d, T = w["Nq"], w["Lq"], w["B"], w["d"], w["T"]
     dtn = w["dtype"]
     want_argmax = {"colbert_rerank_varlen": False, "colbert_tiny": True, "colpali_fwd": True,
-                   "contrastive_train": True, "int8_varlen": False}[name]
+                   "contrastive_train": True, "int8_varlen": False, "contrastive_train_varlen": True}[name]
     if args.argmax != "auto":
         want_argmax = args.argmax == "on"
 
@@ -308,6 +311,36 @@ def main():
                 e2b = torch.cuda.Event(enable_timing=True)
                 e2b.record(stream)
             bd.maxsim_bwd(Q, Dd, amax, g, dQ=dQ, dD=dD, row_ptr=rp, col_idx=ci, workspace=ws)
+            if timed:
+                e2.record(stream)
+                ev_pool.append((e0, e1, e2b, e2))
+
+        bwd_flops = 4.0 * d * Nq * B * Lq
+        step_flops = fwd_flops + bwd_flops
+    elif name == "contrastive_train_varlen":
+        Dd = Ds[0]
+        ws = torch.empty(max(256, bd.maxsim_bwd_varlen_workspace_bytes(Nq, B, Lq, max_ld)), dtype=torch.uint8,
+                         device=dev)
+        dQ = torch.empty((Nq, Lq, d), dtype=torch.float32, device=dev)
+        dD = torch.empty((T, d), dtype=torch.float32, device=dev)
+        rp = torch.empty(T + 1, dtype=torch.int32, device=dev)
+        ci = torch.empty(Nq * B * Lq, dtype=torch.int32, device=dev)
+        tau = w["tau"]
+        eye = torch.eye(Nq, device=dev, dtype=torch.float32)
+
+        def step(i, timed):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3)) if timed else (None,) * 3
+            if timed:
+                e0.record(stream)
+            bd.maxsim_fwd_varlen(Q, Dd, cu, max_ld, scores=scores, argmax=amax)
+            if timed:
+                e1.record(stream)
+            p = torch.softmax(scores / tau, dim=1)
+            g = ((p - eye) / (tau * Nq)).contiguous()
+            if timed:
+                e2b = torch.cuda.Event(enable_timing=True)
+                e2b.record(stream)
+            bd.maxsim_bwd_varlen(Q, Dd, cu, max_ld, amax, g, dQ=dQ, dD=dD, row_ptr=rp, col_idx=ci, workspace=ws)
             if timed:
                 e2.record(stream)
                 ev_pool.append((e0, e1, e2b, e2))
@@ -438,11 +471,11 @@ def main():
                      "mfma_frac": round(achieved / peak, 4), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4)})
     if bwd_ms:
         b_avg = float(np.mean(bwd_ms))
-        Ld = w["Ld_max"]
+        rows = T if name == "contrastive_train_varlen" else B * w["Ld_max"]
         # argmax read, Q and D read (bf16), dQ and dD written (fp32), col_idx written
         # and read back, row_ptr, upstream gradient
-        bwd_bytes = (4 * Nq * B * Lq + 2 * d * (Nq * Lq + B * Ld) + 4 * d * (Nq * Lq + B * Ld)
-                     + 2 * 4 * Nq * B * Lq + 4 * (B * Ld + 1) + 4 * Nq * B)
+        bwd_bytes = (4 * Nq * B * Lq + 2 * d * (Nq * Lq + rows) + 4 * d * (Nq * Lq + rows)
+                     + 2 * 4 * Nq * B * Lq + 4 * (rows + 1) + 4 * Nq * B)
         extra["bwd"] = {"avg_ms": round(b_avg, 5), "algorithmic_bytes": bwd_bytes,
                         "hbm_gbs": round(bwd_bytes / (b_avg * 1e-3) / 1e9, 1),
                         "hbm_frac": round(bwd_bytes / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -880,7 +913,7 @@ def cpu_baseline(w, target_s):
                 oracle.fwd_varlen(q, sub, subcu, odt)
         return time.perf_counter() - t0
 
-    nq, n, reps = (1 if w["name"] == "contrastive_train" else Nq), 1, 1
+    nq, n, reps = (1 if w["name"].startswith("contrastive_train") else Nq), 1, 1
     t = run(nq, n, reps)
     while t < 0.5 * target_s:
         scale = max(2.0, min(16.0, 0.8 * target_s / max(t, 1e-6)))

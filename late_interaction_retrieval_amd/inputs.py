@@ -143,6 +143,9 @@ WORKLOADS = {
     "contrastive_train": dict(id=4, Nq=64, Lq=1024, B=64, Ld=(1024, 1024), d=128, dtype=BF16,
                               tau=0.02),
     "int8_varlen": dict(id=5, Nq=32, Lq=32, B=100000, Ld=(32, 512), d=128, dtype=I8),
+    # the training step over a ragged in-batch corpus (packed backward)
+    "contrastive_train_varlen": dict(id=7, Nq=64, Lq=1024, B=64, Ld=(256, 1024), d=128, dtype=BF16,
+                                     tau=0.02),
 }
 
 

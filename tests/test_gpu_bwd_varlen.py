@@ -152,3 +152,19 @@ def test_workload_colbert_rerank_varlen_full(bd):
     g = rng.standard_normal((Nq, B)).astype(np.float32)
     check(bd, w["Q"], w["D_packed"], w["cu_seqlens"], inputs.F16, A, g, "colbert_rerank_varlen",
           max_Ld=w["Ld_max"])
+
+
+def test_workload_contrastive_train_varlen_full(bd):
+    """The ragged training workload at full size (64 x 64 pairs, Lq = 1024,
+    documents of 256..1024 tokens): seeded argmax uniform over each document's
+    rows, an InfoNCE-shaped upstream gradient of seeded scores."""
+    from gpu_util import infonce_grad
+    w = inputs.make("contrastive_train_varlen")
+    Nq, Lq, B = w["Nq"], w["Lq"], w["B"]
+    lens = w["lens"]
+    rng = np.random.default_rng([7, 3])
+    A = (rng.random((Nq, B, Lq)) * lens[None, :, None]).astype(np.int32)
+    fake_scores = rng.standard_normal((Nq, B)) * 0.05 + np.eye(Nq) * 0.1
+    g = infonce_grad(fake_scores, w["tau"]).astype(np.float32)
+    check(bd, w["Q"], w["D_packed"], w["cu_seqlens"], inputs.BF16, A, g, "contrastive_train_varlen",
+          max_Ld=w["Ld_max"])
