@@ -200,21 +200,30 @@ hipError_t launch_nn(const float* A, const float* B, int Bt, int Na, int Nb, flo
 // destination b*Nb + idx[s] of the other cloud.  The CSR map of a direction
 // is a stable sort of the sources by destination: an LSD radix sort, 8 bits
 // per pass, of (destination, source) pairs, in a fixed order, so the map is
-// the same on every run.  Unselected sources (idx = -1) get the key nd (one
-// past the last destination) and sort to the end.  row_ptr[r] is then the
-// lower bound of r in the sorted keys.
+// the same on every run.  Both directions go through one sort: the Q points
+// (selecting P destinations 0 .. Bt*N-1) come first, then the P points
+// (selecting Q destinations, keyed Bt*N + b*M + j).  Unselected sources
+// (idx = -1) get the key nd = Bt*(N+M) and sort to the end.  row_ptr[r] is
+// then the lower bound of r in the sorted keys.
 // ---------------------------------------------------------------------------
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 8;  // per thread per pass
 constexpr int kSortTile = kSortThreads * kSortItems;
 
-__global__ __launch_bounds__(256) void sort_init(const int32_t* idx, int Na, int Nb, int64_t n, int64_t nd,
-                                                 uint32_t* key, int32_t* val) {
-    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (int64_t)gridDim.x * blockDim.x) {
-        const int32_t t = idx[s];
+// elements 0 .. Bt*M-1: the Q points and their P destinations; then the P
+// points and their Q destinations (offset by Bt*N); the value is the
+// source's global index in its own cloud
+__global__ __launch_bounds__(256) void sort_init(const int32_t* idx_q, const int32_t* idx_p, int N, int M,
+                                                 int64_t nq, int64_t n, int64_t ndp, int64_t nd, uint32_t* key,
+                                                 int32_t* val) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+        const bool qside = e < nq;
+        const int64_t s = qside ? e : e - nq;
+        const int32_t t = qside ? idx_q[s] : idx_p[s];
+        const int Na = qside ? M : N, Nb = qside ? N : M;
         const int64_t b = s / Na;
-        key[s] = (t < 0 || t >= Nb) ? (uint32_t)nd : (uint32_t)(b * Nb + t);
-        val[s] = (int32_t)s;
+        key[e] = (t < 0 || t >= Nb) ? (uint32_t)nd : (uint32_t)((qside ? 0 : ndp) + b * Nb + t);
+        val[e] = (int32_t)s;
     }
 }
 
@@ -234,17 +243,24 @@ __global__ __launch_bounds__(kSortThreads) void sort_hist(const uint32_t* key, i
     hist[(int64_t)threadIdx.x * ntiles + blockIdx.x] = h[threadIdx.x];
 }
 
-// exclusive scan of hist [256 * ntiles] in place (one workgroup, in order)
+// exclusive scan of hist [256 * ntiles] in place (one workgroup, in order):
+// each thread takes 16 consecutive entries per round of 16384, so a round
+// costs one memory round trip
 __global__ __launch_bounds__(1024) void sort_scan(int32_t* hist, int64_t len) {
     __shared__ int wsum[16];
     __shared__ int carry_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) carry_s = 0;
     __syncthreads();
-    for (int64_t i0 = 0; i0 < len; i0 += 1024) {
-        const int64_t i = i0 + tid;
-        const int v = i < len ? hist[i] : 0;
-        int x = v;
+    for (int64_t i0 = 0; i0 < len; i0 += 1024 * 16) {
+        const int64_t e0 = i0 + (int64_t)tid * 16;
+        int v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = e0 + k < len ? hist[e0 + k] : 0;
+        int tot = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) tot += v[k];
+        int x = tot;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int y = __shfl_up(x, off);
@@ -255,7 +271,12 @@ __global__ __launch_bounds__(1024) void sort_scan(int32_t* hist, int64_t len) {
         int wpre = 0;
         for (int w = 0; w < wave; ++w) wpre += wsum[w];
         const int carry = carry_s;
-        if (i < len) hist[i] = carry + wpre + x - v;
+        int run = carry + wpre + x - tot;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (e0 + k < len) hist[e0 + k] = run;
+            run += v[k];
+        }
         __syncthreads();
         if (tid == 1023) carry_s = carry + wpre + x;
         __syncthreads();
@@ -307,15 +328,43 @@ __global__ __launch_bounds__(kSortThreads) void sort_scatter(const uint32_t* key
     }
 }
 
-// row_ptr[r] = first position of a key >= r in the sorted keys, r = 0 .. nd
-__global__ __launch_bounds__(256) void csr_bounds(const uint32_t* key, int64_t n, int64_t nd, int32_t* row_ptr) {
-    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r <= nd; r += (int64_t)gridDim.x * blockDim.x) {
-        int64_t lo = 0, hi = n;
-        while (lo < hi) {
-            const int64_t mid = (lo + hi) >> 1;
-            if (key[mid] < (uint32_t)r) lo = mid + 1; else hi = mid;
+__device__ __forceinline__ int64_t lower_bound(const uint32_t* key, int64_t n, int64_t r) {
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (key[mid] < (uint32_t)r) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+// row_ptr_p[r] = lower bound of r (r = 0 .. ndp); row_ptr_q[r] = lower bound
+// of ndp + r minus that of ndp (r = 0 .. nd - ndp), so each map starts at 0
+__global__ __launch_bounds__(256) void csr_bounds(const uint32_t* key, int64_t n, int64_t ndp, int64_t nd,
+                                                  int32_t* row_ptr_p, int32_t* row_ptr_q) {
+    const int64_t base_q = lower_bound(key, n, ndp);
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r <= nd + 1;
+         r += (int64_t)gridDim.x * blockDim.x) {
+        if (r <= ndp) {
+            row_ptr_p[r] = (int32_t)lower_bound(key, n, r);
+        } else {
+            const int64_t rq = r - ndp - 1;  // 0 .. nd - ndp
+            row_ptr_q[rq] = (int32_t)(lower_bound(key, n, ndp + rq) - base_q);
         }
-        row_ptr[r] = (int32_t)lo;
+    }
+}
+
+// sorted values -> col_idx_p (the first row_ptr_p[ndp]) and col_idx_q (the next)
+__global__ __launch_bounds__(256) void csr_split(const int32_t* val, const int32_t* row_ptr_p,
+                                                 const int32_t* row_ptr_q, int64_t ndp, int64_t ndq,
+                                                 int32_t* col_idx_p, int32_t* col_idx_q) {
+    const int64_t np = row_ptr_p[ndp], nq = row_ptr_q[ndq];
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < np + nq;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        if (e < np) {
+            col_idx_p[e] = val[e];
+        } else {
+            col_idx_q[e - np] = val[e];
+        }
     }
 }
 
@@ -323,15 +372,39 @@ __global__ __launch_bounds__(256) void csr_bounds(const uint32_t* key, int64_t n
 //   2 gx[r] (X[r] - Y[b, idx_x[r]])  +  sum over its CSR sources s of 2 gy[s] (X[r] - Y[s]).
 // 16 lanes per row: lane l sums the row's sources l, l+16, ... in ascending
 // order, the lanes are added by a fixed butterfly, then the row's own term.
-__global__ __launch_bounds__(256) void chamfer_rows(const float* X, const float* Y, const int32_t* idx_x,
-                                                    const float* gx, const float* gy, const int32_t* row_ptr,
-                                                    const int32_t* col_idx, int Nx, int Ny, int64_t nrows,
-                                                    float* dX) {
+struct RowSide {
+    const float* X;
+    const float* Y;
+    const int32_t* idx_x;
+    const float* gx;
+    const float* gy;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    int Nx, Ny;
+    int64_t nrows;
+    float* dX;
+};
+
+// rows of P first (side 0), then rows of Q (side 1), in one launch
+__global__ __launch_bounds__(256) void chamfer_rows(RowSide s0, RowSide s1) {
+    const int64_t rg = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+    const bool second = rg >= s0.nrows;  // uniform per 16-lane group
+    const RowSide& sd = second ? s1 : s0;
+    const int64_t r = second ? rg - s0.nrows : rg;
+    const float* X = sd.X;
+    const float* Y = sd.Y;
+    const int32_t* idx_x = sd.idx_x;
+    const float* gx = sd.gx;
+    const float* gy = sd.gy;
+    const int32_t* row_ptr = sd.row_ptr;
+    const int32_t* col_idx = sd.col_idx;
+    const int Nx = sd.Nx, Ny = sd.Ny;
+    float* dX = sd.dX;
     const int l16 = threadIdx.x & 15;
-    const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
-    const bool ok = r < nrows;
+    const bool ok = r < sd.nrows;
     const int64_t rr = ok ? r : 0;
-    const float x0 = X[rr * 3], x1 = X[rr * 3 + 1], x2 = X[rr * 3 + 2];
+    // a group past the last row reads nothing (that cloud may be empty)
+    const float x0 = ok ? X[rr * 3] : 0.f, x1 = ok ? X[rr * 3 + 1] : 0.f, x2 = ok ? X[rr * 3 + 2] : 0.f;
     float a0 = 0.f, a1 = 0.f, a2 = 0.f;
     if (ok) {
         const int beg = row_ptr[rr], end = row_ptr[rr + 1];
@@ -379,52 +452,51 @@ int key_bits(int64_t nd) {
     return bits;
 }
 
-// CSR of the selection idx [Bt, Na] into Bt*Nb destinations
-hipError_t build_csr(const int32_t* idx, int Bt, int Na, int Nb, int32_t* row_ptr, int32_t* col_idx, void* ws,
-                     hipStream_t stream) {
-    const int64_t n = (int64_t)Bt * Na, nd = (int64_t)Bt * Nb;
+// Both CSR maps with one sort (see above).
+hipError_t build_csr_pair(const ChamferArgs& a, hipStream_t stream) {
+    const int64_t nq = (int64_t)a.Bt * a.M, np = (int64_t)a.Bt * a.N;
+    const int64_t n = nq + np, ndp = np, nd = np + nq;
     hipError_t e;
-    if (n == 0) {
-        hipLaunchKernelGGL(csr_bounds, dim3((unsigned)std::min<int64_t>((nd + 256) / 256, 4096)), dim3(256), 0,
-                           stream, static_cast<const uint32_t*>(nullptr), (int64_t)0, nd, row_ptr);
-        return hipGetLastError();
-    }
-    char* w = static_cast<char*>(ws);
+    char* w = static_cast<char*>(a.workspace);
     uint32_t* k0 = reinterpret_cast<uint32_t*>(w);
     uint32_t* k1 = reinterpret_cast<uint32_t*>(w + align256((size_t)n * 4));
     int32_t* v0 = reinterpret_cast<int32_t*>(w + 2 * align256((size_t)n * 4));
     int32_t* v1 = reinterpret_cast<int32_t*>(w + 3 * align256((size_t)n * 4));
     int32_t* hist = reinterpret_cast<int32_t*>(w + 4 * align256((size_t)n * 4));
-    const int ntiles = (int)((n + kSortTile - 1) / kSortTile);
     const unsigned gb = (unsigned)std::min<int64_t>((n + 255) / 256, 4096);
-    hipLaunchKernelGGL(sort_init, dim3(gb), dim3(256), 0, stream, idx, Na, Nb, n, nd, k0, v0);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int passes = (key_bits(nd) + 7) / 8;
-    for (int ps = 0; ps < passes; ++ps) {
-        // the last pass writes the values straight into col_idx
-        int32_t* vout = ps == passes - 1 ? col_idx : v1;
-        hipLaunchKernelGGL(sort_hist, dim3(ntiles), dim3(kSortThreads), 0, stream, k0, n, 8 * ps, ntiles, hist);
+    if (n > 0) {
+        const int ntiles = (int)((n + kSortTile - 1) / kSortTile);
+        hipLaunchKernelGGL(sort_init, dim3(gb), dim3(256), 0, stream, a.idx_q, a.idx_p, a.N, a.M, nq, n, ndp, nd, k0,
+                           v0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(sort_scan, dim3(1), dim3(1024), 0, stream, hist, (int64_t)ntiles * 256);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(sort_scatter, dim3(ntiles), dim3(kSortThreads), 0, stream, k0, v0, n, 8 * ps, ntiles,
-                           hist, k1, vout);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        std::swap(k0, k1);
-        std::swap(v0, v1);
+        const int passes = (key_bits(nd) + 7) / 8;
+        for (int ps = 0; ps < passes; ++ps) {
+            hipLaunchKernelGGL(sort_hist, dim3(ntiles), dim3(kSortThreads), 0, stream, k0, n, 8 * ps, ntiles, hist);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(sort_scan, dim3(1), dim3(1024), 0, stream, hist, (int64_t)ntiles * 256);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(sort_scatter, dim3(ntiles), dim3(kSortThreads), 0, stream, k0, v0, n, 8 * ps, ntiles,
+                               hist, k1, v1);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            std::swap(k0, k1);
+            std::swap(v0, v1);
+        }
     }
-    hipLaunchKernelGGL(csr_bounds, dim3((unsigned)std::min<int64_t>((nd + 256) / 256, 4096)), dim3(256), 0, stream,
-                       k0, n, nd, row_ptr);
+    hipLaunchKernelGGL(csr_bounds, dim3((unsigned)std::min<int64_t>((nd + 2 + 255) / 256, 4096)), dim3(256), 0, stream,
+                       k0, n, ndp, nd, a.row_ptr_p, a.row_ptr_q);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(csr_split, dim3(gb), dim3(256), 0, stream, v0, a.row_ptr_p, a.row_ptr_q, ndp, nd - ndp,
+                       a.col_idx_p, a.col_idx_q);
     return hipGetLastError();
 }
 
-hipError_t launch_rows(const float* X, const float* Y, const int32_t* idx_x, const float* gx, const float* gy,
-                       const int32_t* row_ptr, const int32_t* col_idx, int Bt, int Nx, int Ny, float* dX,
-                       hipStream_t stream) {
-    const int64_t nrows = (int64_t)Bt * Nx;
+hipError_t launch_rows_pair(const ChamferArgs& a, hipStream_t stream) {
+    RowSide sp{a.P, a.Q, a.idx_p, a.grad_p, a.grad_q, a.row_ptr_p, a.col_idx_p, a.N, a.M, (int64_t)a.Bt * a.N, a.dP};
+    RowSide sq{a.Q, a.P, a.idx_q, a.grad_q, a.grad_p, a.row_ptr_q, a.col_idx_q, a.M, a.N, (int64_t)a.Bt * a.M, a.dQ};
+    const int64_t nrows = sp.nrows + sq.nrows;
     if (nrows == 0) return hipSuccess;
-    hipLaunchKernelGGL(chamfer_rows, dim3((unsigned)((nrows * 16 + 255) / 256)), dim3(256), 0, stream, X, Y, idx_x,
-                       gx, gy, row_ptr, col_idx, Nx, Ny, nrows, dX);
+    hipLaunchKernelGGL(chamfer_rows, dim3((unsigned)((nrows * 16 + 255) / 256)), dim3(256), 0, stream, sp, sq);
     return hipGetLastError();
 }
 
@@ -446,18 +518,13 @@ hipError_t launch_chamfer_fwd(const ChamferArgs& a, hipStream_t stream) {
 namespace maxsim {
 
 size_t chamfer_bwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M) {
-    return std::max<size_t>(256, std::max(sort_bytes((int64_t)Bt * N), sort_bytes((int64_t)Bt * M)));
+    return std::max<size_t>(256, sort_bytes((int64_t)Bt * N + (int64_t)Bt * M));
 }
 
 hipError_t launch_chamfer_bwd(const ChamferArgs& a, hipStream_t stream) {
-    // destinations P: the Q points' selections; destinations Q: the P points'
-    hipError_t e = build_csr(a.idx_q, a.Bt, a.M, a.N, a.row_ptr_p, a.col_idx_p, a.workspace, stream);
+    hipError_t e = build_csr_pair(a, stream);
     if (e != hipSuccess) return e;
-    e = build_csr(a.idx_p, a.Bt, a.N, a.M, a.row_ptr_q, a.col_idx_q, a.workspace, stream);
-    if (e != hipSuccess) return e;
-    e = launch_rows(a.P, a.Q, a.idx_p, a.grad_p, a.grad_q, a.row_ptr_p, a.col_idx_p, a.Bt, a.N, a.M, a.dP, stream);
-    if (e != hipSuccess) return e;
-    return launch_rows(a.Q, a.P, a.idx_q, a.grad_q, a.grad_p, a.row_ptr_q, a.col_idx_q, a.Bt, a.M, a.N, a.dQ, stream);
+    return launch_rows_pair(a, stream);
 }
 
 }  // namespace maxsim
