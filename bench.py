@@ -203,7 +203,7 @@ def read_traffic(kernel, workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (one process, one MI355X); --gpus %d is not "
+        print("bench.py: this benchmark measures one GPU only (one process, one MI355X); --gpus %d is not "
               "supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -631,7 +631,7 @@ def bench_chamfer(args):
                 "flop_per_pair": CHAMFER_FLOP_PER_PAIR, "valu_instr_per_pair": CHAMFER_VALU_PER_PAIR,
                 "valu_lane_instr_per_s_implied": round(valu, 1),
                 "valu_lane_instr_per_s_at_2p4ghz": VALU_LANE_OPS,
-                "peak_note": "published fp32 vector peak (it counts packed fp32 instructions, which this build "
+                "peak_note": "published fp32 vector peak (it counts packed fp32 instructions, which this library "
                              "does not emit)",
                 "bwd_ms": round(bwd_ms, 4)}
     if not args.no_sustained:
