@@ -65,6 +65,10 @@ struct BwdParams {
     // and dq_reduce adds the chunks in ascending order
     int dq_split, dq_docs;
     float* dq_part;
+    // dD rows with more than kHeavy sources: dd_owner appends them to this
+    // list (count first) and dd_heavy reduces each with a whole workgroup
+    int32_t* heavy;
+    int64_t max_heavy;
 };
 
 __device__ __forceinline__ int clamp_tok(int t, int Ld) { return t < 0 ? 0 : (t >= Ld ? Ld - 1 : t); }
@@ -173,6 +177,7 @@ __global__ __launch_bounds__(1024) void csr_scan(BwdParams p) {
     int len;
     doc_rows(p, b, rstart, len);
     int32_t* ws = p.ws + (int64_t)b * p.NG * p.Ld;
+    if (b == 0 && tid == 0) p.heavy[0] = 0;  // dd_owner appends heavy rows after this kernel
     if (tid == 0) carry_s = 0;
     __syncthreads();
     for (int t0 = 0; t0 < len; t0 += 1024) {
@@ -338,6 +343,9 @@ constexpr int kGatherBlocks = 512;                  // 2 per CU on 256 CUs
 constexpr int kRowsPerGroup = 4;
 constexpr int kQueryWindow = 16;  // queries per dD step
 constexpr int kDdBatch = 12;      // dD sources gathered per round (loads in flight)
+// A dD row with more sources than this is left to dd_heavy: one 16-lane group
+// walking thousands of sources would hold up the whole grid.
+constexpr int kHeavy = 512;
 
 __device__ __forceinline__ void fma8(float* acc, float g, const float* v) {
 #pragma unroll
@@ -369,6 +377,7 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
     const int BLq = p.B * p.Lq;
     const int nsrc = p.Nq * BLq;  // col_idx capacity
     int cur[kRowsPerGroup], end[kRowsPerGroup], bdoc[kRowsPerGroup];
+    bool heavy[kRowsPerGroup];
     float acc[kRowsPerGroup][8];
 #pragma unroll
     for (int k = 0; k < kRowsPerGroup; ++k) {
@@ -382,6 +391,14 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
             bdoc[k] = 0;
         } else {
             bdoc[k] = ok ? (int)(row / p.Ld) : 0;
+        }
+        heavy[k] = end[k] - cur[k] > kHeavy;  // uniform per group
+        if (heavy[k]) {
+            if (l16 == 0) {
+                const int slot = atomicAdd(&p.heavy[0], 1);
+                if (slot < p.max_heavy) p.heavy[1 + slot] = (int)row;  // bounded by the workspace
+            }
+            cur[k] = end[k];  // this group skips the row
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
@@ -444,7 +461,74 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int k = 0; k < kRowsPerGroup; ++k) {
         const int64_t row = gid + k * ngroups;
-        if (k < rows_per_group && row < nrows) store8(p.dD + row * 128 + l16 * 8, acc[k]);
+        if (k < rows_per_group && row < nrows && !heavy[k]) store8(p.dD + row * 128 + l16 * 8, acc[k]);
+    }
+}
+
+// The heavy rows, one workgroup at a time each: the row's sources are cut
+// into kGatherGroups contiguous chunks, every 16-lane group sums its chunk in
+// ascending order (16 loads in flight), and the chunk sums are added in
+// group order.  The split is fixed by the row's length, so runs are
+// bit-identical.  The source's document comes from the source (s / Lq).
+template <int ELEM>
+__global__ __launch_bounds__(kGatherThreads) void dd_heavy(BwdParams p) {
+    __shared__ float part[kGatherGroups][128];
+    const int l16 = threadIdx.x & 15, grp = threadIdx.x >> 4;
+    const int BLq = p.B * p.Lq;
+    const int nsrc = p.Nq * BLq;
+    const int count = (int)(p.heavy[0] < p.max_heavy ? p.heavy[0] : p.max_heavy);
+    for (int h = blockIdx.x; h < count; h += gridDim.x) {  // uniform
+        const int64_t row = p.heavy[1 + h];
+        int beg = p.row_ptr[row], end = p.row_ptr[row + 1];
+        beg = beg < 0 ? 0 : (beg > nsrc ? nsrc : beg);
+        end = end < beg ? beg : (end > nsrc ? nsrc : end);
+        const int len = end - beg;
+        const int c0 = beg + (int)((int64_t)len * grp / kGatherGroups);
+        const int c1 = beg + (int)((int64_t)len * (grp + 1) / kGatherGroups);
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        for (int e0 = c0; e0 < c1; e0 += 16) {  // uniform per group
+            const int n = min(16, c1 - e0);
+            int qi = 0;
+            float gv = 0.f;
+            if (l16 < n) {
+                const int src = p.col_idx[e0 + l16];
+                int q = (int)(((unsigned long long)(unsigned)src * p.magic) >> (32 + p.shift));
+                const int qb = (int)(((unsigned long long)(unsigned)src * p.magic_lq) >> (32 + p.shift_lq));
+                int b = qb - q * p.B;
+                b = b < 0 ? 0 : (b >= p.B ? p.B - 1 : b);
+                int i = src - q * BLq - b * p.Lq;
+                q = q < 0 ? 0 : (q >= p.Nq ? p.Nq - 1 : q);  // a consistent map never clamps
+                i = i < 0 ? 0 : (i >= p.Lq ? p.Lq - 1 : i);
+                gv = p.g[(int64_t)q * p.B + b];
+                qi = q * p.Lq + i;
+            }
+            u32x4 raw[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int qj = __shfl(qi, j, 16);
+                if (j < n) raw[j] = *reinterpret_cast<const u32x4*>(p.Q + (int64_t)qj * 256 + l16 * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float gj = __shfl(gv, j, 16);
+                if (j < n) {
+                    float v[8];
+                    cvt8<ELEM>(raw[j], v);
+                    fma8(acc, gj, v);
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[grp][l16 * 8 + e] = acc[e];
+        __syncthreads();
+        if (threadIdx.x < 128) {
+            float t = part[0][threadIdx.x];
+            for (int gr = 1; gr < kGatherGroups; ++gr) t += part[gr][threadIdx.x];
+            p.dD[row * 128 + threadIdx.x] = t;
+        }
+        __syncthreads();  // part is reused by the next heavy row
     }
 }
 
@@ -696,6 +780,11 @@ hipError_t launch_bwd_elem(const BwdParams& p, hipStream_t stream) {
         gather_grid(nrows, &blocks, &rpg);
         hipLaunchKernelGGL((dd_owner<ELEM, VARLEN>), dim3(blocks), dim3(kGatherThreads), 0, stream, p, rpg);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        const unsigned hb = (unsigned)std::min<int64_t>(p.max_heavy, kGatherBlocks);
+        if (hb > 0) {
+            hipLaunchKernelGGL((dd_heavy<ELEM>), dim3(hb), dim3(kGatherThreads), 0, stream, p);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
     return launch_dq<ELEM, VARLEN>(p, stream);
 }
@@ -739,8 +828,9 @@ int bwd_group(int32_t Ld) {
 }
 
 // Workspace layout (each part at a 256-byte boundary): the CSR counts
-// [B][NG][Ld] int32, the packed corpus' document bases [B+1] int32, then the
-// dQ chunk partial sums [S][Nq*Lq][128] fp32 when dQ is split (S > 1).
+// [B][NG][Ld] int32, the packed corpus' document bases [B+1] int32, the heavy
+// row list (count, then rows) int32, then the dQ chunk partial sums
+// [S][Nq*Lq][128] fp32 when dQ is split (S > 1).
 namespace {
 size_t counts_bytes(int32_t Nq, int32_t B, int32_t Ld) {
     const int G = bwd_group(Ld);
@@ -748,18 +838,24 @@ size_t counts_bytes(int32_t Nq, int32_t B, int32_t Ld) {
     const int64_t NG = (Nq + G - 1) / G;
     return (size_t)(B * NG * Ld * (int64_t)sizeof(int32_t));
 }
+// a heavy row has more than kHeavy of the Nq*B*Lq sources
+int64_t max_heavy_rows(int32_t Nq, int32_t B, int32_t Lq) { return (int64_t)Nq * B * Lq / (kHeavy + 1); }
+size_t heavy_bytes(int32_t Nq, int32_t B, int32_t Lq) {
+    return align256((size_t)(1 + max_heavy_rows(Nq, B, Lq)) * sizeof(int32_t));
+}
 }  // namespace
 
 size_t bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld) {
     const size_t c = counts_bytes(Nq, B, Ld);
     if (c == 0 || Lq < 1) return 0;
-    return align256(c) + dq_part_bytes(Nq, Lq, B);
+    return align256(c) + heavy_bytes(Nq, B, Lq) + dq_part_bytes(Nq, Lq, B);
 }
 
 size_t bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld) {
     const size_t c = counts_bytes(Nq, B, max_Ld);
     if (c == 0 || Lq < 1) return 0;
-    return align256(c) + align256((size_t)(B + 1) * sizeof(int32_t)) + dq_part_bytes(Nq, Lq, B);
+    return align256(c) + align256((size_t)(B + 1) * sizeof(int32_t)) + heavy_bytes(Nq, B, Lq) +
+           dq_part_bytes(Nq, Lq, B);
 }
 
 size_t bwd_scatter_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq) {
@@ -808,14 +904,19 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     size_t off = align256(counts_bytes(a.Nq, a.B, a.Ld));
     magic_div((unsigned long long)a.B * a.Lq, &p.magic, &p.shift);
     magic_div((unsigned long long)a.Lq, &p.magic_lq, &p.shift_lq);
+    p.max_heavy = max_heavy_rows(a.Nq, a.B, a.Lq);
     if (a.cu_seqlens) {
         p.cu = a.cu_seqlens;
         p.T = a.T;
         p.docbase = reinterpret_cast<int32_t*>(ws + off);
         off += align256((size_t)(a.B + 1) * sizeof(int32_t));
+        p.heavy = reinterpret_cast<int32_t*>(ws + off);
+        off += heavy_bytes(a.Nq, a.B, a.Lq);
         p.dq_part = reinterpret_cast<float*>(ws + off);
         return a.elem == kBF16 ? launch_bwd_elem<kBF16, true>(p, stream) : launch_bwd_elem<kF16, true>(p, stream);
     }
+    p.heavy = reinterpret_cast<int32_t*>(ws + off);
+    off += heavy_bytes(a.Nq, a.B, a.Lq);
     p.dq_part = reinterpret_cast<float*>(ws + off);
     return a.elem == kBF16 ? launch_bwd_elem<kBF16, false>(p, stream) : launch_bwd_elem<kF16, false>(p, stream);
 }

@@ -142,9 +142,11 @@ def test_bwd_validation(kw, code):
 
 
 def test_workspace_bytes():
-    # one int32 count per (document, group of queries, row)
+    # one int32 count per (document, group of queries, row), then the heavy-row list: a count
+    # and room for every row that can hold more than 512 of the 64*64*1024 sources
     n = L.maxsim_bwd_workspace_bytes(64, 64, 1024, 1024)
-    assert n == 64 * 16 * 1024 * 4  # Ld = 1024 -> 4 queries per group -> 16 groups
+    heavy = (1 + 64 * 64 * 1024 // 513) * 4
+    assert n == 64 * 16 * 1024 * 4 + (heavy + 255) // 256 * 256  # Ld = 1024 -> 4 queries per group
     assert L.maxsim_bwd_workspace_bytes(0, 1, 1, 1) == 0
     assert L.maxsim_bwd_workspace_bytes(1, 1, 1, 5000) == 0
     assert bwd(wsb=n - 1, Nq=64, B=64, Lq=1024, Ld=1024) == bd.MAXSIM_ERR_WORKSPACE
@@ -258,13 +260,14 @@ def test_bwd_varlen_validation(kw, code):
 
 
 def test_bwd_varlen_workspace_bytes():
-    # the counts for max_Ld, the per-document first slots, then the dQ chunk sums, each at a
-    # 256-byte boundary.  320 query rows fill 10 gather workgroups, so the 100 documents are
-    # split into min(ceil(512 / 10), 100 // 8) = 12 chunks for dQ.
+    # the counts for max_Ld, the per-document first slots, the heavy-row list (1 + 32000 // 513
+    # entries), then the dQ chunk sums, each at a 256-byte boundary.  320 query rows fill 10
+    # gather workgroups, so the 100 documents are split into min(ceil(512 / 10), 100 // 8) = 12
+    # chunks for dQ.
     counts = 100 * 1 * 100 * 4  # 10 queries form one group of 16 at Ld = 100
     part = 12 * 320 * 128 * 4
-    assert L.maxsim_bwd_workspace_bytes(10, 100, 32, 100) == 40192 + part
-    assert L.maxsim_bwd_varlen_workspace_bytes(10, 100, 32, 100) == 40192 + 512 + part
+    assert L.maxsim_bwd_workspace_bytes(10, 100, 32, 100) == 40192 + 256 + part
+    assert L.maxsim_bwd_varlen_workspace_bytes(10, 100, 32, 100) == 40192 + 512 + 256 + part
     assert counts <= 40192 < counts + 256
     assert L.maxsim_bwd_scatter_workspace_bytes(10, 100, 32) == part
     assert L.maxsim_bwd_scatter_workspace_bytes(10, 7, 32) == 256  # too few documents to split

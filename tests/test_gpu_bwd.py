@@ -126,3 +126,17 @@ def test_workload_contrastive_forward_sampled(bd):
         cu = inputs.cu_seqlens(np.full(len(bs), Ld, np.int32))
         sim = oracle.sim_at(w["Q"][q:q + 1], D[bs].reshape(-1, 128), cu, oracle.BF16, a[q:q + 1, bs])
         check_argmax(a[q:q + 1, bs], a_ref, m_ref, sim, np.full(len(bs), Ld), "train fwd q%d" % q)
+
+
+def test_workload_contrastive_train_hot_rows(bd):
+    """The training shape with half of every document's sources on 8 hot rows
+    (4096 sources each): those rows take the whole-workgroup path."""
+    w = inputs.make("contrastive_train")
+    Nq, Lq, B, Ld = w["Nq"], w["Lq"], w["B"], w["Ld_max"]
+    D = w["D_packed"].reshape(B, Ld, 128)
+    rng = np.random.default_rng([0, 4, 8])
+    A = rng.integers(0, Ld, size=(Nq, B, Lq)).astype(np.int32)
+    hot = rng.random(A.shape) < 0.5
+    A[hot] = rng.integers(0, 8, size=int(hot.sum()))
+    g = rng.standard_normal((Nq, B)).astype(np.float32) * 0.01
+    check_bwd(bd, w["Q"], D, inputs.BF16, A, g, "contrastive_train hot rows")
