@@ -340,7 +340,8 @@ __device__ __forceinline__ int64_t lower_bound(const uint32_t* key, int64_t n, i
 // row_ptr_p[r] = lower bound of r (r = 0 .. ndp); row_ptr_q[r] = lower bound
 // of ndp + r minus that of ndp (r = 0 .. nd - ndp), so each map starts at 0
 __global__ __launch_bounds__(256) void csr_bounds(const uint32_t* key, int64_t n, int64_t ndp, int64_t nd,
-                                                  int32_t* row_ptr_p, int32_t* row_ptr_q) {
+                                                  int32_t* row_ptr_p, int32_t* row_ptr_q, int32_t* heavy) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) heavy[0] = 0;  // chamfer_rows appends after this kernel
     const int64_t base_q = lower_bound(key, n, ndp);
     for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r <= nd + 1;
          r += (int64_t)gridDim.x * blockDim.x) {
@@ -385,8 +386,13 @@ struct RowSide {
     float* dX;
 };
 
-// rows of P first (side 0), then rows of Q (side 1), in one launch
-__global__ __launch_bounds__(256) void chamfer_rows(RowSide s0, RowSide s1) {
+// A row with more sources than this goes to chamfer_heavy (a whole
+// workgroup), so one 16-lane group never walks a huge bucket alone.
+constexpr int kChHeavy = 1024;
+
+// rows of P first (side 0), then rows of Q (side 1), in one launch; heavy
+// rows are appended to heavy[1 ..] (count in heavy[0]) and left out here
+__global__ __launch_bounds__(256) void chamfer_rows(RowSide s0, RowSide s1, int32_t* heavy, int64_t max_heavy) {
     const int64_t rg = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
     const bool second = rg >= s0.nrows;  // uniform per 16-lane group
     const RowSide& sd = second ? s1 : s0;
@@ -406,8 +412,15 @@ __global__ __launch_bounds__(256) void chamfer_rows(RowSide s0, RowSide s1) {
     // a group past the last row reads nothing (that cloud may be empty)
     const float x0 = ok ? X[rr * 3] : 0.f, x1 = ok ? X[rr * 3 + 1] : 0.f, x2 = ok ? X[rr * 3 + 2] : 0.f;
     float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+    const int beg = ok ? row_ptr[rr] : 0, end = ok ? row_ptr[rr + 1] : 0;
+    if (end - beg > kChHeavy) {  // uniform per group
+        if (l16 == 0) {
+            const int slot = atomicAdd(&heavy[0], 1);
+            if (slot < max_heavy) heavy[1 + slot] = (int32_t)rg;
+        }
+        return;
+    }
     if (ok) {
-        const int beg = row_ptr[rr], end = row_ptr[rr + 1];
         for (int e = beg + l16; e < end; e += 16) {
             const int64_t s = col_idx[e];
             const float w = 2.0f * gy[s];
@@ -438,6 +451,61 @@ __global__ __launch_bounds__(256) void chamfer_rows(RowSide s0, RowSide s1) {
     }
 }
 
+// One heavy row per workgroup at a time: thread t sums the row's sources t,
+// t + 256, ... in ascending order, a fixed pairwise tree in LDS adds the
+// threads, then the row's own term.  Runs are bit-identical.
+__global__ __launch_bounds__(256) void chamfer_heavy(RowSide s0, RowSide s1, const int32_t* heavy, int64_t max_heavy) {
+    __shared__ float red[3][256];
+    const int tid = threadIdx.x;
+    const int count = (int)(heavy[0] < max_heavy ? heavy[0] : max_heavy);
+    for (int h = blockIdx.x; h < count; h += gridDim.x) {  // uniform
+        const int64_t rg = heavy[1 + h];
+        const bool second = rg >= s0.nrows;
+        const RowSide& sd = second ? s1 : s0;
+        const int64_t r = second ? rg - s0.nrows : rg;
+        const float x0 = sd.X[r * 3], x1 = sd.X[r * 3 + 1], x2 = sd.X[r * 3 + 2];
+        const int beg = sd.row_ptr[r], end = sd.row_ptr[r + 1];
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+        for (int e = beg + tid; e < end; e += 256) {
+            const int64_t s = sd.col_idx[e];
+            const float w = 2.0f * sd.gy[s];
+            a0 = __builtin_fmaf(w, x0 - sd.Y[s * 3], a0);
+            a1 = __builtin_fmaf(w, x1 - sd.Y[s * 3 + 1], a1);
+            a2 = __builtin_fmaf(w, x2 - sd.Y[s * 3 + 2], a2);
+        }
+        red[0][tid] = a0;
+        red[1][tid] = a1;
+        red[2][tid] = a2;
+        __syncthreads();
+        for (int half = 128; half > 0; half >>= 1) {
+            if (tid < half) {
+                red[0][tid] += red[0][tid + half];
+                red[1][tid] += red[1][tid + half];
+                red[2][tid] += red[2][tid + half];
+            }
+            __syncthreads();
+        }
+        if (tid == 0) {
+            a0 = red[0][0];
+            a1 = red[1][0];
+            a2 = red[2][0];
+            const int32_t t = sd.idx_x[r];
+            if (t >= 0 && t < sd.Ny) {
+                const int64_t b = r / sd.Nx;
+                const float* y = sd.Y + (b * sd.Ny + t) * 3;
+                const float w = 2.0f * sd.gx[r];
+                a0 = __builtin_fmaf(w, x0 - y[0], a0);
+                a1 = __builtin_fmaf(w, x1 - y[1], a1);
+                a2 = __builtin_fmaf(w, x2 - y[2], a2);
+            }
+            sd.dX[r * 3] = a0;
+            sd.dX[r * 3 + 1] = a1;
+            sd.dX[r * 3 + 2] = a2;
+        }
+        __syncthreads();  // red is reused by the next heavy row
+    }
+}
+
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // workspace of one sort of n elements: keys and values twice, the histogram
@@ -450,6 +518,15 @@ int key_bits(int64_t nd) {
     int bits = 1;
     while (bits < 32 && ((int64_t)1 << bits) <= nd) ++bits;  // keys take values 0 .. nd
     return bits;
+}
+
+// the heavy-row list lives after the sort's buffers in the workspace
+int64_t max_heavy_rows(const ChamferArgs& a) {
+    return ((int64_t)a.Bt * a.N + (int64_t)a.Bt * a.M) / (kChHeavy + 1);
+}
+int32_t* heavy_list(const ChamferArgs& a) {
+    return reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) +
+                                      sort_bytes((int64_t)a.Bt * a.N + (int64_t)a.Bt * a.M));
 }
 
 // Both CSR maps with one sort (see above).
@@ -483,7 +560,7 @@ hipError_t build_csr_pair(const ChamferArgs& a, hipStream_t stream) {
         }
     }
     hipLaunchKernelGGL(csr_bounds, dim3((unsigned)std::min<int64_t>((nd + 2 + 255) / 256, 4096)), dim3(256), 0, stream,
-                       k0, n, ndp, nd, a.row_ptr_p, a.row_ptr_q);
+                       k0, n, ndp, nd, a.row_ptr_p, a.row_ptr_q, heavy_list(a));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(csr_split, dim3(gb), dim3(256), 0, stream, v0, a.row_ptr_p, a.row_ptr_q, ndp, nd - ndp,
@@ -496,7 +573,13 @@ hipError_t launch_rows_pair(const ChamferArgs& a, hipStream_t stream) {
     RowSide sq{a.Q, a.P, a.idx_q, a.grad_q, a.grad_p, a.row_ptr_q, a.col_idx_q, a.M, a.N, (int64_t)a.Bt * a.M, a.dQ};
     const int64_t nrows = sp.nrows + sq.nrows;
     if (nrows == 0) return hipSuccess;
-    hipLaunchKernelGGL(chamfer_rows, dim3((unsigned)((nrows * 16 + 255) / 256)), dim3(256), 0, stream, sp, sq);
+    const int64_t mh = max_heavy_rows(a);
+    hipLaunchKernelGGL(chamfer_rows, dim3((unsigned)((nrows * 16 + 255) / 256)), dim3(256), 0, stream, sp, sq,
+                       heavy_list(a), mh);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || mh == 0) return e;
+    hipLaunchKernelGGL(chamfer_heavy, dim3((unsigned)std::min<int64_t>(mh, 1024)), dim3(256), 0, stream, sp, sq,
+                       heavy_list(a), mh);
     return hipGetLastError();
 }
 
@@ -518,7 +601,8 @@ hipError_t launch_chamfer_fwd(const ChamferArgs& a, hipStream_t stream) {
 namespace maxsim {
 
 size_t chamfer_bwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M) {
-    return std::max<size_t>(256, sort_bytes((int64_t)Bt * N + (int64_t)Bt * M));
+    const int64_t n = (int64_t)Bt * N + (int64_t)Bt * M;
+    return sort_bytes(n) + align256((size_t)(1 + n / (kChHeavy + 1)) * sizeof(int32_t));
 }
 
 hipError_t launch_chamfer_bwd(const ChamferArgs& a, hipStream_t stream) {

@@ -134,6 +134,20 @@ def test_backward_hot_destination_and_unselected(bd):
     check_bwd(bd, P, Q, ip, iq, gp, gq, "hot destination")
 
 
+def test_backward_very_hot_destinations(bd):
+    """Buckets of tens of thousands of sources (every Q point selects one of two
+    P points, every P point one of three Q points): the whole-workgroup path."""
+    Bt, N, M = 2, 3000, 40000
+    P, Q = inputs.point_clouds(88, Bt, N, M)
+    rng = np.random.default_rng(88)
+    ip = rng.integers(0, 3, (Bt, N)).astype(np.int32)
+    iq = rng.integers(0, 2, (Bt, M)).astype(np.int32)
+    iq[:, ::5] = rng.integers(0, N, (Bt, len(range(0, M, 5))))
+    gp = rng.standard_normal((Bt, N)).astype(np.float32)
+    gq = rng.standard_normal((Bt, M)).astype(np.float32)
+    check_bwd(bd, P, Q, ip, iq, gp, gq, "very hot destinations")
+
+
 def test_workload_chamfer_100k_sampled(bd):
     """100K-point clouds (the page's largest): the GPU forward on all points,
     the oracle on 1500 sampled points per direction; the backward at full size
