@@ -14,11 +14,10 @@
 //                  rows -> row_ptr and each group's first slot per row.
 //   3. csr_fill  : per (document, query group), one wave per query.  Within a
 //                  query the sources are ranked in ascending i, 64 at a time:
-//                  every lane ORs its bit into a per-row 64-bit mask in LDS,
-//                  reads the mask back and takes popcount(mask & lanes below)
-//                  as its rank.  OR is commutative, so the result is
-//                  deterministic, and the per-query prefix over the group
-//                  makes the whole fill stable.
+//                  one ballot per bit of the row index gives every lane the
+//                  mask of lanes holding its row, and popcount(mask & lanes
+//                  below) is its rank.  The per-query prefix over the group
+//                  makes the whole fill stable and deterministic.
 //   4. dd_owner  : a 16-lane group owns dD rows, walks their sources and
 //                  writes each row once (no atomics).
 //   5. dq_gather : a 16-lane group owns dQ rows and loops over the B
@@ -230,7 +229,7 @@ __global__ __launch_bounds__(1024) void csr_scan(BwdParams p) {
 }
 
 // One wave per query of the group.  Dynamic LDS: G*Ld int (next slot per
-// (query, row)) followed by G*Ld*2 uint (64-bit lane masks per (query, row)).
+// (query, row)).
 // A wave reads its query's Lq argmax entries once, into registers (at most
 // kMaxLq / 64 per lane), and uses them for both the count and the fill.
 constexpr int kFillIt = kMaxLq / 64;
@@ -242,8 +241,7 @@ __global__ __launch_bounds__(1024) void csr_fill(BwdParams p) {
     const int tid = threadIdx.x, nt = blockDim.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int Ld = p.Ld;
-    int* slot = lds;                                            // [G][Ld]
-    unsigned* mask = reinterpret_cast<unsigned*>(lds + p.G * Ld);  // [G][Ld][2]
+    int* slot = lds;  // [G][Ld]
     const int q = qg * p.G + wave;
     int64_t rstart;
     int len;
@@ -256,11 +254,7 @@ __global__ __launch_bounds__(1024) void csr_fill(BwdParams p) {
         const int i = k * 64 + lane;
         tk[k] = (q < p.Nq && i < p.Lq) ? clamp_tok(a[i], len) : -1;
     }
-    for (int e = tid; e < p.G * Ld; e += nt) {
-        slot[e] = 0;
-        mask[2 * e] = 0u;
-        mask[2 * e + 1] = 0u;
-    }
+    for (int e = tid; e < p.G * Ld; e += nt) slot[e] = 0;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kFillIt; ++k)
@@ -279,36 +273,29 @@ __global__ __launch_bounds__(1024) void csr_fill(BwdParams p) {
     __syncthreads();
     if (q < p.Nq) {
         int* myslot = slot + wave * Ld;
-        unsigned* mymask = mask + 2 * wave * Ld;
         const unsigned long long below = (1ull << lane) - 1ull;
         const int64_t s0 = ((int64_t)q * p.B + b) * p.Lq;
+        const int nbits = Ld > 1 ? 32 - __clz(Ld - 1) : 0;  // bits of a row index
 #pragma unroll
         for (int k = 0; k < kFillIt; ++k) {
             if (k * 64 >= p.Lq) break;  // uniform
             const int t = tk[k];
             const bool active = t >= 0;
-            if (active) atomicOr(&mymask[2 * t + (lane >> 5)], 1u << (lane & 31));
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the ORs have landed
-            __builtin_amdgcn_wave_barrier();
-            unsigned long long mk = 0;
-            int base = 0;
-            if (active) {
-                mk = (unsigned long long)mymask[2 * t] | ((unsigned long long)mymask[2 * t + 1] << 32);
-                base = myslot[t];
+            // the lanes of this step holding the same row: one ballot per bit
+            unsigned long long mk = __ballot(active);
+            for (int bit = 0; bit < nbits; ++bit) {  // uniform
+                const bool one = (t >> bit) & 1;
+                const unsigned long long v = __ballot(one);
+                mk &= one ? v : ~v;
             }
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_wave_barrier();
             if (active) {
+                // the wave's LDS operations run in order: every lane of the row
+                // reads the slot before its lowest lane advances it
+                const int base = myslot[t];
                 const int rank = __popcll(mk & below);
                 p.col_idx[base + rank] = (int)(s0 + k * 64 + lane);
-                if (rank == 0) {  // the lowest lane of the row advances it and clears the mask
-                    myslot[t] = base + __popcll(mk);
-                    mymask[2 * t] = 0u;
-                    mymask[2 * t + 1] = 0u;
-                }
+                if (rank == 0) myslot[t] = base + __popcll(mk);
             }
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_wave_barrier();
         }
     }
 }
@@ -771,7 +758,7 @@ hipError_t launch_bwd_elem(const BwdParams& p, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(csr_scan, dim3(p.B), dim3(1024), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(csr_fill, dim3(groups), dim3(nthr), (size_t)p.G * p.Ld * 12, stream, p);
+    hipLaunchKernelGGL(csr_fill, dim3(groups), dim3(nthr), (size_t)p.G * p.Ld * 4, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     unsigned blocks;
     int rpg;
