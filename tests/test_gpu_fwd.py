@@ -198,3 +198,11 @@ def test_workload_colpali_sampled(bd):
     w = inputs.make("colpali_fwd")
     docs = np.array([0, 1, 4999, 9998, 9999])
     sampled_check(bd, w, docs, "colpali_fwd")
+
+
+def test_workload_contrastive_train_varlen_forward(bd):
+    """The ragged training workload's forward (64 queries x 1024 tokens, 64 packed
+    documents of 256..1024 tokens, bf16, argmax): 12 documents through the oracle."""
+    w = inputs.make("contrastive_train_varlen")
+    docs = np.sort(np.random.default_rng(3).choice(w["B"], size=12, replace=False))
+    sampled_check(bd, w, docs, "contrastive_train_varlen")

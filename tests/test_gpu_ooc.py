@@ -70,10 +70,10 @@ PACKED = [  # (Nq, Lq, lengths, max_Ld, block_docs)
 
 
 @pytest.mark.parametrize("case", PACKED, ids=[str(c[:2]) + "x%d" % len(c[2]) for c in PACKED])
-@pytest.mark.parametrize("pinned", [True, False])
-def test_packed(bd, case, pinned):
+@pytest.mark.parametrize("pinned,dtn", [(True, inputs.F16), (False, inputs.F16), (True, inputs.BF16)],
+                         ids=["pinned-f16", "pageable-f16", "pinned-bf16"])
+def test_packed(bd, case, pinned, dtn):
     Nq, Lq, lens, max_Ld, blk = case
-    dtn = inputs.F16
     seed = 2200 + Nq + Lq + len(lens)
     Q = inputs.random_rows(seed, Nq * Lq, 128, dtn).reshape(Nq, Lq, 128)
     cu = inputs.cu_seqlens(np.asarray(lens, np.int32))
