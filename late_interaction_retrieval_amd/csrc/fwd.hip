@@ -59,7 +59,7 @@ struct FwdParams {
     int split;        // 1: slabs hold whole queries; 2: each query is two half slabs
     int half_rows;    // rows of the first half of a split query
     int num_slabs;
-    int num_streams;  // documents b = stream, stream + num_streams, ...
+    int num_streams;  // document streams (contiguous document ranges, see stream_range)
     float* scores;
     int32_t* argmax;
 };
@@ -208,6 +208,70 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
+// Document stream s of S scores the contiguous range [start(s), start(s+1)).
+// Padded documents are split by count.  A packed corpus is split by work:
+// document b costs its tokens plus DOC_COST (a partial sub-tile and the
+// per-document epilogue, in token units), so with key(b) = cu[b] + DOC_COST*b
+// (increasing in b), start(s) is the first document whose key reaches
+// s*K/S, K = key(B), and every stream gets about K/S, to within one document.
+// (Dealing ragged documents round-robin leaves the longest stream 6-11 %
+// above the mean at the packed workloads' length mixes, and the grid waits
+// for it.)  start(s) is found by the whole workgroup: each round the NT
+// threads test evenly spaced entries of the remaining range and a workgroup
+// count of those below the target narrows it by a factor of NT, so
+// B <= NT^2 needs two rounds of loads.  start(0) = 0 and start(S) = B.  Both
+// ends use the same search, so neighbouring streams agree on their common
+// boundary.  Every thread of the workgroup must call this (it has barriers).
+constexpr int64_t DOC_COST = 32;
+template <bool VARLEN, int NT>
+__device__ __forceinline__ void stream_range(const FwdParams& p, int s, int& bbeg, int& bend) {
+    const int S = p.num_streams;
+    if constexpr (!VARLEN) {
+        bbeg = (int)((int64_t)s * p.B / S);
+        bend = (int)((int64_t)(s + 1) * p.B / S);
+    } else {
+        const int64_t K = p.T + DOC_COST * p.B;
+        const int64_t x0 = (int64_t)s * K / S;
+        const int64_t x1 = (int64_t)(s + 1) * K / S;
+        // the answer lies in [lo, hi] and key(hi) >= x (key(B) = K >= x)
+        int lo0 = 0, hi0 = s == 0 ? 0 : p.B;
+        int lo1 = s + 1 == S ? p.B : 0, hi1 = p.B;
+        const int t = threadIdx.x;
+        while (lo0 < hi0 || lo1 < hi1) {  // uniform
+            const int st0 = (hi0 - lo0) / NT + 1, st1 = (hi1 - lo1) / NT + 1;  // (hi - lo) / st < NT
+            const int64_t i0 = lo0 + (int64_t)t * st0, i1 = lo1 + (int64_t)t * st1;
+            const bool in0 = lo0 < hi0 && i0 <= hi0, in1 = lo1 < hi1 && i1 <= hi1;
+            const int64_t v0 = in0 ? p.cu[i0] + DOC_COST * i0 : 0;
+            const int64_t v1 = in1 ? p.cu[i1] + DOC_COST * i1 : 0;
+            // the samples below x form a prefix t < c; the answer is in (sample c-1, sample c]
+            const int c0 = __syncthreads_count(in0 && v0 < x0);
+            const int c1 = __syncthreads_count(in1 && v1 < x1);
+            if (lo0 < hi0) {
+                if (c0 == 0) {
+                    hi0 = lo0;
+                } else {
+                    const int64_t up0 = lo0 + (int64_t)c0 * st0;
+                    hi0 = up0 < hi0 ? (int)up0 : hi0;
+                    lo0 = lo0 + (c0 - 1) * st0 + 1;
+                    lo0 = lo0 > hi0 ? hi0 : lo0;
+                }
+            }
+            if (lo1 < hi1) {
+                if (c1 == 0) {
+                    hi1 = lo1;
+                } else {
+                    const int64_t up1 = lo1 + (int64_t)c1 * st1;
+                    hi1 = up1 < hi1 ? (int)up1 : hi1;
+                    lo1 = lo1 + (c1 - 1) * st1 + 1;
+                    lo1 = lo1 > hi1 ? hi1 : lo1;
+                }
+            }
+        }
+        bbeg = lo0;
+        bend = lo1 < lo0 ? lo0 : lo1;  // only a non-monotone cu_seqlens (unsupported) could invert them
+    }
+}
+
 // ELEM: kF16 / kBF16 / kI8.  M: MFMA block edge (16 or 32).  QB: M-row query
 // blocks per wave.  WQ x WT waves: WQ along query rows, WT along document
 // tokens.  SPW: M-token sub-tiles each wave contracts per tile, NSI of them at
@@ -269,6 +333,8 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     const int slab = jx % p.num_slabs;
     const int stream = (jx / p.num_slabs) * 8 + xcd;
     if (stream >= p.num_streams || stream >= p.B) return;  // uniform over the workgroup
+    int bbeg, bend;  // this stream's documents
+    stream_range<VARLEN, NT>(p, stream, bbeg, bend);
     const int Lq = p.Lq;
     // The slab is nq queries x ni of their rows, starting at row i0 of each:
     // whole queries (i0 = 0, ni = Lq) or one half of a split query.  Its rows
@@ -611,9 +677,26 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         }
     };
 
+    // 32-token queries in 32x32 blocks (the common ColBERT shape): block cb of a
+    // wave is exactly one query, so once its rows are merged the score is the
+    // sum over lanes 0..31, formed in registers with DPP (no LDS round trip
+    // and nothing left for after the barrier).  The adds pair lanes as the
+    // butterfly xor 1, 2, 4, 8, 16 over the same values does, so the result is
+    // the same as the general path's.
+    const bool wave_sums = !I8 && M == 32 && Lq == 32 && p.split == 1;
+    auto lanes32_sum = [&](float v) {  // lanes 16..31 get the sum over lanes 0..31
+        v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+        v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+        v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+        v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0x140, 0xF, 0xF, false));  // row_mirror
+        // row_bcast:15 into rows 1 and 3 (rows 0 and 2 keep 0)
+        v += bitsf(__builtin_amdgcn_update_dpp(0u, fbits(v), 0x142, 0xA, 0xF, false));
+        return v;
+    };
+
     // End of a document, part 1 (before the step barrier): merge the NG token
     // sets of every query row (lanes lm + M*g) and park the row results.
-    auto epilogue_merge = [&](int par) {
+    auto epilogue_merge = [&](int par, int b) {
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb) {
             float mv = m[cb];
@@ -640,9 +723,16 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                 }
             }
             const int r = (wq * QB + cb) * M + lm;
-            if (g == 0) {
+            if (g == 0 && (ARGMAX || !wave_sums)) {  // row maxima for the general sum or the argmax merge
                 rowmax_s[par][wt][rpad(r)] = mv;
                 if constexpr (ARGMAX) rowarg_s[par][wt][r] = idx;
+            }
+            if constexpr (!I8 && M == 32 && WT == 1) {
+                if (wave_sums) {  // uniform
+                    const float sc = lanes32_sum(mv);
+                    const int ql = wq * QB + cb;
+                    if (lane == 31 && ql < nq) p.scores[(int64_t)(q0 + ql) * p.B + b] = sc;
+                }
             }
             m[cb] = -INFINITY;
             km[cb] = -INFINITY;
@@ -698,6 +788,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             // A split query's two halves each add their partial sum to the
             // zero-filled score: two addends, so the result does not depend on
             // which lands first.
+            if (WT == 1 && wave_sums) return;  // summed in registers by epilogue_merge
             int P = 1;
             while (P < ni && P < 64) P <<= 1;
             const int qpw = 64 / P;
@@ -735,7 +826,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         c.start = 0;
         c.len = 0;
         c.ntiles = 0;
-        if (b < p.B) {
+        if (b < bend) {
             doc_info<VARLEN>(p, b, c.start, c.len);
             c.ntiles = (c.len + TT - 1) / TT;
         }
@@ -750,7 +841,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     // read at the start of step k+1.
     const bool doc_wave = wave == NW - 1;
     auto prefetch_doc = [&](int slot, int b) {
-        if (doc_wave && b < p.B && lane < 2) {
+        if (doc_wave && b < bend && lane < 2) {
             const int32_t* src;
             if constexpr (VARLEN) {
                 src = p.cu + b + lane;
@@ -767,7 +858,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         c.start = 0;
         c.len = 0;
         c.ntiles = 0;
-        if (b < p.B) {
+        if (b < bend) {
             const int v0 = (VARLEN || p.lens) ? docpf[slot][0] : p.Ld;
             if constexpr (VARLEN) {
                 const int v1 = docpf[slot][1];
@@ -790,7 +881,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             n.t += 1;
             return n;
         }
-        return from_prefetch(slot, c.b + p.num_streams);
+        return from_prefetch(slot, c.b + 1);
     };
     // nothing to read at all: every document is empty and D may be absent
     const bool loads = p.T > 0;
@@ -800,25 +891,25 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     // step k >= 1, cs[NBUF-1] = tile k+NBUF-1 goes into the buffer that step
     // k-1 freed.  So at any time the next NBUF-1 tiles are in flight or landed.
     Cur cs[NBUF];
-    cs[0] = at_doc(stream);
+    cs[0] = at_doc(bbeg);
     static_for<NBUF - 1>([&](auto jc) {
         constexpr int j = decltype(jc)::value + 1;
         cs[j] = cs[j - 1];
         if (cs[j].t + 1 < cs[j].ntiles) {
             cs[j].t += 1;
         } else {
-            cs[j] = at_doc(cs[j - 1].b + p.num_streams);
+            cs[j] = at_doc(cs[j - 1].b + 1);
         }
     });
-    prefetch_doc(1, cs[NBUF - 1].b + p.num_streams);
+    prefetch_doc(1, cs[NBUF - 1].b + 1);
     if (loads) {
         static_for<NBUF>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            if (cs[j].b < p.B) issue_tile(j, cs[j].start, cs[j].len, cs[j].t);
+            if (cs[j].b < bend) issue_tile(j, cs[j].start, cs[j].len, cs[j].t);
         });
         // tile 0 has landed once only the loads of tiles 1 .. NBUF-1 may remain;
         // when the stream ends earlier, fewer were issued: wait for all
-        if (cs[NBUF - 1].b < p.B) {
+        if (cs[NBUF - 1].b < bend) {
             if (scale_wave) {
                 wait_vmcnt<(NBUF - 1) * (LPW + 1)>();
             } else {
@@ -833,18 +924,18 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     int step = 0;
     int par = 0;          // parity of the next document to finish
     int pend = -1;        // document whose outputs are parked in rowmax_s[par ^ 1]
-    bool hasn = cs[NBUF - 1].b < p.B;  // the newest tile (cs[NBUF-1]) exists
+    bool hasn = cs[NBUF - 1].b < bend;  // the newest tile (cs[NBUF-1]) exists
     while (true) {
-        const bool has0 = cs[0].b < p.B;
+        const bool has0 = cs[0].b < bend;
         if (pend >= 0) {  // stores first: they must be older than this step's loads
             epilogue_out(pend, par ^ 1);
             pend = -1;
         }
         if (step > 0) {
-            const bool hasl = cs[NBUF - 2].b < p.B;
+            const bool hasl = cs[NBUF - 2].b < bend;
             cs[NBUF - 1] = hasl ? advance(step & 1, cs[NBUF - 2]) : cs[NBUF - 2];
-            hasn = hasl && cs[NBUF - 1].b < p.B;
-            if (hasn) prefetch_doc((step + 1) & 1, cs[NBUF - 1].b + p.num_streams);
+            hasn = hasl && cs[NBUF - 1].b < bend;
+            if (hasn) prefetch_doc((step + 1) & 1, cs[NBUF - 1].b + 1);
             if (loads && hasn) {
                 const int nb = buf + NBUF - 1;
                 issue_tile(nb >= NBUF ? nb - NBUF : nb, cs[NBUF - 1].start, cs[NBUF - 1].len, cs[NBUF - 1].t);
@@ -853,7 +944,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         if (!has0) break;  // nothing issued or pending past here (has0 false => hasn false)
         if (cs[0].t < cs[0].ntiles) compute_tile(buf, cs[0].t, cs[0].len);
         if (cs[0].t + 1 >= cs[0].ntiles) {
-            epilogue_merge(par);
+            epilogue_merge(par, cs[0].b);
             pend = cs[0].b;
             par ^= 1;
         }

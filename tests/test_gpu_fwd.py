@@ -108,6 +108,43 @@ def test_random_shapes_varlen_and_padded(bd, shape, dtn):
     assert np.array_equal(s2, s) and np.array_equal(a2, a), where + ": padded != varlen"
 
 
+# Skewed corpora for the split of documents into streams (contiguous ranges
+# balanced by tokens plus a per-document cost): a long run of empty documents
+# first, then short ones, then a few long ones; 32-token queries (scores
+# summed in registers) and 40-token queries (summed through LDS); and more
+# documents than two rounds of the workgroup search cover (B > 512^2).
+SKEWED = [  # Nq, Lq, B, empty, short (lo, hi), long, (lo, hi)
+    (3, 32, 5000, 3000, (1, 40), 100, (200, 600)),
+    (3, 40, 5000, 3000, (1, 40), 100, (200, 600)),
+    (20, 32, 1200, 10, (32, 300), 2, (3000, 4000)),
+    (2, 32, 300000, 0, (0, 2), 0, (0, 0)),
+]
+
+
+@pytest.mark.parametrize("shape", SKEWED, ids=[str(s) for s in SKEWED])
+def test_skewed_corpus_stream_split(bd, shape):
+    Nq, Lq, B, n_empty, (slo, shi), n_long, (llo, lhi) = shape
+    rng = np.random.default_rng(B + Lq)
+    lens = np.zeros(B, np.int32)
+    n_short = B - n_empty - n_long
+    lens[n_empty:n_empty + n_short] = rng.integers(slo, shi + 1, size=n_short)
+    lens[B - n_long:] = rng.integers(llo, lhi + 1, size=n_long)
+    cu = inputs.cu_seqlens(lens)
+    Q = inputs.random_rows(B + 1, Nq * Lq, 128, inputs.F16).reshape(Nq, Lq, 128)
+    Dp = inputs.random_rows(B + 2, int(cu[-1]), 128, inputs.F16, stream=4)
+    # every score is written: prefill with NaN, which no document can give
+    scores = torch.full((Nq, B), float("nan"), dtype=torch.float32, device=DEV)
+    s, a = bd.maxsim_fwd_varlen(to_dev(Q, inputs.F16), to_dev(Dp, inputs.F16), to_dev(cu), max(1, int(lens.max())),
+                                scores=scores)
+    torch.cuda.synchronize()
+    s, a = s.cpu().numpy(), a.cpu().numpy()
+    assert not np.isnan(s).any(), "some documents were never scored"
+    s_ref, a_ref, m_ref = oracle.fwd_varlen(Q, Dp, cu, oracle.F16, want_rowmax=True)
+    where = "skewed %s" % (shape,)
+    check_scores(s, s_ref, Lq, where)
+    check_argmax(a, a_ref, m_ref, oracle.sim_at(Q, Dp, cu, oracle.F16, a), lens, where)
+
+
 def test_padding_never_selected_all_negative(bd):
     """All valid similarities negative, padding rows huge: padding is never picked."""
     Q = np.full((2, 40, 128), 0.05, np.float16)
@@ -188,6 +225,13 @@ def test_workload_colbert_rerank_varlen_sampled(bd):
     docs = np.sort(np.random.default_rng(1).choice(w["B"], size=64, replace=False))
     docs[0], docs[-1] = 0, w["B"] - 1
     s, _ = sampled_check(bd, w, docs, "colbert_rerank_varlen")
+    # the launch the benchmark times (no argmax) writes every score, and the
+    # same bits as with the argmax
+    scores = torch.full((w["Nq"], w["B"]), float("nan"), dtype=torch.float32, device=DEV)
+    s0, _ = bd.maxsim_fwd_varlen(to_dev(w["Q"], inputs.F16), to_dev(w["D_packed"], inputs.F16),
+                                 to_dev(w["cu_seqlens"]), 300, scores=scores, with_argmax=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(s0.cpu().numpy(), s)
     # padded to 300 with d_lens: identical scores
     Dpad = inputs.pad_packed(w["D_packed"], w["cu_seqlens"], 300)
     s2, _ = run_padded(bd, w["Q"], Dpad, inputs.F16, w["lens"], with_argmax=False)
