@@ -387,8 +387,9 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
 
     // Direct HBM -> LDS loads of one tile into ring slot bf.  Every wave issues
     // exactly LPW (+1 for the scale waves) loads, so vmcnt bookkeeping is
-    // static; lanes whose token is past the document's end fetch a clamped
-    // in-bounds row instead, and the compute masks those tokens.
+    // static; lanes whose token is past the document's end fetch the
+    // document's first row instead (in bounds, and a repeat of a value the
+    // maximum already sees), and the compute masks those tokens where needed.
     const bool scale_wave = I8 && wave < SCW;
     auto issue_tile = [&](int bf, int64_t st, int ln, int tt) {
         const int64_t safe = ln > 0 ? st : 0;
@@ -636,11 +637,17 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             sc_cur = stage_scales(bf, sb);
             stage(bf, sb, cur, prev, sc_prev, j > 0, gsub - 1);
             if (j == nsub - 1) {  // drain: fold the last sub-tile (the only one that can be partial)
+                // Rows past the document's end were loaded as copies of its
+                // first row (issue_tile), so their values repeat that token's
+                // under a later index: they change no maximum, and with the
+                // strict in-lane update and the lower-index merge they never
+                // win an exact argmax either.  Only the keyed argmax, which
+                // ranks values within 2^KB ulp by slot, must mask them.
                 const int tok0 = tok_w + j * M;
-                if (tok0 + M <= ln) {
-                    fold(std::false_type{}, cur, sc_cur, tok0, ln, gsub);
-                } else {
+                if (KEYED && tok0 + M > ln) {
                     fold(std::true_type{}, cur, sc_cur, tok0, ln, gsub);
+                } else {
+                    fold(std::false_type{}, cur, sc_cur, tok0, ln, gsub);
                 }
             }
         });

@@ -145,6 +145,26 @@ def test_skewed_corpus_stream_split(bd, shape):
     check_argmax(a, a_ref, m_ref, oracle.sim_at(Q, Dp, cu, oracle.F16, a), lens, where)
 
 
+@pytest.mark.parametrize("dtn", [inputs.F16, inputs.BF16])
+def test_first_token_max_ragged_tails(bd, dtn):
+    """Every document starts with the token closest to every query row, with
+    partial 32-token sub-tiles.  Rows past a document's end are read as copies
+    of its first token; the maxima must not change and every argmax must stay
+    inside the document."""
+    Nq, Lq = 20, 32
+    # one unit query row repeated, and that row as every document's first
+    # token: similarity 1 at token 0, about N(0, 1/128) elsewhere
+    row = inputs.random_rows(63, 1, 128, dtn)
+    Q = np.repeat(row, Nq * Lq, axis=0).reshape(Nq, Lq, 128)
+    lens = np.array([1, 15, 17, 31, 33, 47, 100, 129, 255, 257, 300], np.int32)
+    cu = inputs.cu_seqlens(lens)
+    Dp = inputs.random_rows(64, int(cu[-1]), 128, dtn, stream=4)
+    for b in range(len(lens)):
+        Dp[cu[b]] = row[0]
+    s, a = full_check_varlen(bd, Q, Dp, cu, dtn, "first-token max %s" % dtn)
+    assert np.all(a == 0)
+
+
 def test_padding_never_selected_all_negative(bd):
     """All valid similarities negative, padding rows huge: padding is never picked."""
     Q = np.full((2, 40, 128), 0.05, np.float16)

@@ -83,6 +83,31 @@ def test_duplicate_tokens_tie_to_first(bd):
     assert np.array_equal(a, a_ref) and np.all(a < 90)
 
 
+def test_first_token_max_ragged_tails(bd):
+    """Every document starts with the token that best matches every query row,
+    and lengths leave partial 16-token sub-tiles.  Rows past a document's end
+    are read as copies of its first token, so they tie the maximum: the argmax
+    must still be the first index, 0, and scores bit-exact."""
+    Nq, Lq = 3, 32
+    # one query row repeated (half of the rows negated), and that row as every
+    # document's first token: token 0 is the exact maximum of the positive rows
+    row, sc = inputs.random_rows(61, 1, 128, inputs.I8)
+    sign = np.where(np.arange(Nq * Lq) % 2 == 0, 1, -1).astype(np.int8)
+    Q = (row * sign[:, None]).reshape(Nq, Lq, 128)
+    qs = np.full((Nq, Lq), sc[0], np.float32)
+    lens = np.array([1, 15, 17, 31, 33, 47, 100, 129, 255, 257], np.int32)
+    cu = inputs.cu_seqlens(lens)
+    Dp, ds = inputs.random_rows(62, int(cu[-1]), 128, inputs.I8, stream=4)
+    for b in range(len(lens)):
+        Dp[cu[b]] = row[0]
+        ds[cu[b]] = sc[0]
+    s_ref, a_ref = oracle.fwd_i8(Q, qs, Dp, ds, cu)
+    assert np.all(a_ref[:, :, 0::2] == 0)  # rows i = 0, 2, ... are the positive copies
+    s, a = run_i8(bd, Q, qs, Dp, ds, cu)
+    assert_bits_equal(s, s_ref, "first-token max")
+    assert np.array_equal(a, a_ref)
+
+
 def test_workload_int8_sampled(bd):
     w = inputs.make("int8_varlen")
     s, a = run_i8(bd, w["Q"], w["q_scale"], w["D_packed"], w["d_scale"], w["cu_seqlens"])
