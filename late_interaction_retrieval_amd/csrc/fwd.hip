@@ -270,6 +270,22 @@ __device__ __forceinline__ void stream_range(const FwdParams& p, int s, int& bbe
         bbeg = lo0;
         bend = lo1 < lo0 ? lo0 : lo1;  // only a non-monotone cu_seqlens (unsupported) could invert them
     }
+    // the same in every thread: keep them (and what is derived from them) scalar
+    bbeg = __builtin_amdgcn_readfirstlane(bbeg);
+    bend = __builtin_amdgcn_readfirstlane(bend);
+}
+
+// Sum over lanes 0..31 of a wave, left in lanes 16..31 (and the sum over
+// lanes 32..63 in lanes 48..63), by DPP.  The adds pair lanes as a butterfly
+// xor 1, 2, 4, 8, 16 does.
+__device__ __forceinline__ float lanes32_sum(float v) {
+    v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0x140, 0xF, 0xF, false));  // row_mirror
+    // row_bcast:15 into rows 1 and 3 (rows 0 and 2 keep 0)
+    v += bitsf(__builtin_amdgcn_update_dpp(0u, fbits(v), 0x142, 0xA, 0xF, false));
+    return v;
 }
 
 // ELEM: kF16 / kBF16 / kI8.  M: MFMA block edge (16 or 32).  QB: M-row query
@@ -687,19 +703,9 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     // 32-token queries in 32x32 blocks (the common ColBERT shape): block cb of a
     // wave is exactly one query, so once its rows are merged the score is the
     // sum over lanes 0..31, formed in registers with DPP (no LDS round trip
-    // and nothing left for after the barrier).  The adds pair lanes as the
-    // butterfly xor 1, 2, 4, 8, 16 over the same values does, so the result is
-    // the same as the general path's.
+    // and nothing left for after the barrier).  lanes32_sum pairs lanes as the
+    // butterfly of the general path does, so the result is the same.
     const bool wave_sums = !I8 && M == 32 && Lq == 32 && p.split == 1;
-    auto lanes32_sum = [&](float v) {  // lanes 16..31 get the sum over lanes 0..31
-        v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-        v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-        v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
-        v += bitsf(__builtin_amdgcn_mov_dpp(fbits(v), 0x140, 0xF, 0xF, false));  // row_mirror
-        // row_bcast:15 into rows 1 and 3 (rows 0 and 2 keep 0)
-        v += bitsf(__builtin_amdgcn_update_dpp(0u, fbits(v), 0x142, 0xA, 0xF, false));
-        return v;
-    };
 
     // End of a document, part 1 (before the step barrier): merge the NG token
     // sets of every query row (lanes lm + M*g) and park the row results.
@@ -970,6 +976,206 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             cs[j] = cs[j + 1];
         });
     }
+}
+
+// Packed corpus, 32-token queries, scores only (the ColBERT re-ranking
+// shape).  A document's epilogue then needs nothing outside the wave (each
+// 32x32 block of a wave is one query: lane merge, DPP sum, one store), so a
+// stream reads its contiguous packed token range [cu[bbeg], cu[bend]) as full
+// 256-token tiles that run across document boundaries, and the fold splits a
+// sub-tile's values where a document ends.  Against tiles aligned to
+// documents this drops the partial last sub-tile of every document (about a
+// tenth of the MFMA work at 32..300-token documents) and about half of the
+// steps with their barriers.  Every maximum and the DPP sum are the same as
+// fwd_kernel's, so the scores are bit-identical to it.
+template <int ELEM>
+__global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
+    using MM = Mma<ELEM, 32>;
+    using Acc = typename MM::Acc;
+    constexpr int M = 32, QB = 2, NW = 8, NT = 64 * NW, SPW = 8, TT = M * SPW, NCH = 16;
+    constexpr int KS = MM::KS, VPL = MM::VPL, FPS = VPL / KS;
+    constexpr int LPW = TT * NCH / NT;  // 1 KB direct loads per wave per tile
+    static_assert(LPW * NT == TT * NCH, "tile must split into whole 1 KB loads per wave");
+    constexpr int DCAP = 4096;  // document ends kept in LDS
+    __shared__ u32x4 dtile[2][TT * NCH];
+    __shared__ int dend_s[DCAP];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane / M, lm = lane % M;
+    const int blk = blockIdx.x;
+    const int xcd = blk & 7;
+    const int jx = blk >> 3;
+    const int slab = jx % p.num_slabs;
+    const int stream = (jx / p.num_slabs) * 8 + xcd;
+    if (stream >= p.num_streams || stream >= p.B) return;  // uniform over the workgroup
+    int bbeg, bend;
+    stream_range<true, NT>(p, stream, bbeg, bend);
+    const int q0 = slab * p.qps;
+    const int nq = min(p.qps, p.Nq - q0);
+    const int nrows = nq * M;
+    const int64_t qrow0 = (int64_t)q0 * M;
+
+    u32x4 bq[QB][KS];  // the wave's 64 query rows, as in fwd_kernel
+#pragma unroll
+    for (int cb = 0; cb < QB; ++cb) {
+        const int r = (wave * QB + cb) * M + lm;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            bq[cb][s] = r < nrows ? *reinterpret_cast<const u32x4*>(p.Q + (qrow0 + r) * 256 + (g * KS + s) * 16)
+                                  : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    const cint_ptr cu = (cint_ptr)p.cu;
+    auto clamp_t = [&](int64_t v) -> int64_t { return v < 0 ? 0 : (v > p.T ? p.T : v); };
+    const int64_t T0 = clamp_t(cu[bbeg]);
+    int64_t T1 = clamp_t(cu[bend]);
+    T1 = T1 < T0 ? T0 : T1;
+    const int ntile = (int)((T1 - T0 + TT - 1) / TT);
+
+    // Tile k: tokens T0 + k*TT ... (past T1: the tile's first row again, in bounds, never folded)
+    auto issue_tile = [&](int bf, int k) {
+        const int64_t st = T0 + (int64_t)k * TT;
+        const int64_t ln = T1 - st;
+#pragma unroll
+        for (int u = 0; u < LPW; ++u) {
+            const int slot0 = (u * NW + wave) * 64;
+            const int sl = slot0 + lane;
+            const int row = sl / NCH;
+            const int c = swz_chunk<NCH>(row, sl % NCH);
+            const int64_t grow = row < ln ? st + row : st;
+            __builtin_amdgcn_global_load_lds((gptr_t)(p.D + grow * 256 + c * 16), (lptr_t)&dtile[bf][slot0], 16, 0, 0);
+        }
+    };
+
+    float m[QB];
+#pragma unroll
+    for (int cb = 0; cb < QB; ++cb) m[cb] = -INFINITY;
+    // The ends of the stream's documents go to LDS once, up front: read at a
+    // boundary, a scalar load would stall the wave for a memory round trip
+    // (its counter is shared with LDS reads, so it cannot be left in flight).
+    // A stream of more than DCAP documents reads them from memory instead.
+    const int nd = bend - bbeg;
+    const bool ends_lds = nd <= DCAP;  // uniform
+    if (ends_lds) {
+        for (int i = tid; i < nd; i += NT) dend_s[i] = (int)clamp_t(p.cu[bbeg + i + 1]);
+    }
+    // (read as the same value in every lane: the document walk, and every
+    // branch on it, stays scalar)
+    auto doc_end = [&](int bb) -> int64_t {
+        return ends_lds ? (int64_t)__builtin_amdgcn_readfirstlane(dend_s[bb - bbeg]) : clamp_t(cu[bb + 1]);
+    };
+    // The document being folded, b, ends at token dend (wave-uniform).
+    int b = bbeg;
+    int64_t dend = T1;
+    auto finish_doc = [&]() {  // document b is complete: merge, sum, store; move to b + 1
+#pragma unroll
+        for (int cb = 0; cb < QB; ++cb) {
+            const float mv = fmaxf(m[cb], xor32_f(m[cb], lane));
+            const float sc = lanes32_sum(mv);
+            const int ql = wave * QB + cb;
+            if (lane == 31 && ql < nq) p.scores[(int64_t)(q0 + ql) * p.B + b] = sc;
+            m[cb] = -INFINITY;
+        }
+        ++b;
+        if (b < bend) dend = doc_end(b);
+    };
+    // Fold the values of tokens lo <= t < hi (relative to the sub-tile).
+    auto fold_range = [&](const Acc* acc, int lo, int hi) {
+#pragma unroll
+        for (int cb = 0; cb < QB; ++cb) {
+            float mx = m[cb];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int t = MM::tok(g, i);
+                mx = fmaxf(mx, (t >= lo && t < hi) ? acc[cb][i] : -INFINITY);
+            }
+            m[cb] = mx;
+        }
+    };
+    // Fold the sub-tile whose first token is t0, finishing every document
+    // that ends inside it (empty ones included).
+    auto fold_sub = [&](const Acc* acc, int64_t t0) {
+        int lo = 0;
+        while (b < bend && dend - t0 < M) {  // uniform
+            const int e = (int)(dend - t0);
+            if (e > lo) fold_range(acc, lo, e);
+            finish_doc();
+            lo = e > lo ? e : lo;
+        }
+        if (b < bend) {
+            if (lo == 0) {
+#pragma unroll
+                for (int cb = 0; cb < QB; ++cb) {
+                    float mx = m[cb];
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) mx = fmaxf(mx, acc[cb][i]);
+                    m[cb] = mx;
+                }
+            } else {
+                fold_range(acc, lo, M);
+            }
+        }
+    };
+    // MFMAs of sub-tile sb into cur; when fold_prev, the previous sub-tile
+    // (wholly inside document b) is folded between them, as in fwd_kernel.
+    // A sub-tile holding a document end is folded afterwards by fold_sub
+    // (folding it between the MFMAs, with a branch per k-step, ran slower).
+    auto stage = [&](int bf, int sb, Acc* cur, const Acc* prev, bool fold_prev) {
+        u32x4 a[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a[s] = dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
+#pragma unroll
+        for (int cb = 0; cb < QB; ++cb) cur[cb] = MM::zero();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+            for (int cb = 0; cb < QB; ++cb) cur[cb] = MM::mma(a[s], bq[cb][s], cur[cb]);
+            if (fold_prev) {  // uniform
+#pragma unroll
+                for (int cb = 0; cb < QB; ++cb)
+#pragma unroll
+                    for (int f = 0; f < FPS; ++f) m[cb] = fmaxf(m[cb], prev[cb][s * FPS + f]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    if (ntile > 0) issue_tile(0, 0);
+    if (ntile > 1) {
+        issue_tile(1, 1);
+        wait_vmcnt<LPW>();  // tile 0 has landed; tile 1 may be in flight
+    } else {
+        wait_vmcnt<0>();
+    }
+    lds_barrier();  // also publishes dend_s
+    if (b < bend) dend = doc_end(b);
+    Acc acc0[QB], acc1[QB];
+    for (int k = 0; k < ntile; ++k) {
+        const int bf = k & 1;
+        // tile k+1 goes into the buffer step k-1 read (tile 1 came with the prologue)
+        if (k >= 1 && k + 1 < ntile) issue_tile(bf ^ 1, k + 1);
+        const int64_t tb = T0 + (int64_t)k * TT;
+        const int64_t left = T1 - tb;
+        const int nsub = left >= TT ? SPW : (int)((left + M - 1) / M);
+        static_for<SPW>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if (j >= nsub) return;  // uniform
+            Acc* cur = (j & 1) ? acc1 : acc0;
+            const Acc* prev = (j & 1) ? acc0 : acc1;
+            const int64_t tprev = tb + (int64_t)(j - 1) * M;
+            const bool whole = j > 0 && b < bend && dend - tprev >= M;  // previous sub-tile inside document b
+            stage(bf, j, cur, prev, whole);
+            if (j > 0 && !whole) fold_sub(prev, tprev);
+            if (j == nsub - 1) fold_sub(cur, tb + (int64_t)j * M);
+        });
+        if (k + 1 < ntile) wait_vmcnt<0>();  // tile k+1 has landed (and this step's stores retired)
+        lds_barrier();
+    }
+    // documents ending on the last sub-tile edge and empty trailing documents
+    while (b < bend) finish_doc();
 }
 
 // One workgroup of W waves scores up to 32 query rows (rows 0 .. nr-1 from
@@ -1245,6 +1451,33 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream, int target_blocks) {
     return hipGetLastError();
 }
 
+// fwd_flat_kernel: 512-row slabs of 16 queries; as many stream groups as fit
+// one workgroup per CU, at least one, and no more streams than documents.
+template <int ELEM>
+hipError_t launch_flat(const FwdArgs& a, hipStream_t stream) {
+    FwdParams p{};
+    p.Q = static_cast<const char*>(a.Q);
+    p.D = static_cast<const char*>(a.D);
+    p.cu = a.cu;
+    p.T = a.T;
+    p.Nq = a.Nq;
+    p.Lq = a.Lq;
+    p.B = a.B;
+    p.Ld = a.Ld;
+    p.split = 1;
+    p.half_rows = a.Lq;
+    p.qps = 16 < a.Nq ? 16 : a.Nq;
+    p.num_slabs = (a.Nq + p.qps - 1) / p.qps;
+    int s8 = 256 / (8 * p.num_slabs);
+    if (s8 < 1) s8 = 1;
+    if (s8 > (a.B + 7) / 8) s8 = (a.B + 7) / 8;
+    p.num_streams = 8 * s8 < a.B ? 8 * s8 : a.B;
+    p.scores = a.scores;
+    const long long blocks = 8LL * p.num_slabs * s8;
+    hipLaunchKernelGGL(fwd_flat_kernel<ELEM>, dim3((unsigned)blocks), dim3(512), 0, stream, p);
+    return hipGetLastError();
+}
+
 template <int ELEM, bool ARGMAX, bool VARLEN>
 hipError_t launch_tiny(const FwdArgs& a, hipStream_t stream) {
     FwdParams p{};
@@ -1286,6 +1519,10 @@ hipError_t dispatch_shape(const FwdArgs& a, hipStream_t stream) {
     if ((int64_t)a.Nq * a.Lq <= 32) {
         if constexpr (ELEM != kI8) return launch_tiny<ELEM, ARGMAX, VARLEN>(a, stream);
         return launch_cfg<ELEM, 16, 2, 1, 4, 1, 1, 3, ARGMAX, VARLEN>(a, stream, 2048);
+    }
+    // Packed corpus, 32-token queries, scores only: tiles across documents.
+    if constexpr (!ARGMAX && VARLEN && ELEM != kI8) {
+        if (a.Lq == 32) return launch_flat<ELEM>(a, stream);
     }
     // Otherwise one persistent workgroup per CU holding a slab of query rows.
     if constexpr (ELEM == kI8) {

@@ -118,6 +118,9 @@ SKEWED = [  # Nq, Lq, B, empty, short (lo, hi), long, (lo, hi)
     (3, 40, 5000, 3000, (1, 40), 100, (200, 600)),
     (20, 32, 1200, 10, (32, 300), 2, (3000, 4000)),
     (2, 32, 300000, 0, (0, 2), 0, (0, 0)),
+    (33, 32, 700, 0, (32, 32), 0, (0, 0)),
+    (16, 32, 3, 1, (1, 1), 1, (256, 256)),
+    (64, 32, 2000, 200, (0, 64), 50, (255, 513)),
 ]
 
 
@@ -143,6 +146,12 @@ def test_skewed_corpus_stream_split(bd, shape):
     where = "skewed %s" % (shape,)
     check_scores(s, s_ref, Lq, where)
     check_argmax(a, a_ref, m_ref, oracle.sim_at(Q, Dp, cu, oracle.F16, a), lens, where)
+    # scores only (for 32-token queries: tiles that run across documents)
+    scores.fill_(float("nan"))
+    s0, _ = bd.maxsim_fwd_varlen(to_dev(Q, inputs.F16), to_dev(Dp, inputs.F16), to_dev(cu), max(1, int(lens.max())),
+                                 scores=scores, with_argmax=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(s0.cpu().numpy(), s), where + ": scores differ without the argmax"
 
 
 @pytest.mark.parametrize("dtn", [inputs.F16, inputs.BF16])
