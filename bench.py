@@ -173,6 +173,18 @@ def inputs_bf16_bits(x):
     return inputs.f32_to_bf16_bits(x)
 
 
+def fwd_kernel_name(Nq, Lq, el, packed, argmax):
+    """The forward kernel the library launches for this shape (its dispatch
+    rule): a single 32-row query block runs one workgroup per document;
+    32-token queries over a packed corpus without argmax run the kernel that
+    tiles across document boundaries; everything else the slab kernel."""
+    if Nq * Lq <= 32 and el != "i8":
+        return "fwd_tiny_kernel"
+    if packed and not argmax and Lq == 32 and el != "i8":
+        return "fwd_flat_kernel"
+    return "fwd_kernel"
+
+
 def source_sha(kind):
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kind]:
@@ -465,7 +477,9 @@ def main():
         sp = sustained_peak(el)
         roofline["sustained_peak"] = round(sp, 1)
         roofline["frac_of_sustained"] = round(achieved / sp, 4)
-    roofline.update({"traffic": traffic, "kernel": "fwd_kernel", "kernel_avg_ms": round(k_avg_ms, 5),
+    roofline.update({"traffic": traffic, "kernel": fwd_kernel_name(Nq, Lq, el, name != "contrastive_train",
+                                                                  want_argmax),
+                     "kernel_avg_ms": round(k_avg_ms, 5),
                      "kernel_median_ms": round(k_med_ms, 5), "algorithmic_flops_per_launch": fwd_flops,
                      "algorithmic_bytes_per_launch": fwd_bytes, "arithmetic_intensity": round(fwd_flops / fwd_bytes, 1),
                      "mfma_frac": round(achieved / peak, 4), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4)})

@@ -59,7 +59,8 @@ struct FwdParams {
     int split;        // 1: slabs hold whole queries; 2: each query is two half slabs
     int half_rows;    // rows of the first half of a split query
     int num_slabs;
-    int num_streams;  // document streams (contiguous document ranges, see stream_range)
+    int num_streams;  // document streams
+    int round_robin;  // 1: stream s takes documents s, s + num_streams, ...; 0: a contiguous range (stream_range)
     float* scores;
     int32_t* argmax;
 };
@@ -349,8 +350,15 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     const int slab = jx % p.num_slabs;
     const int stream = (jx / p.num_slabs) * 8 + xcd;
     if (stream >= p.num_streams || stream >= p.B) return;  // uniform over the workgroup
-    int bbeg, bend;  // this stream's documents
-    stream_range<VARLEN, NT>(p, stream, bbeg, bend);
+    int bbeg, bend, bstep;  // this stream's documents: bbeg, bbeg + bstep, ... < bend
+    if (p.round_robin) {  // uniform
+        bbeg = stream;
+        bend = p.B;
+        bstep = p.num_streams;
+    } else {
+        stream_range<VARLEN, NT>(p, stream, bbeg, bend);
+        bstep = 1;
+    }
     const int Lq = p.Lq;
     // The slab is nq queries x ni of their rows, starting at row i0 of each:
     // whole queries (i0 = 0, ni = Lq) or one half of a split query.  Its rows
@@ -894,7 +902,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             n.t += 1;
             return n;
         }
-        return from_prefetch(slot, c.b + 1);
+        return from_prefetch(slot, c.b + bstep);
     };
     // nothing to read at all: every document is empty and D may be absent
     const bool loads = p.T > 0;
@@ -911,10 +919,10 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         if (cs[j].t + 1 < cs[j].ntiles) {
             cs[j].t += 1;
         } else {
-            cs[j] = at_doc(cs[j - 1].b + 1);
+            cs[j] = at_doc(cs[j - 1].b + bstep);
         }
     });
-    prefetch_doc(1, cs[NBUF - 1].b + 1);
+    prefetch_doc(1, cs[NBUF - 1].b + bstep);
     if (loads) {
         static_for<NBUF>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
@@ -948,7 +956,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             const bool hasl = cs[NBUF - 2].b < bend;
             cs[NBUF - 1] = hasl ? advance(step & 1, cs[NBUF - 2]) : cs[NBUF - 2];
             hasn = hasl && cs[NBUF - 1].b < bend;
-            if (hasn) prefetch_doc((step + 1) & 1, cs[NBUF - 1].b + 1);
+            if (hasn) prefetch_doc((step + 1) & 1, cs[NBUF - 1].b + bstep);
             if (loads && hasn) {
                 const int nb = buf + NBUF - 1;
                 issue_tile(nb >= NBUF ? nb - NBUF : nb, cs[NBUF - 1].start, cs[NBUF - 1].len, cs[NBUF - 1].t);
@@ -1443,6 +1451,11 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream, int target_blocks) {
     int streams = 8 * s8;
     if (streams > a.B) streams = a.B;
     p.num_streams = streams;
+    // A grid that fits one round of workgroups splits the documents into
+    // balanced contiguous ranges; a grid of several rounds is balanced by the
+    // hardware's dispatch of later workgroups, and there each workgroup would
+    // pay the range search again, so it deals documents round-robin.
+    p.round_robin = 8LL * p.num_slabs * s8 > target_blocks;
     p.scores = a.scores;
     p.argmax = a.argmax;
     const long long blocks = 8LL * p.num_slabs * s8;
@@ -1472,6 +1485,7 @@ hipError_t launch_flat(const FwdArgs& a, hipStream_t stream) {
     if (s8 < 1) s8 = 1;
     if (s8 > (a.B + 7) / 8) s8 = (a.B + 7) / 8;
     p.num_streams = 8 * s8 < a.B ? 8 * s8 : a.B;
+    p.round_robin = 0;  // the kernel walks contiguous token ranges
     p.scores = a.scores;
     const long long blocks = 8LL * p.num_slabs * s8;
     hipLaunchKernelGGL(fwd_flat_kernel<ELEM>, dim3((unsigned)blocks), dim3(512), 0, stream, p);
