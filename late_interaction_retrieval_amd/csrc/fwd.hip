@@ -641,13 +641,22 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             }
         }
     };
-    auto compute_tile_pipe = [&](int bf, int tt, int ln) {
+    // Ping-pong accumulators (even / odd stages) and their int8 token scales.
+    // They live across steps: when a tile is full and its document goes on
+    // in the next tile, its last sub-tile is not drained at the end of the
+    // step but folded by the next step's first stage, between its MFMAs (SPW
+    // is even, so that sub-tile sits in acc1 as a stage-(-1) result would).
+    // (fp16/bf16 only: the int8 path measured no faster with it.)
+    Acc acc0[QB], acc1[QB];
+    f32x4 sc0, sc1;
+    bool carry = false;  // acc1 / sc1 hold the unfolded last sub-tile of the previous tile
+    auto compute_tile_pipe = [&](int bf, int tt, int ln, bool last_tile) {
         if (wq * QB * M >= nrows) return;  // uniform: this wave's rows are all past the slab
         const int tok_w = tt * TT + wt * SPW * M;  // first token of this wave's sub-tiles
         int nsub = (ln - tok_w + M - 1) / M;       // sub-tiles holding at least one valid token
         nsub = nsub < 0 ? 0 : (nsub > SPW ? SPW : nsub);
-        Acc acc0[QB], acc1[QB];  // ping-pong accumulators (even / odd stages)
-        f32x4 sc0, sc1;          // their int8 token scales
+        const bool carried = carry;
+        carry = false;
         // stages are expanded at compile time so every accumulator index is static
         static_for<SPW>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
@@ -659,8 +668,11 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             const int sb = wt * SPW + j;
             const int gsub = tt * SUBS + sb;
             sc_cur = stage_scales(bf, sb);
-            stage(bf, sb, cur, prev, sc_prev, j > 0, gsub - 1);
-            if (j == nsub - 1) {  // drain: fold the last sub-tile (the only one that can be partial)
+            // with one token-wave the previous tile's last sub-tile is gsub - 1 too
+            stage(bf, sb, cur, prev, sc_prev, j > 0 || carried, gsub - 1);
+            if (!I8 && WT == 1 && SPW % 2 == 0 && j == SPW - 1 && !last_tile) {
+                carry = true;  // full tile, the document goes on: the next step folds it
+            } else if (j == nsub - 1) {  // drain: fold the last sub-tile (the only one that can be partial)
                 // Rows past the document's end were loaded as copies of its
                 // first row (issue_tile), so their values repeat that token's
                 // under a later index: they change no maximum, and with the
@@ -677,9 +689,9 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         });
     };
 
-    auto compute_tile = [&](int bf, int tt, int ln) {
+    auto compute_tile = [&](int bf, int tt, int ln, bool last_tile) {
         if constexpr ((!I8 && M == 32 && QB <= 2) || I8) {  // two stages of accumulators fit in registers
-            compute_tile_pipe(bf, tt, ln);
+            compute_tile_pipe(bf, tt, ln, last_tile);
             return;
         }
         if (wq * QB * M >= nrows) return;  // uniform: this wave's rows are all past the slab
@@ -963,7 +975,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             }
         }
         if (!has0) break;  // nothing issued or pending past here (has0 false => hasn false)
-        if (cs[0].t < cs[0].ntiles) compute_tile(buf, cs[0].t, cs[0].len);
+        if (cs[0].t < cs[0].ntiles) compute_tile(buf, cs[0].t, cs[0].len, cs[0].t + 1 >= cs[0].ntiles);
         if (cs[0].t + 1 >= cs[0].ntiles) {
             epilogue_merge(par, cs[0].b);
             pend = cs[0].b;
@@ -1004,6 +1016,7 @@ __global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
     constexpr int KS = MM::KS, VPL = MM::VPL, FPS = VPL / KS;
     constexpr int LPW = TT * NCH / NT;  // 1 KB direct loads per wave per tile
     static_assert(LPW * NT == TT * NCH, "tile must split into whole 1 KB loads per wave");
+    static_assert(SPW % 2 == 0, "a carried sub-tile sits in acc1");
     constexpr int DCAP = 4096;  // document ends kept in LDS
     __shared__ u32x4 dtile[2][TT * NCH];
     __shared__ int dend_s[DCAP];
@@ -1161,6 +1174,7 @@ __global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
     lds_barrier();  // also publishes dend_s
     if (b < bend) dend = doc_end(b);
     Acc acc0[QB], acc1[QB];
+    bool carry = false;  // acc1 holds the unfolded last sub-tile of the previous tile
     for (int k = 0; k < ntile; ++k) {
         const int bf = k & 1;
         // tile k+1 goes into the buffer step k-1 read (tile 1 came with the prologue)
@@ -1168,16 +1182,25 @@ __global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
         const int64_t tb = T0 + (int64_t)k * TT;
         const int64_t left = T1 - tb;
         const int nsub = left >= TT ? SPW : (int)((left + M - 1) / M);
+        const bool carried = carry;
+        carry = false;
         static_for<SPW>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             if (j >= nsub) return;  // uniform
             Acc* cur = (j & 1) ? acc1 : acc0;
             const Acc* prev = (j & 1) ? acc0 : acc1;
-            const int64_t tprev = tb + (int64_t)(j - 1) * M;
-            const bool whole = j > 0 && b < bend && dend - tprev >= M;  // previous sub-tile inside document b
+            const int64_t tprev = tb + (int64_t)(j - 1) * M;  // (for j = 0: the previous tile's last sub-tile)
+            const bool has_prev = j > 0 || carried;
+            const bool whole = has_prev && b < bend && dend - tprev >= M;  // previous sub-tile inside document b
             stage(bf, j, cur, prev, whole);
-            if (j > 0 && !whole) fold_sub(prev, tprev);
-            if (j == nsub - 1) fold_sub(cur, tb + (int64_t)j * M);
+            if (has_prev && !whole) fold_sub(prev, tprev);
+            if (j == nsub - 1) {
+                if (j == SPW - 1 && k + 1 < ntile) {
+                    carry = true;  // folded between the next step's first MFMAs (SPW is even: it sits in acc1)
+                } else {
+                    fold_sub(cur, tb + (int64_t)j * M);
+                }
+            }
         });
         if (k + 1 < ntile) wait_vmcnt<0>();  // tile k+1 has landed (and this step's stores retired)
         lds_barrier();
