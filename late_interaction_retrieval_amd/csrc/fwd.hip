@@ -409,17 +409,30 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         code[cb] = -1;
     }
 
-    // Direct HBM -> LDS loads of one tile into ring slot bf.  Every wave issues
-    // exactly LPW (+1 for the scale waves) loads, so vmcnt bookkeeping is
+    // Direct HBM -> LDS loads of one tile into ring slot bf.  Every loading
+    // wave issues exactly LPL (+1 for the scale waves) loads, so vmcnt bookkeeping is
     // static; lanes whose token is past the document's end fetch the
     // document's first row instead (in bounds, and a repeat of a value the
     // maximum already sees), and the compute masks those tokens where needed.
     const bool scale_wave = I8 && wave < SCW;
+    // With two buffers the tile is loaded by the first wave of each SIMD
+    // (waves 0 .. NW/2-1, each twice the even share), and the second wave
+    // issues none: issuing a tile's direct loads stalls a wave for about 1000
+    // cycles, and when both waves of a SIMD stalled together the matrix pipe
+    // stood idle.  The step barrier orders the tile for the waves that read it
+    // without having loaded it.
+    constexpr bool SPLIT_LOADS = NBUF == 2 && NW == 8;
+    constexpr int LW = SPLIT_LOADS ? NW / 2 : NW;  // loading waves
+    constexpr int LPL = TT * NCH / (64 * LW);      // 1 KB loads per loading wave per tile
+    static_assert(LPL * 64 * LW == TT * NCH, "tile must split into whole 1 KB loads per loading wave");
+    static_assert(!I8 || SCW <= LW, "the scale waves are loading waves");
+    const bool loader = wave < LW;
     auto issue_tile = [&](int bf, int64_t st, int ln, int tt) {
         const int64_t safe = ln > 0 ? st : 0;
+        if (!loader) return;  // uniform
 #pragma unroll
-        for (int u = 0; u < LPW; ++u) {
-            const int slot0 = (u * NW + wave) * 64;
+        for (int u = 0; u < LPL; ++u) {
+            const int slot0 = (u * LW + wave) * 64;
             const int sl = slot0 + lane;
             const int row = sl / NCH;
             const int c = swz_chunk<NCH>(row, sl % NCH);
@@ -442,9 +455,9 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         if constexpr (NBUF == 2) {
             wait_vmcnt<0>();
         } else if (scale_wave) {
-            wait_vmcnt<LPW + 1>();
+            wait_vmcnt<LPL + 1>();
         } else {
-            wait_vmcnt<LPW>();
+            wait_vmcnt<LPL>();
         }
     };
 
@@ -944,9 +957,11 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         // when the stream ends earlier, fewer were issued: wait for all
         if (cs[NBUF - 1].b < bend) {
             if (scale_wave) {
-                wait_vmcnt<(NBUF - 1) * (LPW + 1)>();
+                wait_vmcnt<(NBUF - 1) * (LPL + 1)>();
+            } else if (loader) {
+                wait_vmcnt<(NBUF - 1) * LPL>();
             } else {
-                wait_vmcnt<(NBUF - 1) * LPW>();
+                wait_vmcnt<0>();
             }
         } else {
             wait_vmcnt<0>();
@@ -1056,13 +1071,17 @@ __global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
     T1 = T1 < T0 ? T0 : T1;
     const int ntile = (int)((T1 - T0 + TT - 1) / TT);
 
-    // Tile k: tokens T0 + k*TT ... (past T1: the tile's first row again, in bounds, never folded)
+    // Tile k: tokens T0 + k*TT ... (past T1: the tile's first row again, in bounds, never folded).
+    // Loaded by the first wave of each SIMD, as in fwd_kernel.
+    constexpr int LW = NW / 2, LPL = 2 * LPW;
+    const bool loader = wave < LW;
     auto issue_tile = [&](int bf, int k) {
         const int64_t st = T0 + (int64_t)k * TT;
         const int64_t ln = T1 - st;
+        if (!loader) return;  // uniform
 #pragma unroll
-        for (int u = 0; u < LPW; ++u) {
-            const int slot0 = (u * NW + wave) * 64;
+        for (int u = 0; u < LPL; ++u) {
+            const int slot0 = (u * LW + wave) * 64;
             const int sl = slot0 + lane;
             const int row = sl / NCH;
             const int c = swz_chunk<NCH>(row, sl % NCH);
@@ -1167,7 +1186,11 @@ __global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
     if (ntile > 0) issue_tile(0, 0);
     if (ntile > 1) {
         issue_tile(1, 1);
-        wait_vmcnt<LPW>();  // tile 0 has landed; tile 1 may be in flight
+        if (loader) {
+            wait_vmcnt<LPL>();  // tile 0 has landed; tile 1 may be in flight
+        } else {
+            wait_vmcnt<0>();
+        }
     } else {
         wait_vmcnt<0>();
     }
