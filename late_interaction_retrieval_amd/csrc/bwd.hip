@@ -363,13 +363,53 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
     const int64_t nrows = VARLEN ? p.T : (int64_t)p.B * p.Ld;
     const int BLq = p.B * p.Lq;
     const int nsrc = p.Nq * BLq;  // col_idx capacity
+    const int gshift = threadIdx.x & 48;  // this group's first lane in the wave
+    // Packed corpus: a row's source count is about Nq*Lq over its document's
+    // length, so rows of short documents carry several times the sources of
+    // long ones, and rows dealt out by index left the groups holding short
+    // documents' rows running about twice as long as the mean.  There each
+    // group takes the contiguous rows whose first source lies in its share
+    // gid*S/G .. (gid+1)*S/G of the S sources (a 16-lane search over row_ptr,
+    // which is non-decreasing), and walks them kRowsPerGroup at a time.
+    // Every row still belongs to exactly one group and sums its sources in the
+    // same order, so the result is unchanged.
+    int64_t rb = 0, rend = 1;
+    if constexpr (VARLEN) {
+        int64_t S = p.row_ptr[nrows];
+        S = S < 0 ? 0 : (S > nsrc ? nsrc : S);
+        auto lower_bound16 = [&](int64_t x) -> int64_t {  // first row with row_ptr[row] >= x, in [0, nrows]
+            int64_t lo = 0, hi = nrows;
+            while (lo < hi) {  // uniform per 16-lane group
+                const int64_t step = (hi - lo) / 16 + 1;  // (hi - lo) / step < 16
+                const int64_t i = lo + (int64_t)l16 * step;
+                const bool below = i <= hi && p.row_ptr[i] < x;
+                const int c = __popcll((__ballot(below) >> gshift) & 0xffffull);
+                if (c == 0) {
+                    hi = lo;
+                } else {
+                    const int64_t up = lo + (int64_t)c * step;
+                    hi = up < hi ? up : hi;
+                    lo = lo + (int64_t)(c - 1) * step + 1;
+                    lo = lo < hi ? lo : hi;
+                }
+            }
+            return lo;
+        };
+        rb = gid == 0 ? 0 : lower_bound16(gid * S / ngroups);
+        rend = gid + 1 >= ngroups ? nrows : lower_bound16((gid + 1) * S / ngroups);
+        rend = rend < rb ? rb : rend;
+    }
+    for (; rb < rend; rb += VARLEN ? kRowsPerGroup : 1) {  // uniform per 16-lane group
+    // rows of this pass: packed, rb + k (< rend); padded, gid + k * ngroups
+    auto row_of = [&](int k) -> int64_t { return VARLEN ? rb + k : gid + k * ngroups; };
+    auto row_ok = [&](int k, int64_t row) { return VARLEN ? row < rend : (k < rows_per_group && row < nrows); };
     int cur[kRowsPerGroup], end[kRowsPerGroup], bdoc[kRowsPerGroup];
     bool heavy[kRowsPerGroup];
     float acc[kRowsPerGroup][8];
 #pragma unroll
     for (int k = 0; k < kRowsPerGroup; ++k) {
-        const int64_t row = gid + k * ngroups;
-        const bool ok = k < rows_per_group && row < nrows;
+        const int64_t row = row_of(k);
+        const bool ok = row_ok(k, row);
         cur[k] = ok ? p.row_ptr[row] : 0;
         end[k] = ok ? p.row_ptr[row + 1] : 0;
         if constexpr (VARLEN) {
@@ -390,7 +430,6 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
     }
-    const int gshift = threadIdx.x & 48;  // this group's first lane in the wave
     for (int q0 = 0; q0 < p.Nq; q0 += kQueryWindow) {
         const int qend = q0 + kQueryWindow;
         bool more = true;
@@ -447,8 +486,9 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
     }
 #pragma unroll
     for (int k = 0; k < kRowsPerGroup; ++k) {
-        const int64_t row = gid + k * ngroups;
-        if (k < rows_per_group && row < nrows && !heavy[k]) store8(p.dD + row * 128 + l16 * 8, acc[k]);
+        const int64_t row = row_of(k);
+        if (row_ok(k, row) && !heavy[k]) store8(p.dD + row * 128 + l16 * 8, acc[k]);
+    }
     }
 }
 
@@ -765,6 +805,8 @@ hipError_t launch_bwd_elem(const BwdParams& p, hipStream_t stream) {
     const int64_t nrows = VARLEN ? p.T : (int64_t)p.B * p.Ld;
     if (nrows > 0) {
         gather_grid(nrows, &blocks, &rpg);
+        // packed: the groups split the sources evenly, so the full grid serves any row count
+        if (VARLEN) blocks = kGatherBlocks;
         hipLaunchKernelGGL((dd_owner<ELEM, VARLEN>), dim3(blocks), dim3(kGatherThreads), 0, stream, p, rpg);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const unsigned hb = (unsigned)std::min<int64_t>(p.max_heavy, kGatherBlocks);
