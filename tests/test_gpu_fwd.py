@@ -174,6 +174,34 @@ def test_first_token_max_ragged_tails(bd, dtn):
     assert np.all(a == 0)
 
 
+def test_many_documents_per_stream(bd):
+    """64 queries x 32 tokens over 300000 documents of 0..2 tokens: about 4700
+    documents per stream, more than the scores-only kernel keeps in LDS, so it
+    reads document ends from memory.  Scores-only equals the argmax launch bit
+    for bit; a seeded sample of documents is checked against the oracle."""
+    Nq, Lq, B = 64, 32, 300000
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, 3, size=B).astype(np.int32)
+    cu = inputs.cu_seqlens(lens)
+    Q = inputs.random_rows(78, Nq * Lq, 128, inputs.F16).reshape(Nq, Lq, 128)
+    Dp = inputs.random_rows(79, int(cu[-1]), 128, inputs.F16, stream=4)
+    Qd, Dd, cud = to_dev(Q, inputs.F16), to_dev(Dp, inputs.F16), to_dev(cu)
+    scores = torch.full((Nq, B), float("nan"), dtype=torch.float32, device=DEV)
+    s0, _ = bd.maxsim_fwd_varlen(Qd, Dd, cud, 2, scores=scores, with_argmax=False)
+    s1, a1 = bd.maxsim_fwd_varlen(Qd, Dd, cud, 2)
+    torch.cuda.synchronize()
+    s0, s1, a1 = s0.cpu().numpy(), s1.cpu().numpy(), a1.cpu().numpy()
+    assert not np.isnan(s0).any()
+    assert np.array_equal(s0, s1)
+    docs = np.sort(rng.choice(B, size=2000, replace=False))
+    docs[0], docs[-1] = 0, B - 1
+    sub, subcu = sub_corpus(Dp, cu, docs)
+    s_ref, a_ref, m_ref = oracle.fwd_varlen(Q, sub, subcu, oracle.F16, want_rowmax=True)
+    check_scores(s0[:, docs], s_ref, Lq, "many documents per stream")
+    check_argmax(a1[:, docs], a_ref, m_ref, oracle.sim_at(Q, sub, subcu, oracle.F16, a1[:, docs]), np.diff(subcu),
+                 "many documents per stream")
+
+
 def test_padding_never_selected_all_negative(bd):
     """All valid similarities negative, padding rows huge: padding is never picked."""
     Q = np.full((2, 40, 128), 0.05, np.float16)
