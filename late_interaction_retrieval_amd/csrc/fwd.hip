@@ -603,6 +603,11 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         float kt[QB];
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb) kt[cb] = -INFINITY;
+        // Raised issue priority while the stage's MFMA / fold interleave runs:
+        // the other wave of the SIMD, in its epilogue, boundary folds or load
+        // issue, then takes the slots the matrix pipe leaves (INT8 -4 %,
+        // others 0.5-1 %).
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -618,6 +623,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         if constexpr (KEYED) {
             if (has_prev) {
 #pragma unroll
@@ -1169,6 +1175,7 @@ __global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
         for (int s = 0; s < KS; ++s) a[s] = dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb) cur[cb] = MM::zero();
+        __builtin_amdgcn_s_setprio(1);  // as in fwd_kernel's stage
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -1181,6 +1188,7 @@ __global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     if (ntile > 0) issue_tile(0, 0);
