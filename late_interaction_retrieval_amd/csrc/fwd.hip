@@ -1423,6 +1423,12 @@ __global__ __launch_bounds__(64 * W) void fwd_tiny_kernel(FwdParams p) {
     int idx;
     rows_vs_doc<ELEM, W, SPL>(p, p.Q, nrows, st, len, q_s, rowmax_s, rowarg_s, mv, idx);
     if (wave != 0) return;
+    if (p.Nq == 1) {  // uniform: one query, its rows in lanes 0 .. Lq-1 -> DPP sum, no LDS round trip
+        if (ARGMAX && lane < nrows) p.argmax[(int64_t)b * p.Lq + lane] = idx;
+        const float sc = lanes32_sum(lane < nrows ? mv : 0.f);
+        if (lane == 31) p.scores[b] = sc;
+        return;
+    }
     if (lane < nrows) rowmax_s[0][lane] = mv;  // only this wave reads it from here on
     __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): the row maxima are in LDS
     __builtin_amdgcn_wave_barrier();
