@@ -32,9 +32,14 @@
  *   - Query-token count Lq is limited to 1 <= Lq <= 1024.
  *   - A document with no valid token scores -inf and every argmax entry of
  *     it is -1 (the running maximum starts at -inf, Section 4.1).
- *   - Argmax indices are local to the document ([0, length)) and, where
- *     several tokens attain the maximum, point at one of them (the INT8 path
- *     always at the first).
+ *   - Argmax indices are local to the document ([0, length)).  The INT8
+ *     path returns exactly the first token attaining the maximum.  The
+ *     fp16/bf16 paths return a token whose fp32 similarity is within 16 ulp
+ *     of the row maximum (for 32x32 MFMA blocks candidates are ranked by the
+ *     similarity with its low 4 mantissa bits replaced by the token's slot,
+ *     which orders values closer than that by slot, and for negative values
+ *     in the reverse slot order); the score itself always uses the exact
+ *     fp32 maximum.
  */
 #ifndef MAXSIM_H
 #define MAXSIM_H
@@ -275,7 +280,9 @@ size_t maxsim_chamfer_bwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M);
  *   row_ptr_q [Bt*M + 1], col_idx_q [Bt*N]: the same for the Q points.
  *   Entries past row_ptr[last] (sources with idx -1) are unspecified.
  * Selections of -1 add nothing.  workspace: maxsim_chamfer_bwd_workspace_bytes()
- * bytes, 256-byte aligned.  Requirements as maxsim_chamfer_fwd.
+ * bytes, 256-byte aligned.  Requirements as maxsim_chamfer_fwd, and also
+ * Bt*(N+M) < 2^31 (both directions' selections are sorted together with
+ * int32 offsets); MAXSIM_ERR_SHAPE otherwise.
  */
 int maxsim_chamfer_bwd(const float* P, const float* Q, const int32_t* idx_p, const int32_t* idx_q,
                        const float* grad_p, const float* grad_q, int32_t Bt, int32_t N, int32_t M, float* dP,

@@ -487,7 +487,13 @@ class ChamferFunction(torch.autograd.Function):
 
 def chamfer_distance(P, Q):
     """The page's Chamfer distance per batch item, mean_p min_q |p-q|^2 +
-    mean_q min_p |q-p|^2, for P [Bt, N, 3] and Q [Bt, M, 3] fp32, with autograd."""
+    mean_q min_p |q-p|^2, for P [Bt, N, 3] and Q [Bt, M, 3] fp32, with autograd.
+
+    Caller-side convenience, not a library operation: the nearest-neighbour
+    distances and their gradients come from maxsim_chamfer_fwd and
+    maxsim_chamfer_bwd; the mean over points that turns them into the loss
+    is a torch reduction here (its backward hands the per-point weights 1/N
+    and 1/M to maxsim_chamfer_bwd)."""
     dist_p, dist_q = ChamferFunction.apply(P, Q)
     return dist_p.mean(dim=-1) + dist_q.mean(dim=-1)
 

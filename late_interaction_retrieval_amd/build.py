@@ -33,10 +33,6 @@ def hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-PROBE_LIB = os.path.join(HERE, "libmaxsim_probe.so")
-PROBE_SOURCES = ["probe.hip"]
-
-
 def _compile(sources, lib, verbose, extra):
     tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + [
@@ -56,8 +52,7 @@ def _compile(sources, lib, verbose, extra):
 
 
 def build(verbose=False, extra=()):
-    """Build libmaxsim.so and the measurement aid libmaxsim_probe.so."""
-    _compile(PROBE_SOURCES, PROBE_LIB, verbose, extra)
+    """Build libmaxsim.so."""
     return _compile(SOURCES, LIB, verbose, extra)
 
 

@@ -296,6 +296,14 @@ int check_chamfer(int32_t Bt, int32_t N, int32_t M) {
     if ((int64_t)Bt * N >= ((int64_t)1 << 31) || (int64_t)Bt * M >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
     return MAXSIM_OK;
 }
+// The backward sorts both directions' selections together: Bt*(N+M) elements
+// with int32 offsets.
+int check_chamfer_bwd(int32_t Bt, int32_t N, int32_t M) {
+    const int st = check_chamfer(Bt, N, M);
+    if (st != MAXSIM_OK) return st;
+    if ((int64_t)Bt * ((int64_t)N + M) >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
+    return MAXSIM_OK;
+}
 }  // namespace
 
 size_t maxsim_chamfer_fwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M) {
@@ -330,7 +338,7 @@ int maxsim_chamfer_fwd(const float* P, const float* Q, int32_t Bt, int32_t N, in
 }
 
 size_t maxsim_chamfer_bwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M) {
-    if (check_chamfer(Bt, N, M) != MAXSIM_OK) return 0;
+    if (check_chamfer_bwd(Bt, N, M) != MAXSIM_OK) return 0;
     return maxsim::chamfer_bwd_workspace_bytes(Bt, N, M);
 }
 
@@ -338,7 +346,7 @@ int maxsim_chamfer_bwd(const float* P, const float* Q, const int32_t* idx_p, con
                        const float* grad_p, const float* grad_q, int32_t Bt, int32_t N, int32_t M, float* dP,
                        float* dQ, int32_t* row_ptr_p, int32_t* col_idx_p, int32_t* row_ptr_q, int32_t* col_idx_q,
                        void* workspace, size_t workspace_bytes, void* stream) {
-    int st = check_chamfer(Bt, N, M);
+    int st = check_chamfer_bwd(Bt, N, M);
     if (st != MAXSIM_OK) return st;
     if (Bt == 0) return MAXSIM_OK;
     if (!workspace || !row_ptr_p || !row_ptr_q) return MAXSIM_ERR_NULL;

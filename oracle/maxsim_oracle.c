@@ -285,8 +285,12 @@ int oracle_fwd_i8(const int8_t* Q, const float* q_scale, const int8_t* D, const 
  *              length B*Ld + 1, row_ptr[0] = 0,
  *   col_idx  = stable argsort of dst: within each row the sources appear in
  *              ascending s.
+ * A negative argmax entry is what the forward writes for a document with no
+ * valid token (d_lens[b] = 0: the running maximum never leaves -inf, Section
+ * 4.1 "Online-Max Recurrence"); such a source selects no row and appears in
+ * no bucket, so row_ptr[B*Ld] is the number of sources with argmax >= 0.
  * The stable argsort is written as a counting sort that visits s in
- * ascending order.  Returns 0, or -1 if some argmax is out of [0, Ld).
+ * ascending order.  Returns 0, or -1 if some argmax is >= Ld.
  */
 int oracle_csr_build(const int32_t* argmax, int Nq, int B, int Lq, int Ld, int32_t* row_ptr,
                      int32_t* col_idx) {
@@ -296,7 +300,8 @@ int oracle_csr_build(const int32_t* argmax, int Nq, int B, int Lq, int Ld, int32
     for (int64_t s = 0; s < nsrc; ++s) {
         int64_t b = (s / Lq) % B;
         int32_t t = argmax[s];
-        if (t < 0 || t >= Ld) {
+        if (t < 0) continue; /* selects no row */
+        if (t >= Ld) {
             free(cnt);
             return -1;
         }
@@ -306,8 +311,9 @@ int oracle_csr_build(const int32_t* argmax, int Nq, int B, int Lq, int Ld, int32
     for (int64_t r = 0; r < ndst; ++r) row_ptr[r + 1] = (int32_t)(row_ptr[r] + cnt[r]);
     int64_t* cursor = cnt; /* reuse: next free slot of every row */
     for (int64_t r = 0; r < ndst; ++r) cursor[r] = row_ptr[r];
-    for (int64_t s = 0; s < nsrc; ++s) {
+    for (int64_t s = 0; s < nsrc; ++s) { /* ascending s: a stable fill */
         int64_t b = (s / Lq) % B;
+        if (argmax[s] < 0) continue;
         int64_t dst = b * Ld + argmax[s];
         col_idx[cursor[dst]] = (int32_t)s;
         cursor[dst] += 1;
@@ -323,13 +329,16 @@ int oracle_csr_build(const int32_t* argmax, int Nq, int B, int Lq, int Ld, int32
  *   dD[b, t, :] = sum over (q, i) with t*(q, b, i) = t of g[q, b] * Q[q, i, :]
  * Written as the plain definition: one pass over every (q, b, i), adding to
  * the selected rows, in fp64.  Rows of dD that no query token selects stay
- * exactly zero.  Q [Nq, Lq, d], D [B, Ld, d] (fp16 / bf16), argmax
- * [Nq, B, Lq], g [Nq, B] fp32.  Outputs dQ [Nq, Lq, d], dD [B, Ld, d] fp64.
+ * exactly zero.  A source whose argmax is negative (a document with no valid
+ * token) selects no row and adds nothing, as in oracle_csr_build.
+ * Q [Nq, Lq, d], D [B, Ld, d] (fp16 / bf16), argmax [Nq, B, Lq], g [Nq, B]
+ * fp32.  Outputs dQ [Nq, Lq, d], dD [B, Ld, d] fp64.  Returns -1 if some
+ * argmax is >= Ld.
  */
 int oracle_bwd(const uint16_t* Q, const uint16_t* D, int dtype, const int32_t* argmax,
                const float* g, int Nq, int Lq, int B, int Ld, int d, double* dQ, double* dD) {
     for (int64_t s = 0; s < (int64_t)Nq * B * Lq; ++s)
-        if (argmax[s] < 0 || argmax[s] >= Ld) return -1;
+        if (argmax[s] >= Ld) return -1;
     memset(dQ, 0, sizeof(double) * (size_t)Nq * Lq * d);
     memset(dD, 0, sizeof(double) * (size_t)B * Ld * d);
     for (int q = 0; q < Nq; ++q) {
@@ -337,6 +346,7 @@ int oracle_bwd(const uint16_t* Q, const uint16_t* D, int dtype, const int32_t* a
             double gqb = (double)g[(int64_t)q * B + b];
             for (int i = 0; i < Lq; ++i) {
                 int t = argmax[((int64_t)q * B + b) * Lq + i];
+                if (t < 0) continue;
                 const uint16_t* qrow = Q + ((int64_t)q * Lq + i) * d;
                 const uint16_t* drow = D + ((int64_t)b * Ld + t) * d;
                 double* dq = dQ + ((int64_t)q * Lq + i) * d;

@@ -168,13 +168,16 @@ def sim_at(Q, D_packed, cu_seqlens, dtype, sel):
 
 
 def csr_build(argmax, Ld):
-    """argmax [Nq, B, Lq] -> (row_ptr int32 [B*Ld+1], col_idx int32 [Nq*B*Lq])."""
+    """argmax [Nq, B, Lq] -> (row_ptr int32 [B*Ld+1], col_idx int32 [row_ptr[-1]]).
+
+    Negative entries (an empty document) select no row, so col_idx holds
+    Nq*B*Lq entries only when every argmax is >= 0."""
     A = np.ascontiguousarray(argmax, dtype=np.int32)
     Nq, B, Lq = A.shape
     row_ptr = np.empty(B * Ld + 1, np.int32)
     col_idx = np.empty(Nq * B * Lq, np.int32)
     _check(_load().oracle_csr_build(_p(A), Nq, B, Lq, Ld, _p(row_ptr), _p(col_idx)), "csr_build")
-    return row_ptr, col_idx
+    return row_ptr, col_idx[:row_ptr[-1]]
 
 
 def bwd(Q, D, dtype, argmax, g):

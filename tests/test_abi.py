@@ -159,50 +159,6 @@ def test_status_strings():
     assert "unknown" in L.maxsim_status_string(99).decode()
 
 
-PROBE_HEADER = os.path.join(ROOT, "include", "maxsim_probe.h")
-PROBE_LIB = os.path.join(ROOT, "late_interaction_retrieval_amd", "libmaxsim_probe.so")
-
-
-def test_probe_library_exports_and_validation():
-    """The measurement aid: every function maxsim_probe.h declares is exported;
-    invalid arguments are rejected before any launch."""
-    if not os.path.exists(PROBE_LIB):
-        from late_interaction_retrieval_amd import build
-        build.build()
-    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
-    names = set(re.findall(r"\b(maxsim_probe_\w+)\s*\(", text))
-    assert names == {"maxsim_probe_operand_bytes", "maxsim_probe_ops_per_launch", "maxsim_probe_mfma",
-                     "maxsim_probe_valu_lane_ops_per_launch", "maxsim_probe_valu", "maxsim_probe_read"}
-    pl = ctypes.CDLL(PROBE_LIB)
-    for n in names:
-        assert hasattr(pl, n), n
-    pl.maxsim_probe_operand_bytes.restype = ctypes.c_size_t
-    pl.maxsim_probe_operand_bytes.argtypes = [ctypes.c_int32]
-    assert pl.maxsim_probe_operand_bytes(0) == 0
-    assert pl.maxsim_probe_operand_bytes(2) == 2 * 8 * 64 * 12 * 16
-    pl.maxsim_probe_ops_per_launch.restype = ctypes.c_double
-    pl.maxsim_probe_ops_per_launch.argtypes = [ctypes.c_int32] * 3
-    assert pl.maxsim_probe_ops_per_launch(0, 1, 1) == 8 * 8 * 4 * 32768.0
-    pl.maxsim_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                     ctypes.c_void_p, ctypes.c_void_p]
-    assert pl.maxsim_probe_mfma(0, None, 1, 1, A, None) == 1
-    assert pl.maxsim_probe_mfma(0, A, 0, 1, A, None) == 2
-    assert pl.maxsim_probe_mfma(0, A, 1, 0, A, None) == 2
-    assert pl.maxsim_probe_mfma(7, A, 1, 1, A, None) == 3
-    pl.maxsim_probe_valu_lane_ops_per_launch.restype = ctypes.c_double
-    pl.maxsim_probe_valu_lane_ops_per_launch.argtypes = [ctypes.c_int32] * 2
-    assert pl.maxsim_probe_valu_lane_ops_per_launch(2, 3) == 2 * 512 * 3 * 8 * 8
-    pl.maxsim_probe_valu.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                     ctypes.c_void_p]
-    assert pl.maxsim_probe_valu(None, 1, 1, A, None) == 1
-    assert pl.maxsim_probe_valu(A, 0, 1, A, None) == 2
-    pl.maxsim_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
-                                     ctypes.c_void_p]
-    assert pl.maxsim_probe_read(None, 1024, 1, A, None) == 1
-    assert pl.maxsim_probe_read(A, 1000, 1, A, None) == 2
-    assert pl.maxsim_probe_read(A, 1024, 0, A, None) == 2
-
-
 def test_pairs_topk_two_stage_validation():
     ok, NULL, SHAPE, UNSUP, ALIGN, WS = (bd.MAXSIM_OK, bd.MAXSIM_ERR_NULL, bd.MAXSIM_ERR_SHAPE,
                                          bd.MAXSIM_ERR_UNSUPPORTED, bd.MAXSIM_ERR_ALIGN, bd.MAXSIM_ERR_WORKSPACE)
@@ -378,6 +334,12 @@ def test_chamfer_validation():
         ("dP", A), ("dQ", A), ("rpp", A), ("cip", A), ("rpq", A), ("ciq", A), ("ws", A), ("wsb", big),
         ("stream", None))])
     assert bwd_(N=-1) == bd.MAXSIM_ERR_SHAPE
+    # both directions are sorted together: Bt*(N+M) must stay below 2^31
+    # even when Bt*N and Bt*M each do (the forward accepts these sizes)
+    assert bwd_(Bt=1, N=(1 << 31) - 10, M=20) == bd.MAXSIM_ERR_SHAPE
+    assert bwd_(Bt=2, N=(1 << 30) - 1, M=2) == bd.MAXSIM_ERR_SHAPE
+    assert L.maxsim_chamfer_bwd_workspace_bytes(1, (1 << 31) - 10, 20) == 0
+    assert fwd(Bt=1, N=(1 << 31) - 10, M=20, wsb=big) != bd.MAXSIM_ERR_SHAPE
     assert bwd_(gq=None) == bd.MAXSIM_ERR_NULL
     assert bwd_(rpq=None) == bd.MAXSIM_ERR_NULL
     assert bwd_(cip=None) == bd.MAXSIM_ERR_NULL

@@ -31,3 +31,27 @@ def test_workloads_have_inputs():
     for name in inputs.CHAMFER_WORKLOADS:
         w = inputs.make_chamfer(name, Bt=2, N=16, M=8)
         assert w["P"].shape == (2, 16, 3) and w["Q"].shape == (2, 8, 3)
+
+
+def test_default_line_is_the_colpali_headline_with_every_config():
+    sys.path.insert(0, ROOT)
+    import bench
+    old = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        assert bench.parse().workload == "all"
+    finally:
+        sys.argv = old
+    assert bench.HEADLINE == "colpali_fwd"
+    assert set(bench.ALL_CONFIGS) == {"colbert_tiny", "colbert_rerank_varlen", "colbert_rerank_padded",
+                                      "colpali_fwd", "contrastive_train", "int8_varlen"}
+
+
+def test_cpu_baseline_names_the_host():
+    sys.path.insert(0, ROOT)
+    import bench
+    from late_interaction_retrieval_amd import inputs
+    w = inputs.make("colbert_rerank_varlen", B=3, Nq=2)
+    c = bench.cpu_baseline(w, 0.01)
+    assert c["kind"] == "oracle" and c["cores"] >= 1 and c["nproc"] >= 1
+    assert "cpu_model" in c and c["value"] > 0 and "documents" in c["sample"]

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from late_interaction_retrieval_amd import inputs
-from gpu_util import GRAD_REL_TOL, infonce_grad, oracle_dtype, pad_width, rel_fro, to_dev
+from gpu_util import GRAD_REL_TOL, check_grad, infonce_grad, oracle_dtype, pad_width, rel_fro, to_dev
 
 pytestmark = pytest.mark.gpu
 GOLD = os.path.join(os.path.dirname(__file__), "golden", "maxsim_hand.json")
@@ -38,16 +38,15 @@ def check_bwd(bd, Q, D, dtn, A, g, where):
     Ld = D.shape[1]
     rp_ref, ci_ref = oracle.csr_build(A, Ld)
     assert np.array_equal(rp, rp_ref), where + ": row_ptr"
-    assert np.array_equal(ci, ci_ref), where + ": col_idx"
+    assert np.array_equal(ci[:rp_ref[-1]], ci_ref), where + ": col_idx"
     dQ_ref, dD_ref = oracle.bwd(Q, D, oracle_dtype(dtn), A, g)
-    eq, ed = rel_fro(dQ, dQ_ref), rel_fro(dD, dD_ref)
-    assert eq <= GRAD_REL_TOL and ed <= GRAD_REL_TOL, "%s: rel err dQ %.3g dD %.3g" % (where, eq, ed)
+    rq, rd = check_grad(dQ, dQ_ref, "dQ", where), check_grad(dD, dD_ref, "dD", where)
     empty_rows = np.diff(rp_ref).reshape(D.shape[0], Ld) == 0
     assert np.all(dD[empty_rows] == 0.0), where + ": rows without sources must be exactly 0"
     # second call: bit-identical (deterministic, atomic-free)
     dQ2, dD2, rp2, ci2 = run_bwd(bd, Q, D, dtn, A, g)
-    assert np.array_equal(dQ, dQ2) and np.array_equal(dD, dD2) and np.array_equal(ci, ci2)
-    print("%s: rel err dQ %.2e dD %.2e" % (where, eq, ed), flush=True)
+    assert np.array_equal(dQ, dQ2) and np.array_equal(dD, dD2) and np.array_equal(ci[:rp[-1]], ci2[:rp[-1]])
+    print("%s: %s; %s" % (where, rq, rd), flush=True)
 
 
 def test_golden_hand_case(bd):
@@ -110,22 +109,43 @@ def test_workload_contrastive_train_full(bd):
     check_bwd(bd, w["Q"], D, inputs.BF16, A, g, "contrastive_train")
 
 
-def test_workload_contrastive_forward_sampled(bd):
-    """Forward of the training workload: all 4096 pairs on the GPU, a sample of
-    (query, document) pairs through the oracle."""
-    from gpu_util import check_argmax, check_scores
+@pytest.fixture(scope="module")
+def train_ref():
+    """The training workload (64 x 64 pairs, Lq = Ld = 1024, bf16) and the
+    oracle's forward over all 4096 pairs (about 10 s on 16 host threads)."""
     w = inputs.make("contrastive_train")
+    D = w["D_packed"].reshape(w["B"], w["Ld_max"], 128)
+    s_ref, a_ref, m_ref = oracle.fwd_padded(w["Q"], D, oracle.BF16, want_rowmax=True)
+    return w, D, s_ref, a_ref, m_ref
+
+
+def test_workload_contrastive_forward_full(bd, train_ref):
+    """Forward of the training workload: every one of the 4096 pairs against
+    the oracle (scores within 1e-3 * Lq, argmax equal or a near-tie)."""
+    from gpu_util import check_argmax, check_scores
+    w, D, s_ref, a_ref, m_ref = train_ref
     Nq, Lq, B, Ld = w["Nq"], w["Lq"], w["B"], w["Ld_max"]
-    D = w["D_packed"].reshape(B, Ld, 128)
     s, a = bd.maxsim_fwd(to_dev(w["Q"], inputs.BF16), to_dev(D, inputs.BF16))
+    torch.cuda.synchronize()
     s, a = s.cpu().numpy(), a.cpu().numpy()
-    qs, bs = [0, 17, 63], [0, 40, 63]
-    for q in qs:
-        s_ref, a_ref, m_ref = oracle.fwd_padded(w["Q"][q:q + 1], D[bs], oracle.BF16, want_rowmax=True)
-        check_scores(s[q:q + 1, bs], s_ref, Lq, "train fwd q%d" % q)
-        cu = inputs.cu_seqlens(np.full(len(bs), Ld, np.int32))
-        sim = oracle.sim_at(w["Q"][q:q + 1], D[bs].reshape(-1, 128), cu, oracle.BF16, a[q:q + 1, bs])
-        check_argmax(a[q:q + 1, bs], a_ref, m_ref, sim, np.full(len(bs), Ld), "train fwd q%d" % q)
+    err = check_scores(s, s_ref, Lq, "train fwd")
+    cu = inputs.cu_seqlens(np.full(B, Ld, np.int32))
+    sim = oracle.sim_at(w["Q"], w["D_packed"], cu, oracle.BF16, a)
+    flips = check_argmax(a, a_ref, m_ref, sim, np.full(B, Ld), "train fwd")
+    print("contrastive_train forward: 4096 pairs, max |dscore| %.3g, %d of %d argmax near-tie flips"
+          % (err, flips, a.size), flush=True)
+
+
+def test_workload_contrastive_train_chain(bd, train_ref):
+    """The whole training step at full size, as the parity protocol states it:
+    the GPU forward's argmax, the InfoNCE gradient computed once in fp64 from
+    the oracle's scores (tau = 0.02), then the backward on both sides with
+    that same argmax and gradient."""
+    w, D, s_ref, _, _ = train_ref
+    s, a = bd.maxsim_fwd(to_dev(w["Q"], inputs.BF16), to_dev(D, inputs.BF16))
+    torch.cuda.synchronize()
+    g = infonce_grad(s_ref, w["tau"]).astype(np.float32)
+    check_bwd(bd, w["Q"], D, inputs.BF16, a.cpu().numpy(), g, "contrastive_train chain")
 
 
 def test_workload_contrastive_train_hot_rows(bd):

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from late_interaction_retrieval_amd import inputs
-from gpu_util import GRAD_REL_TOL, oracle_dtype, rel_fro, to_dev
+from gpu_util import GRAD_REL_TOL, check_grad, oracle_dtype, rel_fro, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -21,10 +21,9 @@ def bd():
 
 
 def check_grads(dQ, dD, dQ_ref, dD_ref, sources_per_row, where):
-    eq, ed = rel_fro(dQ, dQ_ref), rel_fro(dD, dD_ref)
-    assert eq <= GRAD_REL_TOL and ed <= GRAD_REL_TOL, "%s: rel err dQ %.3g dD %.3g" % (where, eq, ed)
+    rq, rd = check_grad(dQ, dQ_ref, "dQ", where), check_grad(dD, dD_ref, "dD", where)
     assert np.all(dD.reshape(-1, 128)[sources_per_row == 0] == 0.0), where + ": untouched rows must be 0"
-    print("%s: rel err dQ %.2e dD %.2e" % (where, eq, ed), flush=True)
+    print("%s: %s; %s" % (where, rq, rd), flush=True)
 
 
 PADDED = [(1, 1, 1, 1), (2, 7, 3, 5), (3, 33, 4, 70), (1, 32, 50, 180), (17, 100, 3, 129), (4, 1024, 2, 1024)]

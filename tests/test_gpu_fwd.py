@@ -80,6 +80,10 @@ SHAPES = [  # Nq, Lq, B, (Ld lo, hi)
     (40, 32, 17, (32, 300)),
     (3, 128, 6, (60, 200)),
     (2, 300, 4, (1, 513)),
+    # 513..768 tokens: whole queries in 768-row slabs (three 32-row blocks per wave)
+    (2, 513, 5, (0, 300)),
+    (1, 600, 4, (1, 700)),
+    (3, 768, 3, (250, 260)),
     (1, 1024, 3, (1000, 1100)),
     (2, 1000, 2, (64, 64)),
     # short queries (one 32-row block each): documents packed by 32-token
@@ -277,11 +281,11 @@ def test_workload_colbert_tiny_full(bd):
     assert np.array_equal(s, s2) and np.array_equal(a, a2)
 
 
-def test_workload_colbert_rerank_varlen_sampled(bd):
+def test_workload_colbert_rerank_varlen_full(bd):
+    """The re-ranking workload at full size: 64 queries x 10,000 documents of
+    32..300 tokens, every score and argmax against the oracle."""
     w = inputs.make("colbert_rerank_varlen")
-    docs = np.sort(np.random.default_rng(1).choice(w["B"], size=64, replace=False))
-    docs[0], docs[-1] = 0, w["B"] - 1
-    s, _ = sampled_check(bd, w, docs, "colbert_rerank_varlen")
+    s, _ = sampled_check(bd, w, np.arange(w["B"]), "colbert_rerank_varlen")
     # the launch the benchmark times (no argmax) writes every score, and the
     # same bits as with the argmax
     scores = torch.full((w["Nq"], w["B"]), float("nan"), dtype=torch.float32, device=DEV)
@@ -289,15 +293,35 @@ def test_workload_colbert_rerank_varlen_sampled(bd):
                                  to_dev(w["cu_seqlens"]), 300, scores=scores, with_argmax=False)
     torch.cuda.synchronize()
     assert np.array_equal(s0.cpu().numpy(), s)
-    # padded to 300 with d_lens: identical scores
+    # padded to 300 with d_lens (the padded comparison run): identical scores
     Dpad = inputs.pad_packed(w["D_packed"], w["cu_seqlens"], 300)
     s2, _ = run_padded(bd, w["Q"], Dpad, inputs.F16, w["lens"], with_argmax=False)
     assert np.array_equal(s, s2)
 
 
-def test_workload_colpali_sampled(bd):
+def stream_edge_docs(B, nstreams, rng, n):
+    """n seeded document indices of B, always including the first and last
+    document and both sides of several stream boundaries of a grid that
+    splits the documents into nstreams contiguous ranges."""
+    edges = [(k * B) // nstreams for k in range(1, nstreams)]
+    pick = set([0, B - 1])
+    for e in edges:
+        pick.update([e - 1, e])
+    for b in rng.permutation(B):
+        if len(pick) >= n:
+            break
+        pick.add(int(b))
+    return np.array(sorted(pick))
+
+
+def test_workload_colpali_subset(bd):
+    """ColPali at full size on the GPU (4 x 1024-token queries, 10,000 documents
+    of 1024 tokens, bf16, argmax, the benchmark's launch); a seeded subset of
+    1,000 documents, including both sides of stream boundaries, through the
+    oracle."""
     w = inputs.make("colpali_fwd")
-    docs = np.array([0, 1, 4999, 9998, 9999])
+    docs = stream_edge_docs(w["B"], 32, np.random.default_rng(11), 1000)
+    assert len(docs) == 1000
     sampled_check(bd, w, docs, "colpali_fwd")
 
 

@@ -161,3 +161,55 @@ def test_euler_homogeneity_and_mass(dtn, dt):
     assert float((dD * Dd).sum()) == pytest.approx(gs, rel=1e-12, abs=1e-12)
     mass = np.einsum("qb,qk->bk", g.astype(np.float64), Qd.sum(axis=1))
     np.testing.assert_allclose(dD.sum(axis=1), mass, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtn,dt", [(inputs.F16, oracle.F16), (inputs.BF16, oracle.BF16)])
+def test_empty_document_selects_nothing(dtn, dt):
+    """Documents with d_lens = 0 get argmax -1 from the forward (the running
+    maximum never leaves -inf).  Their sources select no row: the CSR is the
+    stable argsort of dst over the sources with argmax >= 0, dQ takes no term
+    from them, and dD is the dense one-hot formulation with those pairs left
+    out.  The empty documents' score is -inf, so by L = sum g * score the
+    pair's gradient is a sum over no tokens."""
+    Nq, Lq, B, Ld, d = 3, 7, 5, 6, 16
+    Q, D, g = _random_case(47, dtn, Nq=Nq, Lq=Lq, B=B, Ld=Ld, d=d)
+    lens = np.array([4, 0, 6, 0, 1], np.int32)
+    s, A = oracle.fwd_padded(Q, D, dt, d_lens=lens)
+    assert np.all(A[:, lens == 0] == -1) and np.all(A[:, lens > 0] >= 0)
+    rp, ci = oracle.csr_build(A, Ld)
+    # numpy: stable argsort of dst over the valid sources only
+    b_of_s = np.broadcast_to(np.arange(B)[None, :, None], A.shape).ravel()
+    a = A.ravel()
+    valid = a >= 0
+    dst = b_of_s * Ld + a
+    cnt = np.bincount(dst[valid], minlength=B * Ld)
+    assert np.array_equal(rp, np.concatenate([[0], np.cumsum(cnt)]))
+    src = np.flatnonzero(valid)
+    assert np.array_equal(ci, src[np.argsort(dst[valid], kind="stable")])
+    assert rp[-1] == Nq * Lq * int((lens > 0).sum())
+    dQ, dD = oracle.bwd(Q, D, dt, A, g)
+    Qd, Dd = decoded(Q), decoded(D)
+    dQ_ref = np.zeros_like(dQ)
+    dD_ref = np.zeros_like(dD)
+    for q in range(Nq):
+        for b in range(B):
+            if lens[b] == 0:
+                continue
+            P = np.zeros((Lq, Ld))
+            P[np.arange(Lq), A[q, b]] = 1.0
+            dQ_ref[q] += g[q, b] * (P @ Dd[b])
+            dD_ref[b] += g[q, b] * (P.T @ Qd[q])
+    np.testing.assert_allclose(dQ, dQ_ref, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dD, dD_ref, rtol=1e-13, atol=1e-14)
+    assert np.all(dD[lens == 0] == 0.0)
+    # the same corpus packed (the empty documents have no rows): same col_idx,
+    # same dQ, and the padded rows of the non-empty documents hold the packed dD
+    cu = inputs.cu_seqlens(lens)
+    Dp = np.concatenate([D[b, :lens[b]] for b in range(B)])
+    rp2, ci2 = oracle.csr_build_varlen(A, cu)
+    assert np.array_equal(ci2, ci)
+    dQ2, dD2 = oracle.bwd_varlen(Q, Dp, cu, dt, A, g)
+    assert np.array_equal(dQ2, dQ)
+    for b in range(B):
+        assert np.array_equal(dD2[cu[b]:cu[b + 1]], dD[b, :lens[b]])
+        assert np.array_equal(rp2[cu[b]:cu[b + 1]], rp[b * Ld:b * Ld + lens[b]])

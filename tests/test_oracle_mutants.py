@@ -62,6 +62,17 @@ MUTANTS = {
                                      "                dQ[qj * 3 + k] += w * diff;"),
     "chamfer_own_term_sign": ("                dP[pi * 3 + k] += w * diff;\n                dQ[qj * 3 + k] -= w * diff;",
                               "                dP[pi * 3 + k] -= w * diff;\n                dQ[qj * 3 + k] -= w * diff;"),
+    # one padding token read as valid (off-by-one in the mask)
+    "mask_off_by_one": ("        len[b] = d_lens ? d_lens[b] : Ld;",
+                        "        len[b] = d_lens ? (d_lens[b] < Ld ? d_lens[b] + 1 : Ld) : Ld;"),
+    # the INT8 epilogue contracted into one fused multiply-add (one rounding instead of two)
+    "i8_epilogue_fma": ("                score = score + v;", "                score = fmaf(m, q_scale[(int64_t)q * Lq + i], score);"),
+    # the padded CSR filled in descending source order (unstable within a row)
+    "csr_fill_unstable": ("    for (int64_t s = 0; s < nsrc; ++s) { /* ascending s: a stable fill */\n        int64_t b = (s / Lq) % B;\n        if (argmax[s] < 0) continue;",
+                          "    for (int64_t s = nsrc - 1; s >= 0; --s) { /* ascending s: a stable fill */\n        int64_t b = (s / Lq) % B;\n        if (argmax[s] < 0) continue;"),
+    # an empty document's -1 clamped to its token 0 instead of selecting nothing
+    "padded_empty_doc_clamped": ("                if (t < 0) continue;\n                const uint16_t* qrow",
+                                 "                if (t < 0) t = 0;\n                const uint16_t* qrow"),
     "chamfer_factor_two_dropped": ("            const double w = 2.0 * (double)gq[qj];", "            const double w = (double)gq[qj];"),
 }
 
