@@ -58,7 +58,8 @@ typedef enum {
     MAXSIM_ERR_UNSUPPORTED = 3, /* d != 128, Lq > 1024, unknown dtype, shape beyond a kernel limit */
     MAXSIM_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
     MAXSIM_ERR_WORKSPACE = 5,   /* workspace smaller than maxsim_bwd_workspace_bytes() */
-    MAXSIM_ERR_HIP = 6          /* the HIP runtime rejected a launch */
+    MAXSIM_ERR_HIP = 6,         /* the HIP runtime rejected a launch */
+    MAXSIM_ERR_SCRATCH = 7      /* maxsim_bwd_noalloc: the shape needs more than its fixed scratch */
 } maxsim_status;
 
 typedef enum { MAXSIM_F16 = 0, MAXSIM_BF16 = 1 } maxsim_dtype;
@@ -142,6 +143,29 @@ int maxsim_bwd(const void* Q, const void* D, int32_t dtype, const int32_t* argma
                const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B, int32_t Ld, int32_t d,
                float* dQ, float* dD, int32_t* row_ptr, int32_t* col_idx, void* workspace,
                size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free variant of maxsim_bwd, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the same kernels and results as maxsim_bwd, with
+ * the workspace taken from a device array the library holds, of
+ * maxsim_bwd_noalloc_scratch_bytes() bytes (64 MiB) on every GPU it runs on,
+ * for the life of the process.  The caller passes inputs and outputs as for
+ * maxsim_bwd.  The call allocates nothing (no hipMalloc, no library routine
+ * that allocates); its first call on a device looks up that device's copy
+ * of the array (hipGetSymbolAddress) with the device current.
+ *   Returns MAXSIM_ERR_SCRATCH, before any HIP call, when
+ *   maxsim_bwd_workspace_bytes() of the shape exceeds the array; other
+ *   arguments and errors as maxsim_bwd.
+ * Every call on one device shares that device's array: calls that overlap
+ * on one device (different streams or threads) race and give unspecified
+ * results.  Calls ordered on one stream are safe; each call writes every
+ * scratch word it reads.
+ */
+size_t maxsim_bwd_noalloc_scratch_bytes(void);
+int maxsim_bwd_noalloc(const void* Q, const void* D, int32_t dtype, const int32_t* argmax,
+                       const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B, int32_t Ld, int32_t d,
+                       float* dQ, float* dD, int32_t* row_ptr, int32_t* col_idx, void* stream);
 
 /* Bytes of device workspace maxsim_bwd_varlen needs (0 on bad sizes). */
 size_t maxsim_bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld);

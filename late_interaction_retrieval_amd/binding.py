@@ -22,6 +22,7 @@ MAXSIM_ERR_UNSUPPORTED = 3
 MAXSIM_ERR_ALIGN = 4
 MAXSIM_ERR_WORKSPACE = 5
 MAXSIM_ERR_HIP = 6
+MAXSIM_ERR_SCRATCH = 7
 MAXSIM_F16 = 0
 MAXSIM_BF16 = 1
 
@@ -36,6 +37,8 @@ SIGNATURES = {
     "maxsim_bwd_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "maxsim_bwd": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
+    "maxsim_bwd_noalloc_scratch_bytes": (ctypes.c_size_t, []),
+    "maxsim_bwd_noalloc": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "maxsim_bwd_varlen_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "maxsim_bwd_varlen": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _P, _P,
                                          _P, _P, _P, ctypes.c_size_t, _P]),
@@ -230,6 +233,29 @@ def maxsim_bwd(Q, D, argmax, grad_scores, dQ=None, dD=None, row_ptr=None, col_id
                           _ptr(dQ), _ptr(dD), _ptr(row_ptr), _ptr(col_idx), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream(Q, stream))
     _check(st, "maxsim_bwd")
+    return dQ, dD, row_ptr, col_idx
+
+
+def maxsim_bwd_noalloc(Q, D, argmax, grad_scores, dQ, dD, row_ptr, col_idx, stream=None):
+    """maxsim_bwd without a workspace and without allocating: the library's own
+    per-device scratch array serves as the workspace, and every output is the
+    caller's.  Returns (dQ, dD, row_ptr, col_idx)."""
+    Nq, Lq, d = Q.shape
+    B, Ld, _ = D.shape
+    dev = Q.device
+    _need(Q, "Q")
+    _need(D, "D", device=dev)
+    _need(argmax, "argmax", torch.int32, dev)
+    _need(grad_scores, "grad_scores", torch.float32, dev)
+    for t, n, dt, numel in ((dQ, "dQ", torch.float32, Nq * Lq * d), (dD, "dD", torch.float32, B * Ld * d),
+                            (row_ptr, "row_ptr", torch.int32, B * Ld + 1),
+                            (col_idx, "col_idx", torch.int32, Nq * B * Lq)):
+        _need(t, n, dt, dev)
+        if t.numel() < numel:
+            raise ValueError("%s holds %d elements, needs %d" % (n, t.numel(), numel))
+    st = lib().maxsim_bwd_noalloc(_ptr(Q), _ptr(D), _dtype_code(Q), _ptr(argmax), _ptr(grad_scores), Nq, Lq, B, Ld,
+                                  d, _ptr(dQ), _ptr(dD), _ptr(row_ptr), _ptr(col_idx), _stream(Q, stream))
+    _check(st, "maxsim_bwd_noalloc")
     return dQ, dD, row_ptr, col_idx
 
 

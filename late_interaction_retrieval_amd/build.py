@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmaxsim.so")
-SOURCES = ["fwd.hip", "bwd.hip", "topk.hip", "ooc.hip", "chamfer.hip", "capi.cpp"]
+SOURCES = ["fwd.hip", "bwd.hip", "topk.hip", "ooc.hip", "chamfer.hip", "noalloc.hip", "capi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

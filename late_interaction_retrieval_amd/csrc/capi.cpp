@@ -121,22 +121,28 @@ size_t maxsim_bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld)
     return maxsim::bwd_workspace_bytes(Nq, B, Lq, Ld);
 }
 
-int maxsim_bwd(const void* Q, const void* D, int32_t dtype, const int32_t* argmax,
-               const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B, int32_t Ld, int32_t d,
-               float* dQ, float* dD, int32_t* row_ptr, int32_t* col_idx, void* workspace,
-               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The padded backward's arguments other than its workspace.
+int check_bwd(const void* Q, const void* D, int32_t dtype, const int32_t* argmax, const float* grad_scores,
+              int32_t Nq, int32_t Lq, int32_t B, int32_t Ld, int32_t d, const float* dQ, const float* dD,
+              const int32_t* row_ptr, const int32_t* col_idx) {
     if (Nq < 1 || B < 1 || Lq < 1 || Ld < 1) return MAXSIM_ERR_SHAPE;
     if ((int64_t)Nq * B * Lq >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
     if ((int64_t)B * Ld >= ((int64_t)1 << 31)) return MAXSIM_ERR_SHAPE;
     if (d != kDim || Lq > kMaxLq || Ld > maxsim::kMaxLdBwd) return MAXSIM_ERR_UNSUPPORTED;
     if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_UNSUPPORTED;
-    if (!Q || !D || !argmax || !grad_scores || !dQ || !dD || !row_ptr || !col_idx || !workspace)
-        return MAXSIM_ERR_NULL;
+    if (!Q || !D || !argmax || !grad_scores || !dQ || !dD || !row_ptr || !col_idx) return MAXSIM_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(dQ, 16) || !aligned(dD, 16) ||
-        !aligned(argmax, 4) || !aligned(grad_scores, 4) || !aligned(row_ptr, 4) ||
-        !aligned(col_idx, 4) || !aligned(workspace, 16))
+        !aligned(argmax, 4) || !aligned(grad_scores, 4) || !aligned(row_ptr, 4) || !aligned(col_idx, 4))
         return MAXSIM_ERR_ALIGN;
-    if (workspace_bytes < maxsim::bwd_workspace_bytes(Nq, B, Lq, Ld)) return MAXSIM_ERR_WORKSPACE;
+    return MAXSIM_OK;
+}
+
+int launch_bwd_padded(const void* Q, const void* D, int32_t dtype, const int32_t* argmax, const float* grad_scores,
+                      int32_t Nq, int32_t Lq, int32_t B, int32_t Ld, float* dQ, float* dD, int32_t* row_ptr,
+                      int32_t* col_idx, void* workspace, void* stream) {
     maxsim::BwdArgs a{};
     a.Q = Q;
     a.D = D;
@@ -153,6 +159,36 @@ int maxsim_bwd(const void* Q, const void* D, int32_t dtype, const int32_t* argma
     a.col_idx = col_idx;
     a.workspace = workspace;
     return hip_status(maxsim::launch_bwd(a, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+int maxsim_bwd(const void* Q, const void* D, int32_t dtype, const int32_t* argmax,
+               const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B, int32_t Ld, int32_t d,
+               float* dQ, float* dD, int32_t* row_ptr, int32_t* col_idx, void* workspace,
+               size_t workspace_bytes, void* stream) {
+    const int st = check_bwd(Q, D, dtype, argmax, grad_scores, Nq, Lq, B, Ld, d, dQ, dD, row_ptr, col_idx);
+    if (st != MAXSIM_OK) return st;
+    if (!workspace) return MAXSIM_ERR_NULL;
+    if (!aligned(workspace, 16)) return MAXSIM_ERR_ALIGN;
+    if (workspace_bytes < maxsim::bwd_workspace_bytes(Nq, B, Lq, Ld)) return MAXSIM_ERR_WORKSPACE;
+    return launch_bwd_padded(Q, D, dtype, argmax, grad_scores, Nq, Lq, B, Ld, dQ, dD, row_ptr, col_idx, workspace,
+                             stream);
+}
+
+size_t maxsim_bwd_noalloc_scratch_bytes(void) { return maxsim::kScratchBytes; }
+
+int maxsim_bwd_noalloc(const void* Q, const void* D, int32_t dtype, const int32_t* argmax,
+                       const float* grad_scores, int32_t Nq, int32_t Lq, int32_t B, int32_t Ld, int32_t d,
+                       float* dQ, float* dD, int32_t* row_ptr, int32_t* col_idx, void* stream) {
+    const int st = check_bwd(Q, D, dtype, argmax, grad_scores, Nq, Lq, B, Ld, d, dQ, dD, row_ptr, col_idx);
+    if (st != MAXSIM_OK) return st;
+    if (maxsim::bwd_workspace_bytes(Nq, B, Lq, Ld) > maxsim::kScratchBytes) return MAXSIM_ERR_SCRATCH;
+    void* scratch = nullptr;
+    if (maxsim::scratch_address(&scratch) != hipSuccess) return MAXSIM_ERR_HIP;
+    return launch_bwd_padded(Q, D, dtype, argmax, grad_scores, Nq, Lq, B, Ld, dQ, dD, row_ptr, col_idx, scratch,
+                             stream);
 }
 
 size_t maxsim_bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld) {
@@ -464,6 +500,8 @@ const char* maxsim_status_string(int status) {
         case MAXSIM_ERR_ALIGN: return "MAXSIM_ERR_ALIGN: misaligned pointer";
         case MAXSIM_ERR_WORKSPACE: return "MAXSIM_ERR_WORKSPACE: workspace too small";
         case MAXSIM_ERR_HIP: return "MAXSIM_ERR_HIP: kernel launch failed";
+        case MAXSIM_ERR_SCRATCH:
+            return "MAXSIM_ERR_SCRATCH: the shape needs more scratch than the allocation-free entry point holds";
         default: return "unknown maxsim status";
     }
 }

@@ -102,6 +102,11 @@ struct BwdArgs {
     int64_t T = 0;
 };
 
+// The allocation-free backward's scratch: a device array of kScratchBytes per
+// device (noalloc.hip).  scratch_address gives the current device's copy.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_address(void** out);
+
 // Queries per CSR group (one wave each) for a document length; 0 if unsupported.
 int bwd_group(int32_t Ld);
 size_t bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld);

@@ -50,7 +50,8 @@ def test_every_declared_symbol_is_exported_with_binding_arity():
                          "maxsim_bwd_prefer_scatter", "maxsim_bwd_scatter_workspace_bytes",
                          "maxsim_fwd_host_stream_staging_bytes", "maxsim_fwd_host_stream",
                          "maxsim_chamfer_fwd_workspace_bytes", "maxsim_chamfer_fwd",
-                         "maxsim_chamfer_bwd_workspace_bytes", "maxsim_chamfer_bwd"}
+                         "maxsim_chamfer_bwd_workspace_bytes", "maxsim_chamfer_bwd",
+                         "maxsim_bwd_noalloc_scratch_bytes", "maxsim_bwd_noalloc"}
     raw = ctypes.CDLL(LIB)
     for name, nargs in decl.items():
         assert hasattr(raw, name), name
@@ -357,3 +358,32 @@ def test_chamfer_workspace_bytes():
     # 2048-element tile), then the heavy-row list (a count and n // 1025 rows)
     n = 10 + 3000
     assert L.maxsim_chamfer_bwd_workspace_bytes(1, 10, 3000) == 4 * ((n * 4 + 255) // 256 * 256) + 2 * 256 * 4 + 256
+
+
+def test_bwd_noalloc_validation():
+    """The allocation-free backward validates like maxsim_bwd (no workspace
+    arguments) and refuses, before any HIP call, a shape whose workspace
+    exceeds its fixed scratch."""
+    cap = L.maxsim_bwd_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+
+    def call(**kw):
+        a = dict(Q=A, D=A, dt=1, am=A, g=A, Nq=4, Lq=32, B=3, Ld=50, d=128, dQ=A, dD=A, rp=A, ci=A, stream=None)
+        a.update(kw)
+        return L.maxsim_bwd_noalloc(a["Q"], a["D"], a["dt"], a["am"], a["g"], a["Nq"], a["Lq"], a["B"], a["Ld"],
+                                    a["d"], a["dQ"], a["dD"], a["rp"], a["ci"], a["stream"])
+
+    assert call(Nq=0) == bd.MAXSIM_ERR_SHAPE
+    assert call(Nq=1 << 12, B=1 << 10, Lq=1 << 10) == bd.MAXSIM_ERR_SHAPE
+    assert call(d=64) == bd.MAXSIM_ERR_UNSUPPORTED
+    assert call(Ld=5000) == bd.MAXSIM_ERR_UNSUPPORTED
+    assert call(dt=5) == bd.MAXSIM_ERR_UNSUPPORTED
+    assert call(am=None) == bd.MAXSIM_ERR_NULL
+    assert call(ci=None) == bd.MAXSIM_ERR_NULL
+    assert call(Q=M) == bd.MAXSIM_ERR_ALIGN
+    assert call(rp=M) == bd.MAXSIM_ERR_ALIGN
+    # 100,000 documents of 180 rows: the workspace exceeds the scratch array
+    assert L.maxsim_bwd_workspace_bytes(1, 100000, 32, 180) > cap
+    assert call(Nq=1, B=100000, Ld=180) == bd.MAXSIM_ERR_SCRATCH
+    assert L.maxsim_bwd_workspace_bytes(64, 64, 1024, 1024) <= cap  # the training step fits
+    assert b"SCRATCH" in L.maxsim_status_string(bd.MAXSIM_ERR_SCRATCH)
