@@ -27,8 +27,12 @@
  *     reads so that no access leaves the buffers described by the sizes:
  *     a document length outside [0, Ld] (padded) is clamped to that range, a
  *     cu_seqlens range outside [0, T) is clamped to it, and an argmax entry
- *     outside [0, Ld) given to the backward is clamped into [0, Ld) (the
- *     gradients are then unspecified, but no access leaves the buffers).
+ *     at or past the document's length given to the backward is clamped to
+ *     its last token (the gradients are then unspecified, but no access
+ *     leaves the buffers).
+ *   - In the backward a negative argmax entry -- what the forward writes for
+ *     a document with no valid token -- selects no row: the source is in no
+ *     CSR bucket and adds nothing to dQ or dD.
  *   - Query-token count Lq is limited to 1 <= Lq <= 1024.
  *   - A document with no valid token scores -inf and every argmax entry of
  *     it is -1 (the running maximum starts at -inf, Section 4.1).
@@ -121,10 +125,13 @@ size_t maxsim_bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld)
  *   Q [Nq, Lq, d], D [B, Ld, d] (dtype), argmax [Nq, B, Lq] int32 from the
  *   forward, grad_scores [Nq, B] fp32 = dL/dscore.
  * Step 1, inverse-grid CSR ("Runtime Inverse-Grid Construction"): with the
- *   source id s = (q*B + b)*Lq + i and destination dst(s) = b*Ld + argmax[s],
- *     row_ptr [B*Ld + 1] out: exclusive prefix sum of the per-row counts,
- *     col_idx [Nq*B*Lq]  out: the sources of row r in ascending s at
- *                             col_idx[row_ptr[r] .. row_ptr[r+1]).
+ *   source id s = (q*B + b)*Lq + i and destination dst(s) = b*Ld + argmax[s]
+ *   (no destination when argmax[s] < 0: a document of d_lens 0),
+ *     row_ptr [B*Ld + 1] out: exclusive prefix sum of the per-row counts
+ *                             (row_ptr[B*Ld] = number of sources with a row),
+ *     col_idx [Nq*B*Lq]  out (capacity): the sources of row r in ascending s
+ *                             at col_idx[row_ptr[r] .. row_ptr[r+1]); entries
+ *                             past row_ptr[B*Ld] are unspecified.
  *   Both are deterministic (bit-identical on every call).
  * Step 2, destination-owned dD ("Destination-Owned Reduction", Eq. (dd)):
  *     dD [B, Ld, d] fp32 out, dD[b,t] = sum over the sources s of row b*Ld+t

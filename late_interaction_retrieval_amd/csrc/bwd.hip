@@ -9,21 +9,22 @@
 // sources occupy the fixed range [b*Nq*Lq, (b+1)*Nq*Lq) of col_idx, so each
 // document's part of the map is built independently:
 //   1. csr_count : per (document, group of G queries) a histogram over the
-//                  document's Ld rows (LDS atomics; counts are order-free).
-//   2. csr_scan  : per document, prefix over the query groups and over the
-//                  rows -> row_ptr and each group's first slot per row.
-//   3. csr_fill  : per (document, query group), one wave per query.  Within a
-//                  query the sources are ranked in ascending i, 64 at a time:
-//                  one ballot per bit of the row index gives every lane the
-//                  mask of lanes holding its row, and popcount(mask & lanes
-//                  below) is its rank.  The per-query prefix over the group
-//                  makes the whole fill stable and deterministic.
-//   4. dd_owner  : a 16-lane group owns dD rows, walks their sources and
+//                  document's rows (LDS atomics; counts are order-free) and
+//                  the group's number of sources.
+//   2. csr_fill  : per (document, query group), one wave per query: the
+//                  document's first slot and row starts from the counts
+//                  (row_ptr), then the group's sources ranked by (row, query,
+//                  i) in LDS -- within a query 64 at a time in ascending i,
+//                  a lane's rank is the number of lower lanes holding its row
+//                  -- and written out run by run.  Stable and deterministic.
+//   3. dd_owner  : a 16-lane group owns dD rows, walks their sources and
 //                  writes each row once (no atomics).
-//   5. dq_gather : a 16-lane group owns dQ rows and loops over the B
+//   4. dq_gather : a 16-lane group owns dQ rows and loops over the B
 //                  documents (Algorithm 3 step 3).
-// argmax entries outside [0, Ld) break the forward's contract; they are
-// clamped into range so that no access leaves the buffers.
+// A negative argmax entry (the forward's value for a document with no valid
+// token) selects no row.  Entries at or past a document's length break the
+// forward's contract; they are clamped into range so that no access leaves
+// the buffers.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -47,15 +48,17 @@ struct BwdParams {
     float* dD;
     int32_t* row_ptr;
     int32_t* col_idx;
-    int32_t* ws;  // [B][NG][Ld]
+    int32_t* ws;    // [B][NG][Ld] per (document, query group) row counts
+    int32_t* gtot;  // [B*NG] per (document, query group) number of sources that select a row
     // floor(n / (B*Lq)) for 0 <= n < 2^31 as (n * magic) >> (32 + shift)
     unsigned long long magic;
     int shift;
     // floor(n / Lq) likewise
     unsigned long long magic_lq;
     int shift_lq;
-    // packed corpus: cu_seqlens [B+1] (nullptr: padded documents of Ld rows),
-    // T rows, and each document's first CSR slot [B+1] (workspace)
+    // packed corpus: cu_seqlens [B+1] (nullptr: padded documents of Ld rows)
+    // and T rows; each document's first CSR slot [B+1] (workspace; nullptr:
+    // the fill sums the groups' totals itself)
     const int32_t* cu;
     int64_t T;
     int32_t* docbase;
@@ -87,53 +90,17 @@ __device__ __forceinline__ void doc_rows(const BwdParams& p, int b, int64_t& sta
     }
 }
 
-// First col_idx slot of document b: its sources follow those of the earlier
-// non-empty documents.
-__device__ __forceinline__ int doc_base(const BwdParams& p, int b) {
-    return p.docbase ? p.docbase[b] : b * p.Nq * p.Lq;
-}
-
-// Packed corpus: docbase[b] = Nq*Lq * (number of non-empty documents before b),
-// b = 0 .. B.  One workgroup of 1024 threads scans the documents in order.
-__global__ __launch_bounds__(1024) void csr_docbase(BwdParams p) {
-    __shared__ int wsum[16];
-    __shared__ int carry_s;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) carry_s = 0;
-    __syncthreads();
-    const int per = p.Nq * p.Lq;
-    for (int b0 = 0; b0 <= p.B; b0 += 1024) {
-        const int b = b0 + tid;
-        int flag = 0;
-        if (b < p.B) {
-            int64_t st;
-            int len;
-            doc_rows(p, b, st, len);
-            flag = len > 0;
-        }
-        int x = flag;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(x, off);
-            if (lane >= off) x += y;
-        }
-        if (lane == 63) wsum[wave] = x;
-        __syncthreads();
-        int wpre = 0;
-        for (int w = 0; w < wave; ++w) wpre += wsum[w];
-        const int carry = carry_s;
-        if (b <= p.B) p.docbase[b] = (carry + wpre + x - flag) * per;
-        __syncthreads();
-        if (tid == 1023) carry_s = carry + wpre + x;
-        __syncthreads();
-    }
-}
+// The row that source s = (q*B + b)*Lq + i selects in document b (of len
+// rows), or -1 for none: a negative argmax (what the forward writes for a
+// document with no valid token) and every source of a document without rows
+// select nothing.  Entries at or past len break the forward's contract and
+// are clamped to the last row so that no access leaves the buffers.
+__device__ __forceinline__ int src_row(int a, int len) { return (a < 0 || len == 0) ? -1 : (a >= len ? len - 1 : a); }
 
 // Workgroup k of the count and fill grids runs on XCD k % 8; all of document
-// b's query groups go to XCD b % 8 (the XCD csr_scan's workgroup b runs on),
-// so its counts and its part of col_idx are written through one L2, where the
-// short scattered writes of the fill combine into whole lines.  The grid has
-// 8 * ceil(B / 8) * NG workgroups; those past the last document do nothing.
+// b's query groups go to XCD b % 8, so its argmax entries and counts stay in
+// one L2 between the two kernels.  The grid has 8 * ceil(B / 8) * NG
+// workgroups; those past the last document do nothing.
 __device__ __forceinline__ bool doc_group(const BwdParams& p, int& b, int& qg) {
     const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int d = j / p.NG;
@@ -142,8 +109,63 @@ __device__ __forceinline__ bool doc_group(const BwdParams& p, int& b, int& qg) {
     return b < p.B;
 }
 
+// Sum of v over the workgroup (every thread gets it); red holds one int per wave.
+__device__ __forceinline__ int block_sum(int v, int* red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    __syncthreads();  // red may still be read by a previous call
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    int t = 0;
+    for (int w = 0; w < nw; ++w) t += red[w];
+    return t;
+}
+
+// Exclusive prefix over the workgroup's threads of two values at once, and
+// their totals; red holds two ints per wave.
+__device__ __forceinline__ void block_exscan2(int x, int y, int* red, int& ex, int& ey, int& tx, int& ty) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int ix = x, iy = y;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int ux = __shfl_up(ix, off), uy = __shfl_up(iy, off);
+        if (lane >= off) {
+            ix += ux;
+            iy += uy;
+        }
+    }
+    __syncthreads();  // red may still be read by a previous call
+    if (lane == 63) {
+        red[2 * wave] = ix;
+        red[2 * wave + 1] = iy;
+    }
+    __syncthreads();
+    int px = 0, py = 0;
+    tx = 0;
+    ty = 0;
+    for (int w = 0; w < nw; ++w) {
+        const int a = red[2 * w], c = red[2 * w + 1];
+        if (w < wave) {
+            px += a;
+            py += c;
+        }
+        tx += a;
+        ty += c;
+    }
+    ex = px + ix - x;
+    ey = py + iy - y;
+}
+
+// 1. csr_count: per (document, group of G queries), one wave per query, the
+// number of the group's sources selecting each of the document's rows (LDS
+// histogram; counts do not depend on the order of the increments) and the
+// group's number of sources that select a row.  Workgroup 0 also clears the
+// heavy-row list that dd_owner appends to after the fill.
 __global__ __launch_bounds__(1024) void csr_count(BwdParams p) {
     extern __shared__ int hist[];  // [Ld]
+    __shared__ int red[16];
+    if (blockIdx.x == 0 && threadIdx.x == 0) p.heavy[0] = 0;
     int b, qg;
     if (!doc_group(p, b, qg)) return;  // uniform
     const int nt = blockDim.x;
@@ -154,149 +176,187 @@ __global__ __launch_bounds__(1024) void csr_count(BwdParams p) {
     int64_t st;
     int len;
     doc_rows(p, b, st, len);
-    if (q < p.Nq && len > 0) {  // an empty document has no rows and no sources
+    int n = 0;
+    if (q < p.Nq) {
         const int32_t* a = p.A + ((int64_t)q * p.B + b) * p.Lq;
-        for (int i = lane; i < p.Lq; i += 64) atomicAdd(&hist[clamp_tok(a[i], len)], 1);
+        for (int i = lane; i < p.Lq; i += 64) {
+            const int t = src_row(a[i], len);
+            if (t >= 0) {
+                atomicAdd(&hist[t], 1);
+                ++n;
+            }
+        }
     }
-    __syncthreads();
+    n = block_sum(n, red);  // (its barriers also order the histogram)
     int32_t* out = p.ws + ((int64_t)b * p.NG + qg) * p.Ld;
     for (int t = threadIdx.x; t < p.Ld; t += nt) out[t] = hist[t];
+    if (threadIdx.x == 0) p.gtot[(int64_t)b * p.NG + qg] = n;
 }
 
-// One workgroup of 1024 threads per document.  The per-group counts of a row
-// are read 16 at a time (independent loads), summed, and after the scan over
-// the rows read again to write each group's first slot.
-__global__ __launch_bounds__(1024) void csr_scan(BwdParams p) {
-    __shared__ int wsum[16];
-    __shared__ int carry_s;
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int base = doc_base(p, b);
-    int64_t rstart;
-    int len;
-    doc_rows(p, b, rstart, len);
-    int32_t* ws = p.ws + (int64_t)b * p.NG * p.Ld;
-    if (b == 0 && tid == 0) p.heavy[0] = 0;  // dd_owner appends heavy rows after this kernel
-    if (tid == 0) carry_s = 0;
-    __syncthreads();
-    for (int t0 = 0; t0 < len; t0 += 1024) {
-        const int t = t0 + tid;
-        int tot = 0;
-        if (t < len) {
-            for (int g0 = 0; g0 < p.NG; g0 += 16) {
-                int c[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) c[j] = g0 + j < p.NG ? ws[(int64_t)(g0 + j) * p.Ld + t] : 0;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) tot += c[j];
-            }
-        }
-        // inclusive scan of tot over the 1024 threads
-        int x = tot;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(x, off);
-            if (lane >= off) x += y;
-        }
-        if (lane == 63) wsum[wave] = x;
-        __syncthreads();
-        int wpre = 0;
-        for (int w = 0; w < wave; ++w) wpre += wsum[w];
-        const int carry = carry_s;
-        const int excl = carry + wpre + x - tot;
-        if (t < len) {
-            int run = base + excl;
-            p.row_ptr[rstart + t] = run;
-            for (int g0 = 0; g0 < p.NG; g0 += 16) {
-                int c[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) c[j] = g0 + j < p.NG ? ws[(int64_t)(g0 + j) * p.Ld + t] : 0;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    if (g0 + j < p.NG) ws[(int64_t)(g0 + j) * p.Ld + t] = run;
-                    run += c[j];
-                }
-            }
-        }
-        __syncthreads();
-        if (tid == 1023) carry_s = carry + wpre + x;
-        __syncthreads();
-    }
-    if (b == p.B - 1 && tid == 0) {  // one past the last row: the number of sources that select a row
-        const int64_t nrows = p.cu ? p.T : (int64_t)p.B * p.Ld;
-        p.row_ptr[nrows] = p.docbase ? p.docbase[p.B] : p.B * p.Nq * p.Lq;
+// With many documents the fill takes each document's first col_idx slot from
+// docbase[b] (b = 0 .. B), the exclusive prefix of the documents' source
+// counts, formed here by one workgroup of 1024 threads in order; with few,
+// every fill workgroup sums the earlier groups' totals itself.
+constexpr int kInlineDocTotals = 2048;  // B * NG up to which the fill sums gtot itself
+
+__global__ __launch_bounds__(1024) void csr_docscan(BwdParams p) {
+    __shared__ int red[32];
+    int carry = 0;
+    for (int b0 = 0; b0 <= p.B; b0 += 1024) {
+        const int b = b0 + threadIdx.x;
+        int n = 0;
+        if (b < p.B)
+            for (int g = 0; g < p.NG; ++g) n += p.gtot[(int64_t)b * p.NG + g];
+        int ex, dummy, tot, dtot;
+        block_exscan2(n, 0, red, ex, dummy, tot, dtot);
+        if (b <= p.B) p.docbase[b] = carry + ex;
+        carry += tot;
     }
 }
 
-// One wave per query of the group.  Dynamic LDS: G*Ld int (next slot per
-// (query, row)).
-// A wave reads its query's Lq argmax entries once, into registers (at most
-// kMaxLq / 64 per lane), and uses them for both the count and the fill.
+// 2. csr_fill: per (document, query group), one wave per query.
+//   a. The document's first slot (sum of the earlier documents' sources), its
+//      row totals (the sum of the groups' counts) and their prefix give every
+//      row's first slot: row_ptr, written by the group-0 workgroup.  This
+//      group's run of row t starts after the earlier groups' sources of t.
+//   b. Within the group the sources are ranked by (row, query, i): per query
+//      and row an LDS count, prefix over rows and then queries, and inside a
+//      query, 64 sources at a time in ascending i, the rank among the lanes
+//      holding the same row (found by an LDS tag per row; only lanes that
+//      share a row with another lane of the step take a ballot of that row
+//      and count the lower lanes in it).  That is the stable order.
+//   c. The sources are placed in LDS in that order and written out by
+//      consecutive threads: each row's run of the group is contiguous in
+//      col_idx, so a wave's stores cover a few runs instead of 64 scattered
+//      words.
+// LDS: G*Ld int (per query and row: counts, then slots), Ld int (per row:
+// global slot minus local slot), G*Lq int (the placed sources, packed as
+// row << 14 | query << 10 | i), G*Ld bytes (per query and row: a lane tag).
 constexpr int kFillIt = kMaxLq / 64;
+constexpr int kFillSlots = 16384;  // G * Ld of a query group (bwd_group keeps it within this)
 
-__global__ __launch_bounds__(1024) void csr_fill(BwdParams p) {
-    extern __shared__ int lds[];
+template <int G>
+__global__ __launch_bounds__(64 * G) void csr_fill(BwdParams p) {
+    constexpr int kLdMax = kFillSlots / G < kMaxLdBwd ? kFillSlots / G : kMaxLdBwd;  // G * Ld <= kFillSlots
+    __shared__ int slot[G * kLdMax];             // [G][Ld]
+    __shared__ int delta[kLdMax];                // [Ld]
+    __shared__ int stage[G * kMaxLq];            // [G*Lq]
+    __shared__ unsigned char tag[G * kLdMax];    // [G][Ld]
+    __shared__ int red[32];
     int b, qg;
     if (!doc_group(p, b, qg)) return;  // uniform
     const int tid = threadIdx.x, nt = blockDim.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int Ld = p.Ld;
-    int* slot = lds;  // [G][Ld]
-    const int q = qg * p.G + wave;
+    const int Ld = p.Ld, NG = p.NG;
+    const int q = qg * G + wave;
     int64_t rstart;
     int len;
     doc_rows(p, b, rstart, len);
-    if (len == 0) return;  // uniform: an empty document has no sources
     const int32_t* a = p.A + ((int64_t)q * p.B + b) * p.Lq;
-    int tk[kFillIt];  // -1: no source in this lane for step k
+    int tk[kFillIt];  // the row each of this lane's sources selects, or -1
 #pragma unroll
     for (int k = 0; k < kFillIt; ++k) {
         const int i = k * 64 + lane;
-        tk[k] = (q < p.Nq && i < p.Lq) ? clamp_tok(a[i], len) : -1;
+        tk[k] = (q < p.Nq && i < p.Lq) ? src_row(a[i], len) : -1;
     }
-    for (int e = tid; e < p.G * Ld; e += nt) slot[e] = 0;
+    // the document's first slot
+    int dbase;
+    if (p.docbase) {
+        dbase = p.docbase[b];
+    } else {
+        int sum = 0;
+        for (int k = tid; k < b * NG; k += nt) sum += p.gtot[k];
+        dbase = block_sum(sum, red);
+    }
+    for (int e = tid; e < G * Ld; e += nt) slot[e] = 0;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kFillIt; ++k)
         if (tk[k] >= 0) atomicAdd(&slot[wave * Ld + tk[k]], 1);
     __syncthreads();
-    // per row: exclusive prefix over the group's queries + the group's first slot
-    const int32_t* first = p.ws + ((int64_t)b * p.NG + qg) * Ld;
-    for (int t = tid; t < Ld; t += nt) {
-        int run = first[t];
-        for (int w = 0; w < p.G; ++w) {
-            const int c = slot[w * Ld + t];
-            slot[w * Ld + t] = run;
-            run += c;
+    // per row t: local slots of the group's queries, and the global run start
+    const int32_t* cnt = p.ws + (int64_t)b * NG * Ld;
+    int carry_lo = 0, carry_row = 0;
+    for (int t0 = 0; t0 < Ld; t0 += nt) {  // uniform
+        const int t = t0 + tid;
+        int gc = 0, rowtot = 0, before = 0;
+        if (t < Ld) {
+            for (int w = 0; w < G; ++w) gc += slot[w * Ld + t];
+            for (int g = 0; g < NG; ++g) {
+                const int c = cnt[(int64_t)g * Ld + t];
+                rowtot += c;
+                before += g < qg ? c : 0;
+            }
         }
+        int ex_lo, ex_row, tot_lo, tot_row;
+        block_exscan2(gc, rowtot, red, ex_lo, ex_row, tot_lo, tot_row);
+        if (t < Ld) {
+            int run = carry_lo + ex_lo;
+            const int row_first = dbase + carry_row + ex_row;
+            delta[t] = row_first + before - run;
+            for (int w = 0; w < G; ++w) {
+                const int c = slot[w * Ld + t];
+                slot[w * Ld + t] = run;
+                run += c;
+            }
+            if (qg == 0 && t < len) p.row_ptr[rstart + t] = row_first;
+        }
+        carry_lo += tot_lo;
+        carry_row += tot_row;
+    }
+    if (qg == 0 && b == p.B - 1 && tid == 0) {  // one past the last row: the number of sources that select a row
+        const int64_t nrows = p.cu ? p.T : (int64_t)p.B * p.Ld;
+        p.row_ptr[nrows] = dbase + carry_row;
     }
     __syncthreads();
     if (q < p.Nq) {
         int* myslot = slot + wave * Ld;
+        unsigned char* mytag = tag + wave * Ld;
         const unsigned long long below = (1ull << lane) - 1ull;
-        const int64_t s0 = ((int64_t)q * p.B + b) * p.Lq;
-        const int nbits = Ld > 1 ? 32 - __clz(Ld - 1) : 0;  // bits of a row index
 #pragma unroll
         for (int k = 0; k < kFillIt; ++k) {
             if (k * 64 >= p.Lq) break;  // uniform
             const int t = tk[k];
             const bool active = t >= 0;
-            // the lanes of this step holding the same row: one ballot per bit
-            unsigned long long mk = __ballot(active);
-            for (int bit = 0; bit < nbits; ++bit) {  // uniform
-                const bool one = (t >> bit) & 1;
-                const unsigned long long v = __ballot(one);
-                mk &= one ? v : ~v;
+            // Lanes of this step sharing a row: every active lane writes its id
+            // under its row and reads it back (the wave's LDS operations run in
+            // order); a lane that reads another id shares its row.  Only for
+            // those rows (about 2 of 64 lanes with random rows) the exact rank
+            // comes from one ballot of the row; a lane alone in its row has
+            // rank 0 and count 1.
+            if (active) mytag[t] = (unsigned char)lane;
+            // other lanes' writes: the tag must be read back from LDS, not forwarded
+            asm volatile("" ::: "memory");
+            const bool shared = active && mytag[t] != (unsigned char)lane;
+            unsigned long long todo = __ballot(shared);
+            int rank = 0, cnt = 1;
+            while (todo) {  // uniform
+                const int j = __builtin_ctzll(todo);
+                const int tj = __builtin_amdgcn_readlane(t, j);
+                const bool same = active && t == tj;
+                const unsigned long long m = __ballot(same);
+                if (same) {
+                    rank = __popcll(m & below);
+                    cnt = __popcll(m);
+                }
+                todo &= ~m;
             }
             if (active) {
-                // the wave's LDS operations run in order: every lane of the row
-                // reads the slot before its lowest lane advances it
+                // every lane of the row reads the slot before its lowest lane advances it
                 const int base = myslot[t];
-                const int rank = __popcll(mk & below);
-                p.col_idx[base + rank] = (int)(s0 + k * 64 + lane);
-                if (rank == 0) myslot[t] = base + __popcll(mk);
+                stage[base + rank] = (t << 14) | (wave << 10) | (k * 64 + lane);
+                if (rank == 0) myslot[t] = base + cnt;
             }
         }
+    }
+    __syncthreads();
+    // the group's carry_lo placed sources, in order; entry e of row t goes to e + delta[t]
+    const int64_t s_q0 = ((int64_t)qg * G * p.B + b) * p.Lq;  // source id of (query qg*G, document b, i = 0)
+    const int64_t s_qstep = (int64_t)p.B * p.Lq;
+    for (int e = tid; e < carry_lo; e += nt) {
+        const int v = stage[e];
+        const int t = v >> 14;
+        p.col_idx[e + delta[t]] = (int)(s_q0 + ((v >> 10) & 15) * s_qstep + (v & 1023));
     }
 }
 
@@ -562,8 +622,9 @@ __global__ __launch_bounds__(kGatherThreads) void dd_heavy(BwdParams p) {
 // Per step of DSTEP documents the gathers of all the group's RPG rows are in
 // flight together (RPG * DSTEP = 8 loads: 4 rows x 2 documents, or 1 row x 8
 // documents when there are few rows).  Packed corpus (VARLEN): lane j of a
-// group holds document b0 + j's first row and length; an empty document gives
-// weight 0 and reads a valid row.  Each row sums its terms in ascending b.
+// group holds document b0 + j's first row and length; an empty document, or
+// a negative argmax, gives weight 0 and reads a valid row.  Each row sums its
+// terms in ascending b.
 template <int ELEM, bool VARLEN, int RPG, int DSTEP>
 __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void dq_gather(BwdParams p, int rows_per_group) {
     const int l16 = threadIdx.x & 15;
@@ -611,10 +672,11 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
                 // document, or one starting at T, reads row T-1 with weight 0
                 const int r = (int)dstart + clamp_tok(araw[k], dlen > 0 ? dlen : 1);
                 tok[k] = r < (int)p.T ? r : (int)p.T - 1;
-                gv[k] = (ok[k] && lane_doc && dlen > 0) ? gv[k] : 0.f;
+                gv[k] = (ok[k] && lane_doc && dlen > 0 && araw[k] >= 0) ? gv[k] : 0.f;
             } else {
+                // a negative argmax (an empty document) selects nothing: weight 0
                 tok[k] = clamp_tok(araw[k], p.Ld);
-                gv[k] = (ok[k] && lane_doc) ? gv[k] : 0.f;
+                gv[k] = (ok[k] && lane_doc && araw[k] >= 0) ? gv[k] : 0.f;
             }
         }
         u32x4 raw[RPG][DSTEP];
@@ -714,7 +776,9 @@ __global__ __launch_bounds__(256) void dd_scatter(BwdParams p) {
             start = (int64_t)b * p.Ld;
             len = p.Ld;
         }
-        const int64_t row = start + clamp_tok(p.A[s], len);
+        const int a = p.A[s];
+        if (a < 0) continue;  // uniform per group: selects no row
+        const int64_t row = start + clamp_tok(a, len);
         const float gv = p.g[qb];
         const unsigned short* qrow = reinterpret_cast<const unsigned short*>(p.Q) + ((int64_t)q * p.Lq + i) * 128;
         float v[8];
@@ -785,21 +849,30 @@ hipError_t launch_dq(BwdParams p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int G>
+hipError_t launch_fill(const BwdParams& p, unsigned groups, hipStream_t stream) {
+    hipLaunchKernelGGL(csr_fill<G>, dim3(groups), dim3(64 * G), 0, stream, p);
+    return hipGetLastError();
+}
+
 template <int ELEM, bool VARLEN>
 hipError_t launch_bwd_elem(const BwdParams& p, hipStream_t stream) {
-    const int nthr = 64 * p.G;
     const unsigned groups = (unsigned)(8 * (((int64_t)p.B + 7) / 8) * p.NG);
     hipError_t e;
-    if (VARLEN) {
-        hipLaunchKernelGGL(csr_docbase, dim3(1), dim3(1024), 0, stream, p);
+    hipLaunchKernelGGL(csr_count, dim3(groups), dim3(64 * p.G), p.Ld * sizeof(int), stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.docbase) {
+        hipLaunchKernelGGL(csr_docscan, dim3(1), dim3(1024), 0, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(csr_count, dim3(groups), dim3(nthr), p.Ld * sizeof(int), stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(csr_scan, dim3(p.B), dim3(1024), 0, stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(csr_fill, dim3(groups), dim3(nthr), (size_t)p.G * p.Ld * 4, stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    switch (p.G) {
+        case 16: e = launch_fill<16>(p, groups, stream); break;
+        case 8: e = launch_fill<8>(p, groups, stream); break;
+        case 4: e = launch_fill<4>(p, groups, stream); break;
+        case 2: e = launch_fill<2>(p, groups, stream); break;
+        default: e = launch_fill<1>(p, groups, stream); break;
+    }
+    if (e != hipSuccess) return e;
     unsigned blocks;
     int rpg;
     const int64_t nrows = VARLEN ? p.T : (int64_t)p.B * p.Ld;
@@ -849,42 +922,47 @@ void magic_div(unsigned long long d, unsigned long long* magic, int* shift) {
 
 }  // namespace
 
-int bwd_group(int32_t Ld) {
-    if (Ld < 1 || Ld > kMaxLdBwd) return 0;
+int bwd_group(int32_t Nq, int32_t Ld) {
+    if (Ld < 1 || Ld > kMaxLdBwd || Nq < 1) return 0;
     int G = 16;
-    while (G > 1 && (int64_t)G * Ld > kMaxLdBwd) G >>= 1;
+    while (G > 1 && (int64_t)G * Ld > kFillSlots) G >>= 1;  // the fill's per (query, row) slots
+    while (G > 1 && G / 2 >= Nq) G >>= 1;                   // no idle query waves beyond Nq
     return G;
 }
 
-// Workspace layout (each part at a 256-byte boundary): the CSR counts
-// [B][NG][Ld] int32, the packed corpus' document bases [B+1] int32, the heavy
-// row list (count, then rows) int32, then the dQ chunk partial sums
-// [S][Nq*Lq][128] fp32 when dQ is split (S > 1).
+// Workspace layout, each part at a 256-byte boundary: the CSR counts
+// [B][NG][Ld] int32; the query groups' totals [B*NG] int32; the documents'
+// first slots [B+1] int32 (used when B*NG > kInlineDocTotals); the heavy-row
+// list (count, then rows) int32; the dQ chunk partial sums [S][Nq*Lq][128]
+// fp32 when dQ is split (S > 1).  Padded documents and a packed corpus (Ld =
+// its longest document) share it.
 namespace {
-size_t counts_bytes(int32_t Nq, int32_t B, int32_t Ld) {
-    const int G = bwd_group(Ld);
-    if (G == 0 || Nq < 1 || B < 1) return 0;
-    const int64_t NG = (Nq + G - 1) / G;
-    return (size_t)(B * NG * Ld * (int64_t)sizeof(int32_t));
-}
+struct WsLayout {
+    size_t counts, gtot, docbase, heavy, dq_part, total;
+};
 // a heavy row has more than kHeavy of the Nq*B*Lq sources
 int64_t max_heavy_rows(int32_t Nq, int32_t B, int32_t Lq) { return (int64_t)Nq * B * Lq / (kHeavy + 1); }
-size_t heavy_bytes(int32_t Nq, int32_t B, int32_t Lq) {
-    return align256((size_t)(1 + max_heavy_rows(Nq, B, Lq)) * sizeof(int32_t));
+bool ws_layout(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld, WsLayout* w) {
+    const int G = bwd_group(Nq, Ld);
+    if (G == 0 || B < 1 || Lq < 1) return false;
+    const int64_t NG = (Nq + G - 1) / G;
+    w->counts = 0;
+    w->gtot = w->counts + align256((size_t)(B * NG * Ld * (int64_t)sizeof(int32_t)));
+    w->docbase = w->gtot + align256((size_t)(B * NG * (int64_t)sizeof(int32_t)));
+    w->heavy = w->docbase + align256((size_t)(B + 1) * sizeof(int32_t));
+    w->dq_part = w->heavy + align256((size_t)(1 + max_heavy_rows(Nq, B, Lq)) * sizeof(int32_t));
+    w->total = w->dq_part + dq_part_bytes(Nq, Lq, B);
+    return true;
 }
 }  // namespace
 
 size_t bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld) {
-    const size_t c = counts_bytes(Nq, B, Ld);
-    if (c == 0 || Lq < 1) return 0;
-    return align256(c) + heavy_bytes(Nq, B, Lq) + dq_part_bytes(Nq, Lq, B);
+    WsLayout w;
+    return ws_layout(Nq, B, Lq, Ld, &w) ? w.total : 0;
 }
 
 size_t bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld) {
-    const size_t c = counts_bytes(Nq, B, max_Ld);
-    if (c == 0 || Lq < 1) return 0;
-    return align256(c) + align256((size_t)(B + 1) * sizeof(int32_t)) + heavy_bytes(Nq, B, Lq) +
-           dq_part_bytes(Nq, Lq, B);
+    return bwd_workspace_bytes(Nq, B, Lq, max_Ld);
 }
 
 size_t bwd_scatter_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq) {
@@ -922,31 +1000,28 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.Lq = a.Lq;
     p.B = a.B;
     p.Ld = a.Ld;
-    p.G = bwd_group(a.Ld);
+    p.G = bwd_group(a.Nq, a.Ld);
     p.NG = (a.Nq + p.G - 1) / p.G;
     p.dQ = a.dQ;
     p.dD = a.dD;
     p.row_ptr = a.row_ptr;
     p.col_idx = a.col_idx;
+    WsLayout w;
+    if (!ws_layout(a.Nq, a.B, a.Lq, a.Ld, &w)) return hipErrorInvalidValue;
     char* ws = static_cast<char*>(a.workspace);
-    p.ws = reinterpret_cast<int32_t*>(ws);
-    size_t off = align256(counts_bytes(a.Nq, a.B, a.Ld));
+    p.ws = reinterpret_cast<int32_t*>(ws + w.counts);
+    p.gtot = reinterpret_cast<int32_t*>(ws + w.gtot);
+    p.docbase = (int64_t)a.B * p.NG > kInlineDocTotals ? reinterpret_cast<int32_t*>(ws + w.docbase) : nullptr;
+    p.heavy = reinterpret_cast<int32_t*>(ws + w.heavy);
+    p.dq_part = reinterpret_cast<float*>(ws + w.dq_part);
     magic_div((unsigned long long)a.B * a.Lq, &p.magic, &p.shift);
     magic_div((unsigned long long)a.Lq, &p.magic_lq, &p.shift_lq);
     p.max_heavy = max_heavy_rows(a.Nq, a.B, a.Lq);
     if (a.cu_seqlens) {
         p.cu = a.cu_seqlens;
         p.T = a.T;
-        p.docbase = reinterpret_cast<int32_t*>(ws + off);
-        off += align256((size_t)(a.B + 1) * sizeof(int32_t));
-        p.heavy = reinterpret_cast<int32_t*>(ws + off);
-        off += heavy_bytes(a.Nq, a.B, a.Lq);
-        p.dq_part = reinterpret_cast<float*>(ws + off);
         return a.elem == kBF16 ? launch_bwd_elem<kBF16, true>(p, stream) : launch_bwd_elem<kF16, true>(p, stream);
     }
-    p.heavy = reinterpret_cast<int32_t*>(ws + off);
-    off += heavy_bytes(a.Nq, a.B, a.Lq);
-    p.dq_part = reinterpret_cast<float*>(ws + off);
     return a.elem == kBF16 ? launch_bwd_elem<kBF16, false>(p, stream) : launch_bwd_elem<kF16, false>(p, stream);
 }
 

@@ -12,7 +12,7 @@ enum ElemType { kF16 = 0, kBF16 = 1, kI8 = 2 };
 
 constexpr int kDim = 128;        // embedding width every kernel is built for
 constexpr int kMaxLq = 1024;     // query tokens one workgroup keeps on chip
-constexpr int kMaxLdBwd = 4096;  // document tokens the CSR fill kernel keeps in LDS
+constexpr int kMaxLdBwd = 4096;  // longest document the backward supports (CSR fill LDS)
 // Below this mean number of sources per dD row the atomic scatter is faster
 // than building the CSR map (measured on MI355X).
 constexpr double kScatterMaxSourcesPerRow = 0.5;
@@ -108,7 +108,7 @@ constexpr size_t kScratchBytes = (size_t)64 << 20;
 hipError_t scratch_address(void** out);
 
 // Queries per CSR group (one wave each) for a document length; 0 if unsupported.
-int bwd_group(int32_t Ld);
+int bwd_group(int32_t Nq, int32_t Ld);
 size_t bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld);
 size_t bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld);
 size_t bwd_scatter_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq);

@@ -143,18 +143,21 @@ def test_bwd_validation(kw, code):
 
 
 def test_workspace_bytes():
-    # one int32 count per (document, group of queries, row), then the heavy-row list: a count
-    # and room for every row that can hold more than 512 of the 64*64*1024 sources
+    # one int32 count per (document, group of queries, row); one total per (document, group);
+    # the documents' first slots (B + 1); the heavy-row list: a count and room for every row
+    # that can hold more than 512 of the 64*64*1024 sources; each part at a 256-byte boundary
     n = L.maxsim_bwd_workspace_bytes(64, 64, 1024, 1024)
     heavy = (1 + 64 * 64 * 1024 // 513) * 4
-    assert n == 64 * 16 * 1024 * 4 + (heavy + 255) // 256 * 256  # Ld = 1024 -> 4 queries per group
+    up = lambda x: (x + 255) // 256 * 256
+    # Ld = 1024 -> groups of 16 queries (16 * 1024 slots), 4 groups per document
+    assert n == 64 * 4 * 1024 * 4 + up(64 * 4 * 4) + up(65 * 4) + up(heavy)
     assert L.maxsim_bwd_workspace_bytes(0, 1, 1, 1) == 0
     assert L.maxsim_bwd_workspace_bytes(1, 1, 1, 5000) == 0
     assert bwd(wsb=n - 1, Nq=64, B=64, Lq=1024, Ld=1024) == bd.MAXSIM_ERR_WORKSPACE
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         s = L.maxsim_status_string(code).decode()
         assert s.startswith("MAXSIM_")
     assert "unknown" in L.maxsim_status_string(99).decode()
@@ -223,8 +226,9 @@ def test_bwd_varlen_workspace_bytes():
     # chunks for dQ.
     counts = 100 * 1 * 100 * 4  # 10 queries form one group of 16 at Ld = 100
     part = 12 * 320 * 128 * 4
-    assert L.maxsim_bwd_workspace_bytes(10, 100, 32, 100) == 40192 + 256 + part
-    assert L.maxsim_bwd_varlen_workspace_bytes(10, 100, 32, 100) == 40192 + 512 + 256 + part
+    # counts, group totals (100), document first slots (101), heavy list, dQ chunks
+    assert L.maxsim_bwd_workspace_bytes(10, 100, 32, 100) == 40192 + 512 + 512 + 256 + part
+    assert L.maxsim_bwd_varlen_workspace_bytes(10, 100, 32, 100) == 40192 + 512 + 512 + 256 + part
     assert counts <= 40192 < counts + 256
     assert L.maxsim_bwd_scatter_workspace_bytes(10, 100, 32) == part
     assert L.maxsim_bwd_scatter_workspace_bytes(10, 7, 32) == 256  # too few documents to split

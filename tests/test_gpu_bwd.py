@@ -64,7 +64,10 @@ def test_golden_hand_case(bd):
 
 
 SHAPES = [(1, 1, 1, 1), (2, 7, 3, 5), (3, 33, 4, 70), (9, 64, 5, 64), (17, 100, 3, 129), (4, 1024, 2, 1024),
-          (20, 32, 7, 300), (1, 5, 1, 4096)]
+          (20, 32, 7, 300), (1, 5, 1, 4096),
+          # groups of 8 and 4 queries (1025..4096-row documents), and more (document, group)
+          # pairs than the fill sums itself (the documents' first slots from their own scan)
+          (9, 40, 3, 1500), (5, 64, 2, 3000), (1, 32, 3000, 50), (33, 16, 150, 40)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
@@ -81,6 +84,28 @@ def test_chain_forward_argmax(bd, shape, dtn):
     else:
         g = np.random.default_rng(seed).standard_normal((Nq, B)).astype(np.float32)
     check_bwd(bd, Q, D, dtn, A, g, "%s %s" % (dtn, shape))
+
+
+@pytest.mark.parametrize("shape", [(5, 40, 7, 90), (2, 16, 2500, 20)], ids=["7docs", "2500docs"])
+@pytest.mark.parametrize("dtn", [inputs.F16, inputs.BF16])
+def test_forward_with_empty_documents_then_backward(bd, shape, dtn):
+    """Padded documents with d_lens = 0: the forward writes argmax -1 for every
+    token of them, and the backward fed the forward's own output drops those
+    sources (no CSR entry, no dQ term, zero dD rows), as the oracle does."""
+    Nq, Lq, B, Ld = shape
+    seed = 950 + B
+    Q = inputs.random_rows(seed, Nq * Lq, 128, dtn).reshape(Nq, Lq, 128)
+    D = inputs.random_rows(seed + 1, B * Ld, 128, dtn, stream=4).reshape(B, Ld, 128)
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, Ld + 1, size=B).astype(np.int32)
+    lens[rng.random(B) < 0.3] = 0
+    lens[1] = 0
+    s, a = bd.maxsim_fwd(to_dev(Q, dtn), to_dev(D, dtn), to_dev(lens))
+    torch.cuda.synchronize()
+    A = a.cpu().numpy()
+    assert np.all(A[:, lens == 0] == -1) and np.all(A[:, lens > 0] >= 0)
+    g = rng.standard_normal((Nq, B)).astype(np.float32)
+    check_bwd(bd, Q, D, dtn, A, g, "empty documents %s %s" % (dtn, shape))
 
 
 def test_hot_tokens(bd):

@@ -67,6 +67,10 @@ CASES = [
     (5, 1024, [1024, 7]),
     (20, 32, list(range(0, 40, 3))),
     (1, 5, [4096]),
+    # 2600 documents, a third of them empty: more (document, group) pairs than
+    # the fill sums itself, so the documents' first slots come from their scan
+    (2, 16, [int(x) for x in np.random.default_rng(26).integers(0, 31, size=2600) * (np.arange(2600) % 3 > 0)]),
+    (4, 48, [1500, 0, 2100, 40]),
 ]
 
 
