@@ -176,8 +176,9 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Row r of the per-document row maxima lives at r + r/32, so threads reading
-// the rows of consecutive queries (stride Lq) do not all hit one bank.
+// Row r of the per-document row maxima (and of the int8 query scales) lives
+// at r + r/32, so threads reading the rows of consecutive queries (stride Lq)
+// do not all hit one bank.
 __device__ __forceinline__ int rpad(int r) { return r + (r >> 5); }
 
 template <bool VARLEN>
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     // so the step barrier is the only one.
     __shared__ float rowmax_s[2][WT][RP];
     __shared__ int rowarg_s[ARGMAX ? 2 : 1][ARGMAX ? WT : 1][ARGMAX ? R : 1];
-    __shared__ float qsc_s[I8 ? R : 1];  // int8: the slab's query scales
+    __shared__ float qsc_s[I8 ? RP : 1];  // int8: the slab's query scales (row r at rpad(r))
     __shared__ int docpf[2][2];          // prefetched document bounds
 
     const int tid = threadIdx.x;
@@ -405,7 +406,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     }
 
     if constexpr (I8) {
-        for (int r = tid; r < nrows; r += NT) qsc_s[r] = p.q_scale[qrow0 + r];
+        for (int r = tid; r < nrows; r += NT) qsc_s[rpad(r)] = p.q_scale[qrow0 + r];
     }
 
     float m[QB];       // running exact maximum per lane and query block
@@ -856,7 +857,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             for (int ql = tid; ql < nq; ql += NT) {
                 float acc = 0.f;
                 for (int i = 0; i < ni; ++i) {
-                    const float v = row_max(par, ql * ni + i) * qsc_s[ql * ni + i];
+                    const float v = row_max(par, ql * ni + i) * qsc_s[rpad(ql * ni + i)];
                     acc = acc + v;
                 }
                 p.scores[(int64_t)(q0 + ql) * p.B + b] = acc;
