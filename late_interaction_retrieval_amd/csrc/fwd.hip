@@ -12,7 +12,7 @@
 //     "Kernel Family"): every document tile it reads is used against all R rows.
 //   * Documents stream HBM -> LDS in tiles (256 tokens in a two-buffer ring
 //     for fp16/bf16 32x32 blocks; 128 or 64 tokens in a three-buffer ring
-//     otherwise) of direct (global_load_lds) loads: the next tiles, possibly
+//     otherwise) of direct (buffer_load ... lds) loads: the next tiles, possibly
 //     of later documents, are in flight while the current one is contracted.
 //     LDS rows are XOR-swizzled by 16-byte chunk so the MFMA operand reads are
 //     bank-conflict free.
@@ -35,7 +35,7 @@
 //     so one wave's non-MFMA work overlaps the other's matrix work.
 //   * Masking (Algorithm 2): positions past the document's length are -inf
 //     before the maximum (or, where that cannot change the result, rows past
-//     the end repeat the document's first row and are folded unmasked).
+//     the end repeat the tile's first row and are folded unmasked).
 //   * Scores only, 32-token queries, packed corpus (ColBERT re-ranking):
 //     fwd_flat_kernel reads each stream's tokens as tiles that run across
 //     document boundaries and splits the fold where a document ends.
@@ -159,9 +159,32 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 typedef const __attribute__((address_space(4))) int32_t* cint_ptr;  // read-only for the kernel: scalar loads
+
+// Direct HBM -> LDS load (buffer_load ... lds) of `size` bytes per lane (4 or
+// 16): lane l's bytes [voff, voff + size) of the nbytes-long range at base
+// land at lds + l * size; bytes at or past nbytes read as zero without a
+// memory access.  base and nbytes must be wave-uniform (they form the buffer
+// descriptor).  The buffer form rather than global_load_lds: the compiler
+// counts a FLAT-encoded LDS load as LDS traffic of unknown order while it is
+// in flight, and then makes every LDS read wait for all earlier ones
+// (lgkmcnt(0)), so a stage's first MFMA waited for all eight of its operand
+// reads instead of the first.
+__device__ __forceinline__ void buffer_load_lds(const void* base, uint32_t nbytes, uint32_t voff, lptr_t lds, int size) {
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(nbytes);
+    // word 3 of a raw (stride 0) gfx9 descriptor: 32-bit data format
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n, 0x00020000);
+    if (size == 16) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, (int)voff, 0, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, (int)voff, 0, 0, 0);
+    }
+}
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also orders global
 // memory, which makes every wave drain its in-flight HBM -> LDS loads
@@ -421,9 +444,11 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
 
     // Direct HBM -> LDS loads of one tile into ring slot bf.  Every loading
     // wave issues exactly LPL (+1 for the scale waves) loads, so vmcnt bookkeeping is
-    // static; lanes whose token is past the document's end fetch the
-    // document's first row instead (in bounds, and a repeat of a value the
-    // maximum already sees), and the compute masks those tokens where needed.
+    // static; lanes whose token is past the document's end fetch the tile's
+    // first row instead (in bounds, and a repeat of a value the maximum
+    // already sees at a lower index), and the compute masks those tokens
+    // where needed.  The descriptor spans the tile's valid rows only, so an
+    // empty document's loads read zeros and touch no memory.
     const bool scale_wave = I8 && wave < SCW;
     // With two buffers the tile is loaded by the first wave of each SIMD
     // (waves 0 .. NW/2-1, each twice the even share), and the second wave
@@ -438,23 +463,24 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     static_assert(!I8 || SCW <= LW, "the scale waves are loading waves");
     const bool loader = wave < LW;
     auto issue_tile = [&](int bf, int64_t st, int ln, int tt) {
-        const int64_t safe = ln > 0 ? st : 0;
         if (!loader) return;  // uniform
+        const int64_t t0 = st + (int64_t)tt * TT;  // the tile's first row
+        int nv = ln - tt * TT;                     // its valid rows
+        nv = nv < 0 ? 0 : (nv > TT ? TT : nv);
 #pragma unroll
         for (int u = 0; u < LPL; ++u) {
             const int slot0 = (u * LW + wave) * 64;
             const int sl = slot0 + lane;
             const int row = sl / NCH;
             const int c = swz_chunk<NCH>(row, sl % NCH);
-            const int tk = tt * TT + row;
-            const int64_t grow = tk < ln ? st + tk : safe;
-            __builtin_amdgcn_global_load_lds((gptr_t)(p.D + grow * ROWB + c * 16), (lptr_t)&dtile[bf][slot0], 16, 0, 0);
+            const uint32_t r = row < nv ? row : 0;
+            buffer_load_lds(p.D + t0 * ROWB, (uint32_t)nv * ROWB, r * ROWB + c * 16, (lptr_t)&dtile[bf][slot0], 16);
         }
         if constexpr (I8) {
             if (scale_wave) {
-                const int tk = tt * TT + wave * 64 + lane;
-                const int64_t grow = tk < ln ? st + tk : safe;
-                __builtin_amdgcn_global_load_lds((gptr_t)(p.d_scale + grow), (lptr_t)&dsc[bf][wave * 64], 4, 0, 0);
+                const int row = wave * 64 + lane;
+                const uint32_t r = row < nv ? row : 0;
+                buffer_load_lds(p.d_scale + t0, (uint32_t)nv * 4, r * 4, (lptr_t)&dsc[bf][wave * 64], 4);
             }
         }
     };
@@ -720,8 +746,8 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             if (!I8 && WT == 1 && SPW % 2 == 0 && j == SPW - 1 && !last_tile) {
                 carry = true;  // full tile, the document goes on: the next step folds it
             } else if (j == nsub - 1) {  // drain: fold the last sub-tile (the only one that can be partial)
-                // Rows past the document's end were loaded as copies of its
-                // first row (issue_tile), so their values repeat that token's
+                // Rows past the document's end were loaded as copies of the
+                // tile's first row (issue_tile), so their values repeat that token's
                 // under a later index: they change no maximum, and with the
                 // strict in-lane update and the lower-index merge they never
                 // win an exact argmax either.  Only the keyed argmax, which
@@ -922,13 +948,11 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     const bool doc_wave = wave == NW - 1;
     auto prefetch_doc = [&](int slot, int b) {
         if (doc_wave && b < bend && lane < 2) {
-            const int32_t* src;
             if constexpr (VARLEN) {
-                src = p.cu + b + lane;
-            } else {
-                src = p.lens ? p.lens + b : nullptr;
+                buffer_load_lds(p.cu + b, 8, lane * 4, (lptr_t)&docpf[slot][0], 4);
+            } else if (p.lens) {
+                buffer_load_lds(p.lens + b, 4, 0, (lptr_t)&docpf[slot][0], 4);
             }
-            if (src) __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)&docpf[slot][0], 4, 0, 0);
         }
     };
     auto from_prefetch = [&](int slot, int b) {
@@ -1105,7 +1129,8 @@ __global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
     T1 = T1 < T0 ? T0 : T1;
     const int ntile = (int)((T1 - T0 + TT - 1) / TT);
 
-    // Tile k: tokens T0 + k*TT ... (past T1: the tile's first row again, in bounds, never folded).
+    // Tile k: tokens T0 + k*TT ... (past T1: the tile's first row again, in bounds, never folded;
+    // past the end of D: zeros, no access).
     // Loaded by the first wave of each SIMD, as in fwd_kernel.
     constexpr int LW = NW / 2, LPL = 2 * LPW;
     const bool loader = wave < LW;
@@ -1113,14 +1138,15 @@ __global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
         const int64_t st = T0 + (int64_t)k * TT;
         const int64_t ln = T1 - st;
         if (!loader) return;  // uniform
+        const int nv = ln < 0 ? 0 : (ln > TT ? TT : (int)ln);
 #pragma unroll
         for (int u = 0; u < LPL; ++u) {
             const int slot0 = (u * LW + wave) * 64;
             const int sl = slot0 + lane;
             const int row = sl / NCH;
             const int c = swz_chunk<NCH>(row, sl % NCH);
-            const int64_t grow = row < ln ? st + row : st;
-            __builtin_amdgcn_global_load_lds((gptr_t)(p.D + grow * 256 + c * 16), (lptr_t)&dtile[bf][slot0], 16, 0, 0);
+            const uint32_t r = row < nv ? row : 0;
+            buffer_load_lds(p.D + st * 256, (uint32_t)nv * 256, r * 256 + c * 16, (lptr_t)&dtile[bf][slot0], 16);
         }
     };
 
