@@ -151,6 +151,15 @@ template <int NCH>
 __device__ __forceinline__ int swz(int row, int c) {
     return row * NCH + swz_chunk<NCH>(row, c);
 }
+// The swizzle reads only the row's low four bits, so for an M-row sub-tile
+// (M a multiple of 16) swz(sb*M + lm, c) = sb*M*NCH + swz(lm, c): a per-lane
+// slot plus a per-sub-tile constant, which the compiler folds into the LDS
+// read's immediate offset when the sub-tile index is known.
+template <int NCH, int M>
+__device__ __forceinline__ int sub_slot(int sb, int lane_slot) {
+    static_assert(M % 16 == 0, "sub-tiles span whole swizzle periods");
+    return sb * (M * NCH) + lane_slot;
+}
 
 // s_waitcnt vmcnt(N) (other counters untouched), gfx9 encoding.
 template <int N>
@@ -373,9 +382,26 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets branches on it stay scalar
     const int wq = wave % WQ;
-    const int wt = wave / WQ;
+    // token-wave index: a compile-time 0 for int8 with one token-wave (the
+    // 16-wave argmax workgroups need it to stay within 128 VGPRs; fp16/bf16
+    // measured 2-3 % slower with it, so they keep the computed value)
+    const int wt = (I8 && WT == 1) ? 0 : wave / WQ;
     const int g = lane / M;    // lane group: k-chunks of the operands, token set of the result
     const int lm = lane % M;   // operand row / result column
+    int aslot[KS];             // LDS slot of operand chunk s of row lm of a sub-tile
+#pragma unroll
+    for (int s = 0; s < KS; ++s) aslot[s] = swz<NCH>(lm, g * KS + s);
+    // Operand chunk s of row lm of sub-tile sb in ring slot bf.  int8 reads it
+    // at the per-lane slot plus the sub-tile's constant (30 fewer VGPRs, and
+    // room for 16-wave workgroups); fp16/bf16 keep the full swizzle per read,
+    // which compiles to the same reads with a schedule measured no slower.
+    auto opnd = [&](int bf, int sb, int s) -> u32x4 {
+        if constexpr (I8) {
+            return dtile[bf][sub_slot<NCH, M>(sb, aslot[s])];
+        } else {
+            return dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
+        }
+    };
 
     const int blk = blockIdx.x;
     const int xcd = blk & 7;
@@ -513,7 +539,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                 const f32x4 sc = *reinterpret_cast<const f32x4*>(&dsc[bf][sb * M + 4 * g]);
                 u32x4 a[KS];
 #pragma unroll
-                for (int s = 0; s < KS; ++s) a[s] = dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
+                for (int s = 0; s < KS; ++s) a[s] = opnd(bf, sb, s);
 #pragma unroll
                 for (int cb = 0; cb < QB; ++cb) {
                     Acc acc = MM::zero();
@@ -533,7 +559,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             for (int s = 0; s < KS; ++s) {
                 u32x4 a[NS];
 #pragma unroll
-                for (int n = 0; n < NS; ++n) a[n] = dtile[bf][swz<NCH>((sb0 + n) * M + lm, g * KS + s)];
+                for (int n = 0; n < NS; ++n) a[n] = opnd(bf, sb0 + n, s);
 #pragma unroll
                 for (int cb = 0; cb < QB; ++cb)
 #pragma unroll
@@ -633,7 +659,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     auto stage = [&](int bf, int sb, Acc* cur, const Acc* prev, const f32x4& sc_prev, bool has_prev, int gprev) {
         u32x4 a[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) a[s] = dtile[bf][swz<NCH>(sb * M + lm, g * KS + s)];
+        for (int s = 0; s < KS; ++s) a[s] = opnd(bf, sb, s);
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb) cur[cb] = MM::zero();
         float kt[QB];
@@ -1654,8 +1680,15 @@ hipError_t dispatch_shape(const FwdArgs& a, hipStream_t stream) {
     }
     // Otherwise one persistent workgroup per CU holding a slab of query rows.
     if constexpr (ELEM == kI8) {
-        // 1024 rows: 8 waves x 128 rows, 16x16x64 int8 blocks
-        return launch_cfg<ELEM, 16, 8, 8, 1, 16, 1, 2, ARGMAX, VARLEN>(a, stream, 256);
+        // 1024-row slabs in 16x16x64 int8 blocks.  Scores only: 8 waves x 128
+        // rows.  With the argmax (two compares and selects more per value):
+        // 16 waves x 64 rows, 4 waves per SIMD, 6 % faster there (1.2 % slower
+        // without it).
+        if constexpr (ARGMAX) {
+            return launch_cfg<ELEM, 16, 4, 16, 1, 16, 1, 2, ARGMAX, VARLEN>(a, stream, 256);
+        } else {
+            return launch_cfg<ELEM, 16, 8, 8, 1, 16, 1, 2, ARGMAX, VARLEN>(a, stream, 256);
+        }
     } else {
         if (a.Lq > 512 && a.Lq <= 768) {
             // 768-row slabs of whole queries: 8 waves x 96 rows, 2 waves per SIMD
