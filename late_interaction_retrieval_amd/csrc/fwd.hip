@@ -904,11 +904,35 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                 p.argmax[((int64_t)(q0 + ql) * p.B + b) * Lq + i] = row_arg(par, r);
             }
         }
-        if constexpr (I8) {
-            // Exact epilogue: v_i = fl32(m_i * q_scale_i), summed in ascending i.
+        if constexpr (I8 && ARGMAX) {
+            // Exact epilogue: v_i = fl32(m_i * q_scale_i), summed in ascending i,
+            // one thread per query.
             for (int ql = tid; ql < nq; ql += NT) {
                 float acc = 0.f;
                 for (int i = 0; i < ni; ++i) {
+                    const float v = row_max(par, ql * ni + i) * qsc_s[rpad(ql * ni + i)];
+                    acc = acc + v;
+                }
+                p.scores[(int64_t)(q0 + ql) * p.B + b] = acc;
+            }
+        } else if constexpr (I8) {
+            // The same sums, by the second wave (the first is a loading wave
+            // and carried this latency-bound loop on the step's critical
+            // path), with 8 rows read ahead of the serial adds: 1.6 % faster.
+            // (With the argmax, 16 waves at the 128-VGPR limit, this measured
+            // 2.5 % slower, so that path keeps the plain loop above.)
+            const int first = (tid + NT - (NW > 1 ? 64 : 0)) % NT;  // a rotation of the thread ids
+            for (int ql = first; ql < nq; ql += NT) {
+                float acc = 0.f;
+                int i = 0;
+                for (; i + 8 <= ni; i += 8) {
+                    float v[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) v[k] = row_max(par, ql * ni + i + k) * qsc_s[rpad(ql * ni + i + k)];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) acc = acc + v[k];
+                }
+                for (; i < ni; ++i) {
                     const float v = row_max(par, ql * ni + i) * qsc_s[rpad(ql * ni + i)];
                     acc = acc + v;
                 }
