@@ -995,7 +995,9 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     // shared with LDS and returns out of order) and no vector load into
     // registers sits in the loop.  Slot k&1 is written at the end of step k and
     // read at the start of step k+1.
-    const bool doc_wave = wave == NW - 1;
+    // (a loading wave when some waves skip the step-end wait: its wait retires the prefetch)
+    constexpr bool LATE = I8 && SPLIT_LOADS;
+    const bool doc_wave = wave == (LATE ? 0 : NW - 1);
     auto prefetch_doc = [&](int slot, int b) {
         if (doc_wave && b < bend && lane < 2) {
             if constexpr (VARLEN) {
@@ -1081,30 +1083,50 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     int par = 0;          // parity of the next document to finish
     int pend = -1;        // document whose outputs are parked in rowmax_s[par ^ 1]
     bool hasn = cs[NBUF - 1].b < bend;  // the newest tile (cs[NBUF-1]) exists
+    // int8 with split loads: the waves that issue no tile loads run a step's
+    // bookkeeping (the next tile's descriptor, the previous document's
+    // stores) after their contraction rather than before it, so each SIMD's
+    // matrix pipe has a wave to feed it from the step's start; issuing no
+    // loads, they need no wait for the next tile either (int8 scores -1.3 %;
+    // fp16/bf16 measured 0.4-0.7 % slower with it and keep the plain order).
+    const bool late = LATE && !loader;  // uniform
+    auto next_tile = [&]() {
+        const bool hasl = cs[NBUF - 2].b < bend;
+        cs[NBUF - 1] = hasl ? advance(step & 1, cs[NBUF - 2]) : cs[NBUF - 2];
+        hasn = hasl && cs[NBUF - 1].b < bend;
+    };
     while (true) {
         const bool has0 = cs[0].b < bend;
-        if (pend >= 0) {  // stores first: they must be older than this step's loads
+        if (!late && pend >= 0) {  // stores first: they must be older than this step's loads
             epilogue_out(pend, par ^ 1);
             pend = -1;
         }
-        if (step > 0) {
-            const bool hasl = cs[NBUF - 2].b < bend;
-            cs[NBUF - 1] = hasl ? advance(step & 1, cs[NBUF - 2]) : cs[NBUF - 2];
-            hasn = hasl && cs[NBUF - 1].b < bend;
+        if (step > 0 && !late) {
+            next_tile();
             if (hasn) prefetch_doc((step + 1) & 1, cs[NBUF - 1].b + bstep);
             if (loads && hasn) {
                 const int nb = buf + NBUF - 1;
                 issue_tile(nb >= NBUF ? nb - NBUF : nb, cs[NBUF - 1].start, cs[NBUF - 1].len, cs[NBUF - 1].t);
             }
         }
-        if (!has0) break;  // nothing issued or pending past here (has0 false => hasn false)
+        if (!has0) {  // nothing issued or pending past here (has0 false => hasn false)
+            if (pend >= 0) epilogue_out(pend, par ^ 1);  // a late wave's last document
+            break;
+        }
         if (cs[0].t < cs[0].ntiles) compute_tile(buf, cs[0].t, cs[0].len, cs[0].t + 1 >= cs[0].ntiles);
+        if (late) {
+            if (pend >= 0) {
+                epilogue_out(pend, par ^ 1);
+                pend = -1;
+            }
+            if (step > 0) next_tile();
+        }
         if (cs[0].t + 1 >= cs[0].ntiles) {
             epilogue_merge(par, cs[0].b);
             pend = cs[0].b;
             par ^= 1;
         }
-        if (loads) {
+        if (loads && !late) {
             if (hasn) {
                 wait_next_tile();
             } else {
