@@ -50,7 +50,10 @@ def test_golden_hand_case(bd):
 
 
 SHAPES = [(1, 1, 4, (1, 3)), (2, 7, 9, (0, 40)), (3, 32, 20, (32, 512)), (40, 32, 13, (1, 100)),
-          (1, 300, 5, (10, 600)), (2, 1024, 3, (100, 200))]
+          (1, 300, 5, (10, 600)), (2, 1024, 3, (100, 200)),
+          # more queries in a slab than threads in the workgroup (single-token queries:
+          # the per-query sums wrap around the workgroup), and two slabs of 512 queries
+          (600, 1, 7, (1, 300)), (520, 2, 3, (5, 90))]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
