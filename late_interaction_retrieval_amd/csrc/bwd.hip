@@ -164,12 +164,13 @@ __device__ __forceinline__ void block_exscan2(int x, int y, int* red, int& ex, i
 // heavy-row list that dd_owner appends to after the fill.
 __global__ __launch_bounds__(1024) void csr_count(BwdParams p) {
     extern __shared__ int hist[];  // [Ld]
-    __shared__ int red[16];
+    __shared__ int total;          // the group's sources that select a row
     if (blockIdx.x == 0 && threadIdx.x == 0) p.heavy[0] = 0;
     int b, qg;
     if (!doc_group(p, b, qg)) return;  // uniform
     const int nt = blockDim.x;
     for (int t = threadIdx.x; t < p.Ld; t += nt) hist[t] = 0;
+    if (threadIdx.x == 0) total = 0;
     __syncthreads();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int q = qg * p.G + wave;
@@ -187,10 +188,13 @@ __global__ __launch_bounds__(1024) void csr_count(BwdParams p) {
             }
         }
     }
-    n = block_sum(n, red);  // (its barriers also order the histogram)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
+    if (lane == 0 && n > 0) atomicAdd(&total, n);
+    __syncthreads();
     int32_t* out = p.ws + ((int64_t)b * p.NG + qg) * p.Ld;
     for (int t = threadIdx.x; t < p.Ld; t += nt) out[t] = hist[t];
-    if (threadIdx.x == 0) p.gtot[(int64_t)b * p.NG + qg] = n;
+    if (threadIdx.x == 0) p.gtot[(int64_t)b * p.NG + qg] = total;
 }
 
 // With many documents the fill takes each document's first col_idx slot from
@@ -229,36 +233,58 @@ __global__ __launch_bounds__(1024) void csr_docscan(BwdParams p) {
 //      consecutive threads: each row's run of the group is contiguous in
 //      col_idx, so a wave's stores cover a few runs instead of 64 scattered
 //      words.
-// LDS: G*Ld int (per query and row: counts, then slots), Ld int (per row:
-// global slot minus local slot), G*Lq int (the placed sources, packed as
-// row << 14 | query << 10 | i), G*Ld bytes (per query and row: a lane tag).
+// LDS, sized to the shape at launch (fill_lds_bytes): G*Ld int (per query and
+// row: counts, then slots), Ld int (per row: global slot minus local slot),
+// G*Lq int (the placed sources, packed as row << 14 | query << 10 | i), G*Ld
+// bytes (per query and row: a lane tag).  Sized to the largest shapes instead,
+// the arrays held one workgroup per CU, and short queries over many short
+// documents (4000 workgroups of 512 sources) ran 2.6x slower.
 constexpr int kFillIt = kMaxLq / 64;
 constexpr int kFillSlots = 16384;  // G * Ld of a query group (bwd_group keeps it within this)
+constexpr int kFillPre = 8;        // query groups per document whose counts the fill loads up front
 
-template <int G>
+size_t fill_lds_bytes(int G, int Ld, int Lq) {
+    return ((size_t)G * Ld + Ld + (size_t)G * Lq) * sizeof(int) + (((size_t)G * Ld + 3) & ~(size_t)3);
+}
+
+// KIT: 64-source steps per query (Lq <= 64 * KIT); short queries take fewer
+// registers, so more workgroups share a CU.
+template <int G, int KIT>
 __global__ __launch_bounds__(64 * G) void csr_fill(BwdParams p) {
-    constexpr int kLdMax = kFillSlots / G < kMaxLdBwd ? kFillSlots / G : kMaxLdBwd;  // G * Ld <= kFillSlots
-    __shared__ int slot[G * kLdMax];             // [G][Ld]
-    __shared__ int delta[kLdMax];                // [Ld]
-    __shared__ int stage[G * kMaxLq];            // [G*Lq]
-    __shared__ unsigned char tag[G * kLdMax];    // [G][Ld]
+    extern __shared__ int lds[];
     __shared__ int red[32];
+    const int Ld = p.Ld, NG = p.NG;
+    int* slot = lds;                                                           // [G][Ld]
+    int* delta = slot + G * Ld;                                                // [Ld]
+    int* stage = delta + Ld;                                                   // [G*Lq]
+    unsigned char* tag = reinterpret_cast<unsigned char*>(stage + G * p.Lq);  // [G][Ld]
     int b, qg;
     if (!doc_group(p, b, qg)) return;  // uniform
     const int tid = threadIdx.x, nt = blockDim.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int Ld = p.Ld, NG = p.NG;
     const int q = qg * G + wave;
     int64_t rstart;
     int len;
     doc_rows(p, b, rstart, len);
     const int32_t* a = p.A + ((int64_t)q * p.B + b) * p.Lq;
-    int tk[kFillIt];  // the row each of this lane's sources selects, or -1
+    int tk[KIT];  // the row each of this lane's sources selects, or -1
 #pragma unroll
-    for (int k = 0; k < kFillIt; ++k) {
+    for (int k = 0; k < KIT; ++k) {
         const int i = k * 64 + lane;
         tk[k] = (q < p.Nq && i < p.Lq) ? src_row(a[i], len) : -1;
     }
+    // The first row chunk's per-group counts (every group of a document up to
+    // kFillPre) are loaded now, with the argmax, rather than after the
+    // histogram's barrier: with short queries a workgroup holds a few hundred
+    // sources and that second round trip was a large part of its time.
+    // (Short queries only: long ones have work enough to hide it, and the
+    // registers would cost them a workgroup per CU.)
+    constexpr int NPRE = KIT <= 4 ? kFillPre : 1;
+    const int32_t* cnt = p.ws + (int64_t)b * NG * Ld;
+    const bool pre = KIT <= 4 && NG <= NPRE;  // uniform
+    int cpre[NPRE];
+#pragma unroll
+    for (int g = 0; g < NPRE; ++g) cpre[g] = (pre && g < NG && tid < Ld) ? cnt[(int64_t)g * Ld + tid] : 0;
     // the document's first slot
     int dbase;
     if (p.docbase) {
@@ -271,21 +297,28 @@ __global__ __launch_bounds__(64 * G) void csr_fill(BwdParams p) {
     for (int e = tid; e < G * Ld; e += nt) slot[e] = 0;
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kFillIt; ++k)
+    for (int k = 0; k < KIT; ++k)
         if (tk[k] >= 0) atomicAdd(&slot[wave * Ld + tk[k]], 1);
     __syncthreads();
     // per row t: local slots of the group's queries, and the global run start
-    const int32_t* cnt = p.ws + (int64_t)b * NG * Ld;
     int carry_lo = 0, carry_row = 0;
     for (int t0 = 0; t0 < Ld; t0 += nt) {  // uniform
         const int t = t0 + tid;
         int gc = 0, rowtot = 0, before = 0;
         if (t < Ld) {
             for (int w = 0; w < G; ++w) gc += slot[w * Ld + t];
-            for (int g = 0; g < NG; ++g) {
-                const int c = cnt[(int64_t)g * Ld + t];
-                rowtot += c;
-                before += g < qg ? c : 0;
+            if (pre && t0 == 0) {
+#pragma unroll
+                for (int g = 0; g < NPRE; ++g) {
+                    rowtot += cpre[g];
+                    before += g < qg ? cpre[g] : 0;
+                }
+            } else {
+                for (int g = 0; g < NG; ++g) {
+                    const int c = cnt[(int64_t)g * Ld + t];
+                    rowtot += c;
+                    before += g < qg ? c : 0;
+                }
             }
         }
         int ex_lo, ex_row, tot_lo, tot_row;
@@ -314,7 +347,7 @@ __global__ __launch_bounds__(64 * G) void csr_fill(BwdParams p) {
         unsigned char* mytag = tag + wave * Ld;
         const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-        for (int k = 0; k < kFillIt; ++k) {
+        for (int k = 0; k < KIT; ++k) {
             if (k * 64 >= p.Lq) break;  // uniform
             const int t = tk[k];
             const bool active = t >= 0;
@@ -849,10 +882,19 @@ hipError_t launch_dq(BwdParams p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int G, int KIT>
+hipError_t launch_fill_kit(const BwdParams& p, unsigned groups, hipStream_t stream) {
+    hipLaunchKernelGGL((csr_fill<G, KIT>), dim3(groups), dim3(64 * G), fill_lds_bytes(G, p.Ld, p.Lq), stream, p);
+    return hipGetLastError();
+}
 template <int G>
 hipError_t launch_fill(const BwdParams& p, unsigned groups, hipStream_t stream) {
-    hipLaunchKernelGGL(csr_fill<G>, dim3(groups), dim3(64 * G), 0, stream, p);
-    return hipGetLastError();
+    static_assert(kFillIt == 16, "steps per query: 1, 2, 4, 8 or 16");
+    if (p.Lq <= 64) return launch_fill_kit<G, 1>(p, groups, stream);
+    if (p.Lq <= 128) return launch_fill_kit<G, 2>(p, groups, stream);
+    if (p.Lq <= 256) return launch_fill_kit<G, 4>(p, groups, stream);
+    if (p.Lq <= 512) return launch_fill_kit<G, 8>(p, groups, stream);
+    return launch_fill_kit<G, 16>(p, groups, stream);
 }
 
 template <int ELEM, bool VARLEN>
@@ -922,9 +964,13 @@ void magic_div(unsigned long long d, unsigned long long* magic, int* shift) {
 
 }  // namespace
 
-int bwd_group(int32_t Nq, int32_t Ld) {
+int bwd_group(int32_t Nq, int32_t Lq, int32_t Ld) {
     if (Ld < 1 || Ld > kMaxLdBwd || Nq < 1) return 0;
-    int G = 16;
+    // Groups of 16 queries for long queries; 8 for short ones (Lq <= 256),
+    // whose workgroups hold few sources each: there smaller workgroups, more
+    // of them per CU, measured 12 % faster at 64 x 32-token queries over 1000
+    // documents, and 16 stays 1 % faster for 1024-token queries.
+    int G = Lq > 256 ? 16 : 8;
     while (G > 1 && (int64_t)G * Ld > kFillSlots) G >>= 1;  // the fill's per (query, row) slots
     while (G > 1 && G / 2 >= Nq) G >>= 1;                   // no idle query waves beyond Nq
     return G;
@@ -943,7 +989,7 @@ struct WsLayout {
 // a heavy row has more than kHeavy of the Nq*B*Lq sources
 int64_t max_heavy_rows(int32_t Nq, int32_t B, int32_t Lq) { return (int64_t)Nq * B * Lq / (kHeavy + 1); }
 bool ws_layout(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld, WsLayout* w) {
-    const int G = bwd_group(Nq, Ld);
+    const int G = bwd_group(Nq, Lq, Ld);
     if (G == 0 || B < 1 || Lq < 1) return false;
     const int64_t NG = (Nq + G - 1) / G;
     w->counts = 0;
@@ -1000,7 +1046,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.Lq = a.Lq;
     p.B = a.B;
     p.Ld = a.Ld;
-    p.G = bwd_group(a.Nq, a.Ld);
+    p.G = bwd_group(a.Nq, a.Lq, a.Ld);
     p.NG = (a.Nq + p.G - 1) / p.G;
     p.dQ = a.dQ;
     p.dD = a.dD;

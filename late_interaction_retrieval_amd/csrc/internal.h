@@ -108,7 +108,7 @@ constexpr size_t kScratchBytes = (size_t)64 << 20;
 hipError_t scratch_address(void** out);
 
 // Queries per CSR group (one wave each) for a document length; 0 if unsupported.
-int bwd_group(int32_t Nq, int32_t Ld);
+int bwd_group(int32_t Nq, int32_t Lq, int32_t Ld);
 size_t bwd_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t Ld);
 size_t bwd_varlen_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq, int32_t max_Ld);
 size_t bwd_scatter_workspace_bytes(int32_t Nq, int32_t B, int32_t Lq);

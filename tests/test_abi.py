@@ -224,12 +224,12 @@ def test_bwd_varlen_workspace_bytes():
     # entries), then the dQ chunk sums, each at a 256-byte boundary.  320 query rows fill 10
     # gather workgroups, so the 100 documents are split into min(ceil(512 / 10), 100 // 8) = 12
     # chunks for dQ.
-    counts = 100 * 1 * 100 * 4  # 10 queries form one group of 16 at Ld = 100
+    counts = 100 * 2 * 100 * 4  # 10 short queries form two groups of 8 at Ld = 100
     part = 12 * 320 * 128 * 4
-    # counts, group totals (100), document first slots (101), heavy list, dQ chunks
-    assert L.maxsim_bwd_workspace_bytes(10, 100, 32, 100) == 40192 + 512 + 512 + 256 + part
-    assert L.maxsim_bwd_varlen_workspace_bytes(10, 100, 32, 100) == 40192 + 512 + 512 + 256 + part
-    assert counts <= 40192 < counts + 256
+    # counts, group totals (200), document first slots (101), heavy list, dQ chunks
+    assert L.maxsim_bwd_workspace_bytes(10, 100, 32, 100) == 80128 + 1024 + 512 + 256 + part
+    assert L.maxsim_bwd_varlen_workspace_bytes(10, 100, 32, 100) == 80128 + 1024 + 512 + 256 + part
+    assert counts <= 80128 < counts + 256
     assert L.maxsim_bwd_scatter_workspace_bytes(10, 100, 32) == part
     assert L.maxsim_bwd_scatter_workspace_bytes(10, 7, 32) == 256  # too few documents to split
     assert L.maxsim_bwd_scatter_workspace_bytes(64, 64, 1024) == 256  # 65536 rows fill the chip: no split
