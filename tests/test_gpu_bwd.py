@@ -67,7 +67,12 @@ SHAPES = [(1, 1, 1, 1), (2, 7, 3, 5), (3, 33, 4, 70), (9, 64, 5, 64), (17, 100, 
           (20, 32, 7, 300), (1, 5, 1, 4096),
           # groups of 8 and 4 queries (1025..4096-row documents), and more (document, group)
           # pairs than the fill sums itself (the documents' first slots from their own scan)
-          (9, 40, 3, 1500), (5, 64, 2, 3000), (1, 32, 3000, 50), (33, 16, 150, 40)]
+          (9, 40, 3, 1500), (5, 64, 2, 3000), (1, 32, 3000, 50), (33, 16, 150, 40),
+          # every number of 64-source steps per query in the fill (Lq 65 .. 1024), groups of 8
+          # (Lq <= 256) and 16, and the largest fill LDS: 8 x 2048 and 16 x 1024 (query, row)
+          # slots, and 4 queries per group at 4096 rows
+          (20, 65, 3, 600), (40, 256, 2, 2048), (17, 257, 2, 700), (9, 513, 2, 300),
+          (33, 1024, 2, 1024), (9, 1024, 2, 4096)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
