@@ -71,6 +71,10 @@ CASES = [
     # the fill sums itself, so the documents' first slots come from their scan
     (2, 16, [int(x) for x in np.random.default_rng(26).integers(0, 31, size=2600) * (np.arange(2600) % 3 > 0)]),
     (4, 48, [1500, 0, 2100, 40]),
+    # the fill's step counts and group sizes at its largest LDS (G x max_Ld = 16384), and
+    # 40 short queries (groups of 8) over 1200 ragged documents
+    (12, 200, [2048, 17, 0]), (17, 300, [700, 0, 512, 33]), (9, 600, [1024, 5, 900]),
+    (40, 32, [int(x) for x in np.random.default_rng(40).integers(0, 181, size=1200)]),
 ]
 
 
