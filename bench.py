@@ -378,10 +378,15 @@ def run_workload(name, args, cpu_seconds, want_argmax=None):
         # and read back, row_ptr, upstream gradient
         bwd_bytes = (4 * Nq * B * Lq + 2 * d * (Nq * Lq + rows) + 4 * d * (Nq * Lq + rows)
                      + 2 * 4 * Nq * B * Lq + 4 * (rows + 1) + 4 * Nq * B)
+        # What actually moves: every source gathers one Q row (for dD) and one D row
+        # (for dQ), 2 * d bytes each, from L2 or the memory-side cache.
+        gathered = 2 * (2 * d) * Nq * B * Lq
         extra["bwd"] = {"avg_ms": round(b_avg, 5), "algorithmic_bytes": bwd_bytes,
                         "hbm_gbs": round(bwd_bytes / (b_avg * 1e-3) / 1e9, 1),
                         "hbm_frac": round(bwd_bytes / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "bound": "hbm", "timed": "HIP events around the backward's launches"}
+                        "bound": "hbm", "timed": "HIP events around the backward's launches",
+                        "row_gather_bytes": gathered,
+                        "row_gather_gbs": round(gathered / (b_avg * 1e-3) / 1e9, 1)}
 
     cpu = None
     if not args.no_cpu_baseline and cpu_seconds > 0:
