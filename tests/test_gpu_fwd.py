@@ -159,6 +159,33 @@ def test_skewed_corpus_stream_split(bd, shape):
 
 
 @pytest.mark.parametrize("dtn", [inputs.F16, inputs.BF16])
+@pytest.mark.parametrize("Lq", [64, 600])
+def test_very_long_documents(bd, dtn, Lq):
+    """Documents of 100000 and 70000 tokens (390 and 274 tiles each) beside a
+    5-token one: tile offsets and sub-tile codes far from zero, one document
+    per stream, packed and padded (with d_lens) bit for bit."""
+    Nq = 2
+    lens = np.array([100000, 5, 70000], np.int32)
+    cu = inputs.cu_seqlens(lens)
+    Q = inputs.random_rows(31 + Lq, Nq * Lq, 128, dtn).reshape(Nq, Lq, 128)
+    Dp = inputs.random_rows(32 + Lq, int(cu[-1]), 128, dtn, stream=4)
+    s, a = bd.maxsim_fwd_varlen(to_dev(Q, dtn), to_dev(Dp, dtn), to_dev(cu), int(lens.max()))
+    torch.cuda.synchronize()
+    s, a = s.cpu().numpy(), a.cpu().numpy()
+    s_ref, a_ref, m_ref = oracle.fwd_varlen(Q, Dp, cu, oracle_dtype(dtn), want_rowmax=True)
+    where = "long documents %s Lq %d" % (dtn, Lq)
+    check_scores(s, s_ref, Lq, where)
+    check_argmax(a, a_ref, m_ref, oracle.sim_at(Q, Dp, cu, oracle_dtype(dtn), a), lens, where)
+    # padded: the same rows in [3, 100000] with d_lens
+    Dpad = np.zeros((3, int(lens.max()), 128), Dp.dtype)
+    for b in range(3):
+        Dpad[b, :lens[b]] = Dp[cu[b]:cu[b + 1]]
+    s2, a2 = bd.maxsim_fwd(to_dev(Q, dtn), to_dev(Dpad, dtn), to_dev(lens))
+    torch.cuda.synchronize()
+    assert np.array_equal(s2.cpu().numpy(), s) and np.array_equal(a2.cpu().numpy(), a), where + ": padded differs"
+
+
+@pytest.mark.parametrize("dtn", [inputs.F16, inputs.BF16])
 def test_first_token_max_ragged_tails(bd, dtn):
     """Every document starts with the token closest to every query row, with
     partial 32-token sub-tiles.  Rows past a document's end are read as copies
