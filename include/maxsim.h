@@ -110,7 +110,10 @@ int maxsim_fwd_varlen(const void* Q, const void* D_packed, const int32_t* cu_seq
  *     v_i    = fl32(m_i * q_scale[q,i])
  *     score  = fp32 sum of v_i in ascending i, no fused multiply-add
  *   Q [Nq, Lq, d] int8, q_scale [Nq, Lq] fp32 (> 0)
- *   D_packed [T, d] int8, d_scale [T] fp32 (> 0), cu_seqlens as above.
+ *   D_packed [T, d] int8, d_scale [T] fp32 in [2^-125, 2^100], cu_seqlens as above.
+ * The d_scale range is what the kernel's exact arithmetic needs (it forms
+ * fl32(dot_ij * d_scale[j]) / 2 for negative dot_ij and doubles the maximum
+ * back); the quantiser's scales (max|x| / 127, or 1) lie far inside it.
  */
 int maxsim_fwd_i8(const int8_t* Q, const float* q_scale, const int8_t* D_packed,
                   const float* d_scale, const int32_t* cu_seqlens, int32_t Nq, int32_t Lq,

@@ -36,6 +36,10 @@
 //   * Masking (Algorithm 2): positions past the document's length are -inf
 //     before the maximum (or, where that cannot change the result, rows past
 //     the end repeat the tile's first row and are folded unmasked).
+//   * int8 (Section 4.3): each value fl32(dot * d_scale) comes from one fused
+//     multiply-add on an accumulator started at the bits of 2^23, and each
+//     query's exact sum runs in ascending row order at raised wave priority,
+//     by a thread per query or, for queries of 64 rows or more, by a wave.
 //   * Scores only, 32-token queries, packed corpus (ColBERT re-ranking):
 //     fwd_flat_kernel reads each stream's tokens as tiles that run across
 //     document boundaries and splits the fold where a document ends.
@@ -358,6 +362,10 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     // is kept separately.  int8 (bit-exact) and 16x16 blocks compare exactly.
     constexpr bool KEYED = ARGMAX && !I8 && M == 32;
     constexpr unsigned KMASK = VPL - 1;
+    // int8 with one token-wave: a document's merge parks each row's term
+    // v_i = fl32(m_i * q_scale_i) rather than its maximum (no later merge
+    // compares maxima), so the serial per-query sums read one value per row.
+    constexpr bool I8_TERMS = I8 && WT == 1;
 
     // Ring of NBUF tile buffers: tile k is contracted while tiles k+1 ..
     // k+NBUF-1 are in flight.
@@ -531,25 +539,9 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     auto subtiles = [&](auto ns_tag, auto mask_tag, int bf, int sb0, int tok0, int ln, int gsub0) {
         constexpr int NS = decltype(ns_tag)::value;
         constexpr bool MASK = decltype(mask_tag)::value;
+        static_assert(!I8, "int8 always takes the pipelined path");
         float v[NS][QB][VPL];
-        if constexpr (I8) {
-#pragma unroll
-            for (int n = 0; n < NS; ++n) {
-                const int sb = sb0 + n;
-                const f32x4 sc = *reinterpret_cast<const f32x4*>(&dsc[bf][sb * M + 4 * g]);
-                u32x4 a[KS];
-#pragma unroll
-                for (int s = 0; s < KS; ++s) a[s] = opnd(bf, sb, s);
-#pragma unroll
-                for (int cb = 0; cb < QB; ++cb) {
-                    Acc acc = MM::zero();
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) acc = MM::mma(a[s], bq[cb][s], acc);
-#pragma unroll
-                    for (int i = 0; i < VPL; ++i) v[n][cb][i] = (float)acc[i] * sc[i];
-                }
-            }
-        } else {
+        {
             Acc acc[NS][QB];
 #pragma unroll
             for (int n = 0; n < NS; ++n)
@@ -626,7 +618,19 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     // Per k-step the stage issues one MFMA per query block and folds VPL/KS
     // values of each of the previous stage's blocks (a fixed, hand-interleaved
     // order; the scheduling barrier keeps the compiler from regrouping it).
-    // int8 values are the exact products fl32(float(dot) * d_scale[token]).
+    //
+    // int8 values are the exact products fl32(float(dot) * d_scale[token]),
+    // formed by one fused multiply-add instead of a convert and a multiply.
+    // Each accumulator starts at the integer 0x4B000000, the bits of the
+    // float 2^23, so after the contraction (|dot| <= 128 * 127^2 < 2^21) its
+    // bits read as the float 2^23 + dot when dot >= 0 and 2^23 + dot/2 when
+    // dot < 0 (the binade below 2^23 has half the spacing).  fma(that, s,
+    // -2^23 * s) has an exact addend (a power of two times s) and rounds once,
+    // to fl32(dot * s), or to fl32(dot * s) / 2 for negative dot, which is
+    // exact while d_scale >= 2^-125.  Halving every negative value keeps all
+    // orders and ties (the sign is unchanged and all negatives scale alike),
+    // so the running maxima and argmax are those of the exact values, and a
+    // negative row maximum is doubled back (exactly) before the query scale.
     static_assert(VPL % KS == 0, "fold parts");
     constexpr int FPS = VPL / KS;  // values folded per block per k-step
     auto stage_scales = [&](int bf, int sb) {
@@ -636,9 +640,16 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             return f32x4{1.f, 1.f, 1.f, 1.f};
         }
     };
+    auto acc_start = [&]() -> Acc {
+        if constexpr (I8) {
+            return Acc{0x4B000000, 0x4B000000, 0x4B000000, 0x4B000000};
+        } else {
+            return MM::zero();
+        }
+    };
     auto value = [&](const Acc& acc, int i, const f32x4& sc) -> float {
         if constexpr (I8) {
-            return (float)acc[i] * sc[i];
+            return __builtin_fmaf(__int_as_float(acc[i]), sc[i], -(sc[i] * 8388608.0f));
         } else {
             return acc[i];
         }
@@ -661,7 +672,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) a[s] = opnd(bf, sb, s);
 #pragma unroll
-        for (int cb = 0; cb < QB; ++cb) cur[cb] = MM::zero();
+        for (int cb = 0; cb < QB; ++cb) cur[cb] = acc_start();
         float kt[QB];
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb) kt[cb] = -INFINITY;
@@ -791,29 +802,29 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
     auto compute_tile = [&](int bf, int tt, int ln, bool last_tile) {
         if constexpr ((!I8 && M == 32 && QB <= 2) || I8) {  // two stages of accumulators fit in registers
             compute_tile_pipe(bf, tt, ln, last_tile);
-            return;
-        }
-        if (wq * QB * M >= nrows) return;  // uniform: this wave's rows are all past the slab
-        const int tok_w = tt * TT + wt * SPW * M;  // first token of this wave's sub-tiles
-        int nsub = (ln - tok_w + M - 1) / M;       // sub-tiles holding at least one valid token
-        nsub = nsub < 0 ? 0 : (nsub > SPW ? SPW : nsub);
+        } else {
+            if (wq * QB * M >= nrows) return;  // uniform: this wave's rows are all past the slab
+            const int tok_w = tt * TT + wt * SPW * M;  // first token of this wave's sub-tiles
+            int nsub = (ln - tok_w + M - 1) / M;       // sub-tiles holding at least one valid token
+            nsub = nsub < 0 ? 0 : (nsub > SPW ? SPW : nsub);
 #pragma unroll
-        for (int k = 0; k < SPW; k += NSI) {
-            if (k >= nsub) break;  // uniform
-            const int sb = wt * SPW + k;
-            const int tok0 = tok_w + k * M;
-            const int gsub = tt * SUBS + sb;
-            if (NSI == 2 && k + 1 < nsub) {
-                if (tok0 + 2 * M <= ln) {
-                    subtiles(std::integral_constant<int, 2>{}, std::false_type{}, bf, sb, tok0, ln, gsub);
+            for (int k = 0; k < SPW; k += NSI) {
+                if (k >= nsub) break;  // uniform
+                const int sb = wt * SPW + k;
+                const int tok0 = tok_w + k * M;
+                const int gsub = tt * SUBS + sb;
+                if (NSI == 2 && k + 1 < nsub) {
+                    if (tok0 + 2 * M <= ln) {
+                        subtiles(std::integral_constant<int, 2>{}, std::false_type{}, bf, sb, tok0, ln, gsub);
+                    } else {
+                        subtiles(std::integral_constant<int, 2>{}, std::true_type{}, bf, sb, tok0, ln, gsub);
+                    }
                 } else {
-                    subtiles(std::integral_constant<int, 2>{}, std::true_type{}, bf, sb, tok0, ln, gsub);
-                }
-            } else {
-                if (tok0 + M <= ln) {
-                    subtiles(std::integral_constant<int, 1>{}, std::false_type{}, bf, sb, tok0, ln, gsub);
-                } else {
-                    subtiles(std::integral_constant<int, 1>{}, std::true_type{}, bf, sb, tok0, ln, gsub);
+                    if (tok0 + M <= ln) {
+                        subtiles(std::integral_constant<int, 1>{}, std::false_type{}, bf, sb, tok0, ln, gsub);
+                    } else {
+                        subtiles(std::integral_constant<int, 1>{}, std::true_type{}, bf, sb, tok0, ln, gsub);
+                    }
                 }
             }
         }
@@ -856,7 +867,12 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             }
             const int r = (wq * QB + cb) * M + lm;
             if (g == 0 && (ARGMAX || !wave_sums)) {  // row maxima for the general sum or the argmax merge
-                rowmax_s[par][wt][rpad(r)] = mv;
+                if constexpr (I8_TERMS) {
+                    // v_i = fl32(m_i * q_scale_i) right away (a negative maximum was held halved)
+                    rowmax_s[par][0][rpad(r)] = (mv < 0.f ? mv + mv : mv) * qsc_s[rpad(r)];
+                } else {
+                    rowmax_s[par][wt][rpad(r)] = mv;
+                }
                 if constexpr (ARGMAX) rowarg_s[par][wt][r] = idx;
             }
             if constexpr (!I8 && M == 32 && WT == 1) {
@@ -876,6 +892,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         float mv = rowmax_s[par][0][rpad(r)];
 #pragma unroll
         for (int w = 1; w < WT; ++w) mv = fmaxf(mv, rowmax_s[par][w][rpad(r)]);
+        if constexpr (I8) mv = mv < 0.f ? mv + mv : mv;  // a negative int8 maximum was held halved
         return mv;
     };
     auto row_arg = [&](int par, int r) {
@@ -892,6 +909,14 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
         }
         return idx;
     };
+    // int8 term v_i of row r (in ascending i these form the exact score)
+    auto row_term = [&](int par, int r) -> float {
+        if constexpr (I8_TERMS) {
+            return rowmax_s[par][0][rpad(r)];
+        } else {
+            return row_max(par, r) * qsc_s[rpad(r)];
+        }
+    };
     // End of a document, part 2 (after the step barrier): argmax stores and
     // the per-query sums of the row maxima.
     auto epilogue_out = [&](int b, int par) {
@@ -904,40 +929,56 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                 p.argmax[((int64_t)(q0 + ql) * p.B + b) * Lq + i] = row_arg(par, r);
             }
         }
-        if constexpr (I8 && ARGMAX) {
-            // Exact epilogue: v_i = fl32(m_i * q_scale_i), summed in ascending i,
-            // one thread per query.
-            for (int ql = tid; ql < nq; ql += NT) {
-                float acc = 0.f;
-                for (int i = 0; i < ni; ++i) {
-                    const float v = row_max(par, ql * ni + i) * qsc_s[rpad(ql * ni + i)];
-                    acc = acc + v;
-                }
-                p.scores[(int64_t)(q0 + ql) * p.B + b] = acc;
-            }
-        } else if constexpr (I8) {
-            // The same sums, by the second wave (the first is a loading wave
-            // and carried this latency-bound loop on the step's critical
-            // path), with 8 rows read ahead of the serial adds: 1.6 % faster.
-            // (With the argmax, 16 waves at the 128-VGPR limit, this measured
-            // 2.5 % slower, so that path keeps the plain loop above.)
-            const int first = (tid + NT - (NW > 1 ? 64 : 0)) % NT;  // a rotation of the thread ids
-            for (int ql = first; ql < nq; ql += NT) {
-                float acc = 0.f;
-                int i = 0;
-                for (; i + 8 <= ni; i += 8) {
-                    float v[8];
+        if constexpr (I8) {
+            // Exact epilogue: score = ((v_0 + v_1) + v_2) + ... in fp32, a
+            // serial chain per query, run at raised wave priority (it sits on
+            // the step's critical path; at the stages' priority the waves in
+            // their contraction left it few issue slots: 2-7 % slower).
+            __builtin_amdgcn_s_setprio(2);
+            if (R >= 64 && ni >= 64) {
+                // Long queries: a wave per query reads 64 consecutive terms at
+                // once and adds them in order through readlane (lanes past the
+                // query add +0, which changes no sum that starts at +0).
+                for (int ql = (wave + NW - 1) % NW; ql < nq; ql += NW) {  // uniform per wave
+                    const int r0 = ql * ni;
+                    float acc = 0.f;
+                    for (int c = 0; c < ni; c += 64) {
+                        const float t = c + lane < ni ? row_term(par, r0 + c + lane) : 0.f;
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) v[k] = row_max(par, ql * ni + i + k) * qsc_s[rpad(ql * ni + i + k)];
+                        for (int k = 0; k < 64; ++k) acc = acc + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), k));
+                    }
+                    if (lane == 0) p.scores[(int64_t)(q0 + ql) * p.B + b] = acc;
+                }
+            } else {
+                // A thread per query, on the second wave first (measured
+                // faster; the 16-wave argmax kernel excepted), the next 8 rows
+                // read while the current 8 are added.  With the argmax the
+                // plain loop: at the 128-VGPR limit the read-ahead would spill.
+                constexpr bool FIRST_WAVE = ARGMAX && NW == 16;
+                for (int ql = FIRST_WAVE ? tid : (tid + NT - (NW > 1 ? 64 : 0)) % NT; ql < nq; ql += NT) {
+                    const int r0 = ql * ni;
+                    float acc = 0.f;
+                    int i = 0;
+                    if (!ARGMAX && ni >= 16) {
+                        float cur[8], nxt[8];
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) acc = acc + v[k];
+                        for (int k = 0; k < 8; ++k) cur[k] = row_term(par, r0 + k);
+                        for (i = 8; i + 8 <= ni; i += 8) {
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) nxt[k] = row_term(par, r0 + i + k);
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) acc = acc + cur[k];
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) cur[k] = nxt[k];
+                        }
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) acc = acc + cur[k];  // rows i-8 .. i-1
+                    }
+                    for (; i < ni; ++i) acc = acc + row_term(par, r0 + i);
+                    p.scores[(int64_t)(q0 + ql) * p.B + b] = acc;
                 }
-                for (; i < ni; ++i) {
-                    const float v = row_max(par, ql * ni + i) * qsc_s[rpad(ql * ni + i)];
-                    acc = acc + v;
-                }
-                p.scores[(int64_t)(q0 + ql) * p.B + b] = acc;
             }
+            __builtin_amdgcn_s_setprio(0);
         } else {
             // P lanes per query (P = ni rounded up to a power of two, at most 64),
             // 64 / P queries per wave pass, butterfly sum inside each lane group.
