@@ -111,6 +111,44 @@ def test_first_token_max_ragged_tails(bd):
     assert np.array_equal(a, a_ref)
 
 
+@pytest.mark.parametrize("Lq", [32, 300])
+def test_negative_maxima_and_scale_range(bd, Lq):
+    """Row maxima that are negative (one- and two-token documents, about half
+    of their rows, and tokens that negate query rows), rows that mix signs,
+    zero dots and exact ties, and document scales spread over [2^-100, 2^40]
+    plus the header's ends 2^-125 and 2^100.  The kernel holds negative values
+    halved until the end; scores and argmax must still be bit-exact."""
+    rng = np.random.default_rng(77 + Lq)
+    Nq = 3
+    Q = rng.integers(-127, 128, (Nq, Lq, 128)).astype(np.int8)
+    qs = (2.0 ** rng.uniform(-8, 4, (Nq, Lq))).astype(np.float32)
+    lens = np.array([1, 2, 16, 17, 40, 300, 5], np.int32)
+    cu = inputs.cu_seqlens(lens)
+    T = int(cu[-1])
+    D = rng.integers(-127, 128, (T, 128)).astype(np.int8)
+    # documents 0..2 (1, 2 and 16 tokens): every token the negation of a query
+    # row; document 3: every other token so, and one all-zero token
+    flat = Q.reshape(-1, 128).astype(np.int16)
+    for b in range(3):
+        for j in range(cu[b], cu[b + 1]):
+            D[j] = np.clip(-flat[rng.integers(0, flat.shape[0])], -127, 127).astype(np.int8)
+    for j in range(cu[3], cu[4], 2):
+        D[j] = np.clip(-flat[rng.integers(0, flat.shape[0])], -127, 127).astype(np.int8)
+    D[cu[3] + 1] = 0
+    D[cu[4] + 3] = D[cu[4] + 7]  # exact ties within a document
+    ds = (2.0 ** rng.uniform(-100, 40, T)).astype(np.float32)
+    ds[cu[5]] = np.float32(2.0 ** -125)
+    ds[cu[5] + 1] = np.float32(2.0 ** 100)
+    ds[cu[4] + 7] = ds[cu[4] + 3]
+    s_ref, a_ref = oracle.fwd_i8(Q, qs, D, ds, cu)
+    s, a = run_i8(bd, Q, qs, D, ds, cu)
+    assert_bits_equal(s, s_ref, "negative maxima, Lq %d" % Lq)
+    assert np.array_equal(a, a_ref)
+    s2, _ = run_i8(bd, Q, qs, D, ds, cu, with_argmax=False)
+    assert_bits_equal(s2, s_ref, "negative maxima, Lq %d, no argmax" % Lq)
+    assert np.any(s_ref[:, :3] < 0)  # the anti-aligned documents do give negative maxima
+
+
 def test_workload_int8_subset(bd):
     w = inputs.make("int8_varlen")
     s, a = run_i8(bd, w["Q"], w["q_scale"], w["D_packed"], w["d_scale"], w["cu_seqlens"])
