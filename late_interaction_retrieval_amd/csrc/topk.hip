@@ -53,24 +53,64 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* scores,
     for (int shift = 56; shift >= 0; shift -= 8) {
         for (int e = tid; e < 256; e += kTopkThreads) hist[e] = 0u;
         __syncthreads();
-        for (int j = tid; j < B; j += kTopkThreads) {
-            const unsigned long long key = topk_key(row, idr, j);
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        for (int j0 = 0; j0 < B; j0 += kTopkThreads) {  // uniform
+            const int j = j0 + tid;
+            bool in = false;
+            unsigned d = 0u;
+            if (j < B) {
+                const unsigned long long key = topk_key(row, idr, j);
+                in = (key & mask) == prefix;
+                d = (unsigned)(key >> shift) & 255u;
+            }
+            // the leading digits of similar scores coincide: when every key of
+            // the wave falls in one bin, one atomic adds the wave's count
+            const unsigned long long inb = __ballot(in);
+            if (inb != 0ull) {
+                const int first = __ffsll((long long)inb) - 1;
+                const unsigned d0 = (unsigned)__shfl((int)d, first);
+                if (__ballot(in && d != d0) == 0ull) {
+                    if ((tid & 63) == first) atomicAdd(&hist[d0], (unsigned)__popcll(inb));
+                } else if (in) {
+                    atomicAdd(&hist[d], 1u);
+                }
+            }
         }
         __syncthreads();
-        if (tid == 0) {
-            unsigned cum = 0;
-            int digit = 0;
-            for (int d = 255; d >= 0; --d) {
-                if (cum + hist[d] >= (unsigned)krem) {
-                    digit = d;
-                    break;
-                }
-                cum += hist[d];
+        if (tid < 64) {
+            // the digit holding the krem-th largest key under the prefix, by
+            // one wave: lane l sums bins 255-4l .. 252-4l, a scan over the
+            // lanes gives the count above each lane's bins, and the lane where
+            // the count reaches krem walks its four bins
+            unsigned c[4], local = 0u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                c[k] = hist[255 - 4 * tid - k];
+                local += c[k];
             }
-            s_krem = krem - (int)cum;
-            s_prefix = prefix | ((unsigned long long)digit << shift);
-            s_done = hist[digit] == (unsigned)(krem - (int)cum);  // every key under the new prefix is taken
+            unsigned incl = local;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const unsigned t = (unsigned)__shfl_up((int)incl, off);
+                if (tid >= off) incl += t;
+            }
+            const unsigned above = incl - local;  // keys in bins above this lane's
+            if (above < (unsigned)krem && incl >= (unsigned)krem) {  // exactly one lane
+                unsigned cum = above;
+                int digit = 255 - 4 * tid - 3;
+                unsigned hd = c[3];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if (cum + c[k] >= (unsigned)krem) {
+                        digit = 255 - 4 * tid - k;
+                        hd = c[k];
+                        break;
+                    }
+                    cum += c[k];
+                }
+                s_krem = krem - (int)cum;
+                s_prefix = prefix | ((unsigned long long)digit << shift);
+                s_done = hd == (unsigned)(krem - (int)cum);  // every key under the new prefix is taken
+            }
         }
         __syncthreads();
         prefix = s_prefix;
