@@ -243,6 +243,13 @@ __device__ __forceinline__ unsigned xor32_u(unsigned v, int lane) {
     return lane < 32 ? r[1] : r[0];
 }
 __device__ __forceinline__ float xor32_f(float v, int lane) { return bitsf(xor32_u(fbits(v), lane)); }
+// Value of lane l ^ 16 (v_permlane16_swap: rows of 16 lanes swap pairwise,
+// odd rows of the first operand with even rows of the second).
+__device__ __forceinline__ unsigned xor16_u(unsigned v, int lane) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+}
+__device__ __forceinline__ float xor16_f(float v, int lane) { return bitsf(xor16_u(fbits(v), lane)); }
 
 
 // Calls f(std::integral_constant<int, j>{}) for j = 0 .. N-1, expanded at
@@ -854,9 +861,14 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             }
 #pragma unroll
             for (int off = M; off < 64; off <<= 1) {
-                const float om = off == 32 ? xor32_f(mv, lane) : __shfl_xor(mv, off);
+                // off 16 through v_permlane16_swap where it measured faster (one
+                // token-wave: int8 1-5 %; with four token-waves 12 % slower)
+                const bool x16 = WT == 1 && off == 16;
+                const float om = off == 32 ? xor32_f(mv, lane) : x16 ? xor16_f(mv, lane) : __shfl_xor(mv, off);
                 if constexpr (ARGMAX) {
-                    const int oi = off == 32 ? (int)xor32_u((unsigned)idx, lane) : __shfl_xor(idx, off);
+                    const int oi = off == 32 ? (int)xor32_u((unsigned)idx, lane)
+                                   : x16     ? (int)xor16_u((unsigned)idx, lane)
+                                             : __shfl_xor(idx, off);
                     if (om > mv || (om == mv && (unsigned)oi < (unsigned)idx)) {
                         mv = om;
                         idx = oi;
