@@ -20,7 +20,9 @@
 //   3. dd_owner  : a 16-lane group owns dD rows, walks their sources and
 //                  writes each row once (no atomics).
 //   4. dq_gather : a 16-lane group owns dQ rows and loops over the B
-//                  documents (Algorithm 3 step 3).
+//                  documents (Algorithm 3 step 3); extra workgroups of the
+//                  same launch reduce the dD rows with very many sources
+//                  that dd_owner left to them.
 // A negative argmax entry (the forward's value for a document with no valid
 // token) selects no row.  Entries at or past a document's length break the
 // forward's contract; they are clamped into range so that no access leaves
@@ -68,7 +70,8 @@ struct BwdParams {
     int dq_split, dq_docs;
     float* dq_part;
     // dD rows with more than kHeavy sources: dd_owner appends them to this
-    // list (count first) and dd_heavy reduces each with a whole workgroup
+    // list (count first) and extra workgroups of the dQ launch reduce each
+    // with a whole workgroup (heavy_rows)
     int32_t* heavy;
     int64_t max_heavy;
 };
@@ -423,7 +426,7 @@ constexpr int kGatherBlocks = 512;                  // 2 per CU on 256 CUs
 constexpr int kRowsPerGroup = 4;
 constexpr int kQueryWindow = 16;  // queries per dD step
 constexpr int kDdBatch = 12;      // dD sources gathered per round (loads in flight)
-// A dD row with more sources than this is left to dd_heavy: one 16-lane group
+// A dD row with more sources than this is left to heavy_rows: one 16-lane group
 // walking thousands of sources would hold up the whole grid.
 constexpr int kHeavy = 512;
 
@@ -590,14 +593,16 @@ __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(
 // ascending order (16 loads in flight), and the chunk sums are added in
 // group order.  The split is fixed by the row's length, so runs are
 // bit-identical.  The source's document comes from the source (s / Lq).
+// Run by the workgroups of the dQ launch past its gather grid (heavy worker
+// h0 of hstride), which follows dd_owner on the stream, so the list is
+// complete; a separate launch cost about 4.5 us even with no heavy row.
 template <int ELEM>
-__global__ __launch_bounds__(kGatherThreads) void dd_heavy(BwdParams p) {
-    __shared__ float part[kGatherGroups][128];
+__device__ __forceinline__ void heavy_rows(const BwdParams& p, int h0, int hstride, float (*part)[128]) {
     const int l16 = threadIdx.x & 15, grp = threadIdx.x >> 4;
     const int BLq = p.B * p.Lq;
     const int nsrc = p.Nq * BLq;
     const int count = (int)(p.heavy[0] < p.max_heavy ? p.heavy[0] : p.max_heavy);
-    for (int h = blockIdx.x; h < count; h += gridDim.x) {  // uniform
+    for (int h = h0; h < count; h += hstride) {  // uniform
         const int64_t row = p.heavy[1 + h];
         int beg = p.row_ptr[row], end = p.row_ptr[row + 1];
         beg = beg < 0 ? 0 : (beg > nsrc ? nsrc : beg);
@@ -658,10 +663,19 @@ __global__ __launch_bounds__(kGatherThreads) void dd_heavy(BwdParams p) {
 // group holds document b0 + j's first row and length; an empty document, or
 // a negative argmax, gives weight 0 and reads a valid row.  Each row sums its
 // terms in ascending b.
+//
+// Workgroups past the gather grid (blockIdx.x >= gather_blocks, every chunk
+// row y) reduce the heavy dD rows instead (heavy_rows).
 template <int ELEM, bool VARLEN, int RPG, int DSTEP>
-__global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void dq_gather(BwdParams p, int rows_per_group) {
+__global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void dq_gather(BwdParams p, int rows_per_group, int gather_blocks) {
+    if ((int)blockIdx.x >= gather_blocks) {  // uniform over the workgroup
+        __shared__ float part[kGatherGroups][128];
+        const int hx = (int)gridDim.x - gather_blocks;  // heavy columns, each gridDim.y workgroups
+        heavy_rows<ELEM>(p, ((int)blockIdx.x - gather_blocks) * (int)gridDim.y + (int)blockIdx.y, hx * (int)gridDim.y, part);
+        return;
+    }
     const int l16 = threadIdx.x & 15;
-    const int64_t ngroups = (int64_t)gridDim.x * kGatherGroups;
+    const int64_t ngroups = (int64_t)gather_blocks * kGatherGroups;
     const int64_t gid = (int64_t)blockIdx.x * kGatherGroups + (threadIdx.x >> 4);
     const int64_t nrows = (int64_t)p.Nq * p.Lq;
     int aoff[RPG], goff[RPG];  // Nq*B*Lq < 2^31 (checked by the host)
@@ -862,20 +876,24 @@ size_t dq_part_bytes(int32_t Nq, int32_t Lq, int32_t B) {
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// heavy_blocks: extra workgroups that reduce the heavy dD rows dd_owner listed
+// (0 when there is no list).
 template <int ELEM, bool VARLEN>
-hipError_t launch_dq(BwdParams p, hipStream_t stream) {
+hipError_t launch_dq(BwdParams p, unsigned heavy_blocks, hipStream_t stream) {
     const int64_t nrows = (int64_t)p.Nq * p.Lq;
     unsigned blocks;
     int rpg;
     gather_grid(nrows, &blocks, &rpg);
     p.dq_split = dq_split_of(nrows, p.B);
     p.dq_docs = (p.B + p.dq_split - 1) / p.dq_split;
+    // about heavy_blocks heavy workers in all, spread over the chunk rows
+    const unsigned hx = (heavy_blocks + p.dq_split - 1) / p.dq_split;
+    const dim3 grid(blocks + hx, p.dq_split);
     if (rpg == 1)
-        hipLaunchKernelGGL((dq_gather<ELEM, VARLEN, 1, 8>), dim3(blocks, p.dq_split), dim3(kGatherThreads), 0, stream,
-                           p, rpg);
+        hipLaunchKernelGGL((dq_gather<ELEM, VARLEN, 1, 8>), grid, dim3(kGatherThreads), 0, stream, p, rpg, (int)blocks);
     else
-        hipLaunchKernelGGL((dq_gather<ELEM, VARLEN, kRowsPerGroup, 2>), dim3(blocks, p.dq_split), dim3(kGatherThreads),
-                           0, stream, p, rpg);
+        hipLaunchKernelGGL((dq_gather<ELEM, VARLEN, kRowsPerGroup, 2>), grid, dim3(kGatherThreads), 0, stream, p, rpg,
+                           (int)blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.dq_split == 1) return e;
     hipLaunchKernelGGL(dq_reduce, dim3((unsigned)((nrows * 32 + 15) / 16)), dim3(256), 0, stream, p);
@@ -924,13 +942,9 @@ hipError_t launch_bwd_elem(const BwdParams& p, hipStream_t stream) {
         if (VARLEN) blocks = kGatherBlocks;
         hipLaunchKernelGGL((dd_owner<ELEM, VARLEN>), dim3(blocks), dim3(kGatherThreads), 0, stream, p, rpg);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const unsigned hb = (unsigned)std::min<int64_t>(p.max_heavy, kGatherBlocks);
-        if (hb > 0) {
-            hipLaunchKernelGGL((dd_heavy<ELEM>), dim3(hb), dim3(kGatherThreads), 0, stream, p);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
     }
-    return launch_dq<ELEM, VARLEN>(p, stream);
+    const unsigned hb = nrows > 0 ? (unsigned)std::min<int64_t>(p.max_heavy, kGatherBlocks) : 0u;
+    return launch_dq<ELEM, VARLEN>(p, hb, stream);
 }
 
 template <int ELEM, bool VARLEN>
@@ -947,9 +961,7 @@ hipError_t launch_scatter_elem(const BwdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL((dd_scatter<ELEM, VARLEN>), dim3(sb), dim3(256), 0, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    unsigned blocks;
-    int rpg;
-    return launch_dq<ELEM, VARLEN>(p, stream);
+    return launch_dq<ELEM, VARLEN>(p, 0u, stream);
 }
 
 // ceil-rounded magic multiplier for floor(n / d), 0 <= n < 2^31:
