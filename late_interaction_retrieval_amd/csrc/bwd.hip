@@ -183,11 +183,41 @@ __global__ __launch_bounds__(1024) void csr_count(BwdParams p) {
     int n = 0;
     if (q < p.Nq) {
         const int32_t* a = p.A + ((int64_t)q * p.B + b) * p.Lq;
-        for (int i = lane; i < p.Lq; i += 64) {
-            const int t = src_row(a[i], len);
-            if (t >= 0) {
-                atomicAdd(&hist[t], 1);
-                ++n;
+        if (p.Lq >= 256 && (p.Lq & 3) == 0 && (reinterpret_cast<uintptr_t>(a) & 15) == 0) {  // uniform
+            // long queries: 16-byte loads, up to four per lane in flight before
+            // the atomics (one 4-byte load per lane between atomics left the
+            // loads serial; training shape 2.5 % faster).  Short ones keep a
+            // lane per entry: with a quarter of the lanes busy they measured 4 %
+            // slower.
+            const int n4 = p.Lq >> 2;
+            const int4* a4 = reinterpret_cast<const int4*>(a);
+            for (int i0 = 0; i0 < n4; i0 += 256) {  // uniform
+                int4 v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int i = i0 + k * 64 + lane;
+                    v[k] = i < n4 ? a4[i] : make_int4(-1, -1, -1, -1);  // -1 selects no row
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int e[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int t = src_row(e[c], len);
+                        if (t >= 0) {
+                            atomicAdd(&hist[t], 1);
+                            ++n;
+                        }
+                    }
+                }
+            }
+        } else {
+            for (int i = lane; i < p.Lq; i += 64) {
+                const int t = src_row(a[i], len);
+                if (t >= 0) {
+                    atomicAdd(&hist[t], 1);
+                    ++n;
+                }
             }
         }
     }
