@@ -250,6 +250,17 @@ __device__ __forceinline__ unsigned xor16_u(unsigned v, int lane) {
     return (lane & 16) ? r[0] : r[1];
 }
 __device__ __forceinline__ float xor16_f(float v, int lane) { return bitsf(xor16_u(fbits(v), lane)); }
+// max(v, v of lane l ^ 32) and max(v, v of lane l ^ 16): with both operands
+// v, each swap returns the lane's own value and its partner's, in an order
+// that depends on the lane, so their maximum needs no lane select.
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
+    return fmaxf(bitsf(r[0]), bitsf(r[1]));
+}
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+    return fmaxf(bitsf(r[0]), bitsf(r[1]));
+}
 
 
 // Calls f(std::integral_constant<int, j>{}) for j = 0 .. N-1, expanded at
@@ -864,8 +875,8 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                 // off 16 through v_permlane16_swap where it measured faster (one
                 // token-wave: int8 1-5 %; with four token-waves 12 % slower)
                 const bool x16 = WT == 1 && off == 16;
-                const float om = off == 32 ? xor32_f(mv, lane) : x16 ? xor16_f(mv, lane) : __shfl_xor(mv, off);
                 if constexpr (ARGMAX) {
+                    const float om = off == 32 ? xor32_f(mv, lane) : x16 ? xor16_f(mv, lane) : __shfl_xor(mv, off);
                     const int oi = off == 32 ? (int)xor32_u((unsigned)idx, lane)
                                    : x16     ? (int)xor16_u((unsigned)idx, lane)
                                              : __shfl_xor(idx, off);
@@ -874,7 +885,7 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                         idx = oi;
                     }
                 } else {
-                    mv = fmaxf(mv, om);
+                    mv = off == 32 ? xor32_max(mv) : x16 ? xor16_max(mv) : fmaxf(mv, __shfl_xor(mv, off));
                 }
             }
             const int r = (wq * QB + cb) * M + lm;
@@ -971,7 +982,46 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                     const int r0 = ql * ni;
                     float acc = 0.f;
                     int i = 0;
-                    if (!ARGMAX && ni >= 16) {
+                    if (I8_TERMS && (ni & 7) == 0) {  // uniform
+                        // Groups of 8 rows start at multiples of 8, so none
+                        // crosses a 32-row pad step: one address per group
+                        // and immediate offsets.  Scores only: the next
+                        // group is read while the current one is added.
+                        const int ng = ni >> 3;
+                        auto ld = [&](float(&v)[8], int gi) {
+                            const float* t = &rowmax_s[par][0][rpad(r0 + 8 * gi)];
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) v[k] = t[k];
+                        };
+                        auto add = [&](const float(&v)[8]) {
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) acc = acc + v[k];
+                        };
+                        float x[8], y[8];
+                        if constexpr (ARGMAX) {
+                            for (int gi = 0; gi < ng; ++gi) {
+                                ld(x, gi);
+                                add(x);
+                            }
+                        } else {
+                            ld(x, 0);
+                            int gi = 1;
+                            for (; gi + 1 < ng; gi += 2) {
+                                ld(y, gi);
+                                add(x);
+                                ld(x, gi + 1);
+                                add(y);
+                            }
+                            if (gi < ng) {
+                                ld(y, gi);
+                                add(x);
+                                add(y);
+                            } else {
+                                add(x);
+                            }
+                        }
+                        i = ni;
+                    } else if (!ARGMAX && ni >= 16) {
                         float cur[8], nxt[8];
 #pragma unroll
                         for (int k = 0; k < 8; ++k) cur[k] = row_term(par, r0 + k);
@@ -1298,7 +1348,7 @@ __global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
     auto finish_doc = [&]() {  // document b is complete: merge, sum, store; move to b + 1
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb) {
-            const float mv = fmaxf(m[cb], xor32_f(m[cb], lane));
+            const float mv = xor32_max(m[cb]);
             const float sc = lanes32_sum(mv);
             const int ql = wave * QB + cb;
             if (lane == 31 && ql < nq) p.scores[(int64_t)(q0 + ql) * p.B + b] = sc;
