@@ -857,7 +857,13 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
 
     // End of a document, part 1 (before the step barrier): merge the NG token
     // sets of every query row (lanes lm + M*g) and park the row results.
+    // int8 terms with 16-row blocks: after the merge every 16-lane group
+    // holds every block's merged maxima, so group g forms and stores the
+    // terms of block j + g, four blocks per pass instead of one.
+    constexpr bool SPREAD = I8_TERMS && M == 16 && QB % 4 == 0;
     auto epilogue_merge = [&](int par, int b) {
+        float mvs[SPREAD ? QB : 1];
+        int ids[SPREAD ? QB : 1];
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb) {
             float mv = m[cb];
@@ -889,7 +895,10 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                 }
             }
             const int r = (wq * QB + cb) * M + lm;
-            if (g == 0 && (ARGMAX || !wave_sums)) {  // row maxima for the general sum or the argmax merge
+            if constexpr (SPREAD) {
+                mvs[cb] = mv;
+                ids[cb] = idx;
+            } else if (g == 0 && (ARGMAX || !wave_sums)) {  // row maxima for the general sum or the argmax merge
                 if constexpr (I8_TERMS) {
                     // v_i = fl32(m_i * q_scale_i) right away (a negative maximum was held halved)
                     rowmax_s[par][0][rpad(r)] = (mv < 0.f ? mv + mv : mv) * qsc_s[rpad(r)];
@@ -908,6 +917,24 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
             m[cb] = -INFINITY;
             km[cb] = -INFINITY;
             code[cb] = -1;
+        }
+        if constexpr (SPREAD) {
+#pragma unroll
+            for (int j = 0; j < QB; j += 4) {
+                float v = mvs[j];
+                int id = ids[j];
+#pragma unroll
+                for (int u = 1; u < 4; ++u) {
+                    if (g == u) {
+                        v = mvs[j + u];
+                        id = ids[j + u];
+                    }
+                }
+                const int r = (wq * QB + j + g) * M + lm;
+                // v_i = fl32(m_i * q_scale_i) (a negative maximum was held halved)
+                rowmax_s[par][0][rpad(r)] = (v < 0.f ? v + v : v) * qsc_s[rpad(r)];
+                if constexpr (ARGMAX) rowarg_s[par][wt][r] = id;
+            }
         }
     };
     // Row r's maximum / argmax over the token-waves (ties: lower index).
