@@ -1385,15 +1385,27 @@ __global__ __launch_bounds__(512) void fwd_flat_kernel(FwdParams p) {
         if (b < bend) dend = doc_end(b);
     };
     // Fold the values of tokens lo <= t < hi (relative to the sub-tile).
-    auto fold_range = [&](const Acc* acc, int lo, int hi) {
+    // Slot i of a lane holds token tok(0, i) + 4g (g = lane / 32), so one
+    // word of in-range tokens shifted by 4g gives every slot's test as a bit;
+    // each slot's bit becomes an all-ones / all-zeros mask, and each value is
+    // one bitfield insert of its bits or those of -inf.
+    static_assert(M == 32 && MM::NG == 2, "fold_range assumes the 32x32 layout");
+    const uint32_t sh4 = (uint32_t)g * 4u;
+    auto fold_range = [&](const Acc* acc, int lo, int hi) {  // 0 <= lo < hi <= 32
+        const uint32_t tm = (hi >= 32 ? 0xFFFFFFFFu : (1u << hi) - 1u) & ~((1u << lo) - 1u);
+        const uint32_t w = tm >> sh4;  // bit u: token u + 4g lies in range
+        uint32_t mk[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int u = MM::tok(0, i);
+            mk[i] = (uint32_t)((int32_t)(w << (31 - u)) >> 31);
+        }
 #pragma unroll
         for (int cb = 0; cb < QB; ++cb) {
             float mx = m[cb];
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int t = MM::tok(g, i);
-                mx = fmaxf(mx, (t >= lo && t < hi) ? acc[cb][i] : -INFINITY);
-            }
+            for (int i = 0; i < VPL; ++i)
+                mx = fmaxf(mx, bitsf((fbits(acc[cb][i]) & mk[i]) | (~mk[i] & 0xFF800000u)));
             m[cb] = mx;
         }
     };
