@@ -1599,13 +1599,17 @@ __device__ __forceinline__ void rows_vs_doc(const FwdParams& p, const char* qrow
                 Acc acc = MM::zero();
 #pragma unroll
                 for (int s2 = 0; s2 < KS; ++s2) acc = MM::mma(a[j][s2], bq[cb][s2], acc);
+                // Unmasked: a slot past the document's end holds a copy of
+                // its first token (len > 0 here), the same value under a
+                // later index, so it changes no maximum, and the strict
+                // update and the lower-index merge never let it win the
+                // argmax.
 #pragma unroll
                 for (int i = 0; i < VPL; ++i) {
-                    const int tk = sb * M + MM::tok(g, i);
-                    const float v = tk < len ? acc[i] : -INFINITY;
+                    const float v = acc[i];
                     if (v > m[cb]) {  // strict: the earliest token keeps a tie
                         m[cb] = v;
-                        best[cb] = tk;
+                        best[cb] = sb * M + MM::tok(g, i);
                     }
                 }
             }

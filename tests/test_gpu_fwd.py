@@ -186,12 +186,12 @@ def test_very_long_documents(bd, dtn, Lq):
 
 
 @pytest.mark.parametrize("dtn", [inputs.F16, inputs.BF16])
-def test_first_token_max_ragged_tails(bd, dtn):
+@pytest.mark.parametrize("Nq,Lq", [(20, 32), (1, 32), (2, 16), (1, 7)])
+def test_first_token_max_ragged_tails(bd, dtn, Nq, Lq):
     """Every document starts with the token closest to every query row, with
-    partial 32-token sub-tiles.  Rows past a document's end are read as copies
-    of its first token; the maxima must not change and every argmax must stay
-    inside the document."""
-    Nq, Lq = 20, 32
+    partial 32-token (and, for the few-row kernel, 16-token) sub-tiles.  Rows
+    past a document's end are read as copies of its first token; the maxima
+    must not change and every argmax must stay inside the document."""
     # one unit query row repeated, and that row as every document's first
     # token: similarity 1 at token 0, about N(0, 1/128) elsewhere
     row = inputs.random_rows(63, 1, 128, dtn)
@@ -201,7 +201,7 @@ def test_first_token_max_ragged_tails(bd, dtn):
     Dp = inputs.random_rows(64, int(cu[-1]), 128, dtn, stream=4)
     for b in range(len(lens)):
         Dp[cu[b]] = row[0]
-    s, a = full_check_varlen(bd, Q, Dp, cu, dtn, "first-token max %s" % dtn)
+    s, a = full_check_varlen(bd, Q, Dp, cu, dtn, "first-token max %s Nq %d Lq %d" % (dtn, Nq, Lq))
     assert np.all(a == 0)
 
 
