@@ -237,22 +237,12 @@ __device__ __forceinline__ void doc_info(const FwdParams& p, int b, int64_t& sta
 __device__ __forceinline__ unsigned fbits(float x) { return __float_as_uint(x); }
 __device__ __forceinline__ float bitsf(unsigned x) { return __uint_as_float(x); }
 
-// Value of lane l ^ 32 (v_permlane32_swap: no LDS round trip).
-__device__ __forceinline__ unsigned xor32_u(unsigned v, int lane) {
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return lane < 32 ? r[1] : r[0];
-}
-__device__ __forceinline__ float xor32_f(float v, int lane) { return bitsf(xor32_u(fbits(v), lane)); }
-// Value of lane l ^ 16 (v_permlane16_swap: rows of 16 lanes swap pairwise,
-// odd rows of the first operand with even rows of the second).
-__device__ __forceinline__ unsigned xor16_u(unsigned v, int lane) {
-    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return (lane & 16) ? r[0] : r[1];
-}
-__device__ __forceinline__ float xor16_f(float v, int lane) { return bitsf(xor16_u(fbits(v), lane)); }
-// max(v, v of lane l ^ 32) and max(v, v of lane l ^ 16): with both operands
-// v, each swap returns the lane's own value and its partner's, in an order
-// that depends on the lane, so their maximum needs no lane select.
+// Lane exchanges without an LDS round trip.  v_permlane32_swap swaps the
+// upper 32 lanes of its first operand with the lower 32 of its second;
+// v_permlane16_swap swaps the odd 16-lane rows of the first with the even
+// rows of the second.  With v as both operands, each returns the lane's own
+// value and that of lane l ^ 32 (or l ^ 16), in an order that depends on the
+// lane, so their maximum (or minimum) needs no lane select.
 __device__ __forceinline__ float xor32_max(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
     return fmaxf(bitsf(r[0]), bitsf(r[1]));
@@ -260,6 +250,15 @@ __device__ __forceinline__ float xor32_max(float v) {
 __device__ __forceinline__ float xor16_max(float v) {
     const auto r = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
     return fmaxf(bitsf(r[0]), bitsf(r[1]));
+}
+// The same pairings for the unsigned minimum.
+__device__ __forceinline__ unsigned xor32_min_u(unsigned v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return r[0] < r[1] ? r[0] : r[1];
+}
+__device__ __forceinline__ unsigned xor16_min_u(unsigned v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return r[0] < r[1] ? r[0] : r[1];
 }
 
 
@@ -882,13 +881,20 @@ __global__ __launch_bounds__(64 * WQ * WT) void fwd_kernel(FwdParams p) {
                 // token-wave: int8 1-5 %; with four token-waves 12 % slower)
                 const bool x16 = WT == 1 && off == 16;
                 if constexpr (ARGMAX) {
-                    const float om = off == 32 ? xor32_f(mv, lane) : x16 ? xor16_f(mv, lane) : __shfl_xor(mv, off);
-                    const int oi = off == 32 ? (int)xor32_u((unsigned)idx, lane)
-                                   : x16     ? (int)xor16_u((unsigned)idx, lane)
-                                             : __shfl_xor(idx, off);
-                    if (om > mv || (om == mv && (unsigned)oi < (unsigned)idx)) {
-                        mv = om;
-                        idx = oi;
+                    if (off == 32 || x16) {
+                        // the larger value, then the lowest index (unsigned:
+                        // -1, no candidate, loses) among the lanes holding it
+                        const float mx = off == 32 ? xor32_max(mv) : xor16_max(mv);
+                        const unsigned c = mv == mx ? (unsigned)idx : 0xFFFFFFFFu;
+                        idx = (int)(off == 32 ? xor32_min_u(c) : xor16_min_u(c));
+                        mv = mx;
+                    } else {
+                        const float om = __shfl_xor(mv, off);
+                        const int oi = __shfl_xor(idx, off);
+                        if (om > mv || (om == mv && (unsigned)oi < (unsigned)idx)) {
+                            mv = om;
+                            idx = oi;
+                        }
                     }
                 } else {
                     mv = off == 32 ? xor32_max(mv) : x16 ? xor16_max(mv) : fmaxf(mv, __shfl_xor(mv, off));
@@ -1620,11 +1626,18 @@ __device__ __forceinline__ void rows_vs_doc(const FwdParams& p, const char* qrow
     for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
         for (int off = M; off < 64; off <<= 1) {
-            const float om = off == 32 ? xor32_f(m[cb], lane) : __shfl_xor(m[cb], off);
-            const int oi = off == 32 ? (int)xor32_u((unsigned)best[cb], lane) : __shfl_xor(best[cb], off);
-            if (om > m[cb] || (om == m[cb] && (unsigned)oi < (unsigned)best[cb])) {
-                m[cb] = om;
-                best[cb] = oi;
+            if (off == 32) {  // the larger value, then the lowest index among the lanes holding it
+                const float mx = xor32_max(m[cb]);
+                const unsigned c = m[cb] == mx ? (unsigned)best[cb] : 0xFFFFFFFFu;
+                best[cb] = (int)xor32_min_u(c);
+                m[cb] = mx;
+            } else {
+                const float om = __shfl_xor(m[cb], off);
+                const int oi = __shfl_xor(best[cb], off);
+                if (om > m[cb] || (om == m[cb] && (unsigned)oi < (unsigned)best[cb])) {
+                    m[cb] = om;
+                    best[cb] = oi;
+                }
             }
         }
         if (g == 0) {
