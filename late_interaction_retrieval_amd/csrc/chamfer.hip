@@ -244,19 +244,29 @@ __global__ __launch_bounds__(kSortThreads) void sort_hist(const uint32_t* key, i
 }
 
 // exclusive scan of hist [256 * ntiles] in place (one workgroup, in order):
-// each thread takes 16 consecutive entries per round of 16384, so a round
-// costs one memory round trip
+// each thread takes 16 consecutive entries per round of 16384.  A round goes
+// through LDS: coalesced loads and stores on the memory side (a thread's own
+// 16 entries read straight from memory were 64 bytes apart across the wave,
+// and the one workgroup's load path set the time), and a row of 17 words per
+// thread, so the thread's 16 reads hit distinct banks across the wave.
+constexpr int kScanRound = 1024 * 16;
 __global__ __launch_bounds__(1024) void sort_scan(int32_t* hist, int64_t len) {
+    __shared__ int buf[1024 * 17];
     __shared__ int wsum[16];
     __shared__ int carry_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) carry_s = 0;
-    __syncthreads();
-    for (int64_t i0 = 0; i0 < len; i0 += 1024 * 16) {
-        const int64_t e0 = i0 + (int64_t)tid * 16;
+    for (int64_t i0 = 0; i0 < len; i0 += kScanRound) {
+        const int64_t cnt = len - i0 < kScanRound ? len - i0 : kScanRound;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int e = k * 1024 + tid;
+            buf[(e >> 4) * 17 + (e & 15)] = e < cnt ? hist[i0 + e] : 0;
+        }
+        __syncthreads();
         int v[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = e0 + k < len ? hist[e0 + k] : 0;
+        for (int k = 0; k < 16; ++k) v[k] = buf[tid * 17 + k];
         int tot = 0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) tot += v[k];
@@ -274,10 +284,15 @@ __global__ __launch_bounds__(1024) void sort_scan(int32_t* hist, int64_t len) {
         int run = carry + wpre + x - tot;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-            if (e0 + k < len) hist[e0 + k] = run;
+            buf[tid * 17 + k] = run;
             run += v[k];
         }
         __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int e = k * 1024 + tid;
+            if (e < cnt) hist[i0 + e] = buf[(e >> 4) * 17 + (e & 15)];
+        }
         if (tid == 1023) carry_s = carry + wpre + x;
         __syncthreads();
     }
