@@ -10,9 +10,9 @@
 // the expanded form |a|^2 + |b|^2 - 2<a, b> loses the small distances that
 // decide a nearest neighbour to cancellation, so the distance is formed
 // directly on the vector ALU: 3 subtractions, 1 multiply and 2 fused
-// multiply-adds, then a compare and two selects.  Each lane keeps kPts
+// multiply-adds, then a compare and two selects.  Each lane keeps 8 (or 4)
 // source points in registers; the target points are uniform across the
-// wave and arrive by scalar loads, so one load feeds 64 x kPts distances.
+// wave and arrive by scalar loads, so one load feeds 64 x 8 (or 4) distances.
 // The targets of a batch item are split into chunks over workgroups when
 // there are too few source tiles to fill the chip; the chunks' minima are
 // merged in ascending chunk order.
@@ -25,9 +25,7 @@
 namespace maxsim {
 namespace {
 
-constexpr int kPts = 8;            // source points per lane
 constexpr int kNnThreads = 256;    // 4 waves
-constexpr int kSrcTile = kNnThreads * kPts;
 constexpr int kTgtStep = 16;       // targets per scalar-load step
 constexpr int kMinChunk = 128;     // targets per chunk, at least
 
@@ -46,7 +44,9 @@ struct NnParams {
 
 // grid: Bt * tiles * chunks workgroups; chunk-major inside a batch item so
 // that the workgroups sharing a target chunk are launched together.
+template <int kPts>  // source points per lane
 __global__ __launch_bounds__(kNnThreads) void nn_kernel(NnParams p) {
+    constexpr int kSrcTile = kNnThreads * kPts;
     const int per_item = p.tiles * p.chunks;
     const int b = blockIdx.x / per_item;
     const int rem = blockIdx.x - b * per_item;
@@ -148,8 +148,9 @@ __global__ __launch_bounds__(256) void nn_empty(float* dist, int32_t* idx, int64
     }
 }
 
-void nn_plan(int Bt, int Na, int Nb, int* tiles, int* chunks, int* chunk_len) {
-    *tiles = (Na + kSrcTile - 1) / kSrcTile;
+void nn_plan_pts(int Bt, int Na, int Nb, int pts, int* tiles, int* chunks, int* chunk_len) {
+    const int src_tile = kNnThreads * pts;
+    *tiles = (Na + src_tile - 1) / src_tile;
     const int64_t blocks = (int64_t)Bt * *tiles;
     // about 4096 workgroups at most (rounded down: at 100K x 100K points,
     // 2058 workgroups left a nearly empty second round of the 1792 that fit
@@ -162,11 +163,25 @@ void nn_plan(int Bt, int Na, int Nb, int* tiles, int* chunks, int* chunk_len) {
     if (*chunks < 1) *chunks = 1;
     *chunk_len = len;
 }
+// 8 source points per lane, or 4 where the 8-point plan fills less than a
+// round of the chip (fewer than 2048 workgroups: small clouds or few of
+// them): there twice the workgroups, and no idle half tile below 2048
+// sources, outweigh the scalar target loads shared by half as many points
+// (32 x 2048 x 2048: -11 %, 64 x 1024 x 1024: -40 %; 1 x 100K x 100K, whose
+// 8-point plan has 4067 workgroups, ran 3 % slower with 4).
+void nn_plan(int Bt, int Na, int Nb, int* pts, int* tiles, int* chunks, int* chunk_len) {
+    nn_plan_pts(Bt, Na, Nb, 8, tiles, chunks, chunk_len);
+    *pts = 8;
+    if ((int64_t)Bt * *tiles * *chunks < 2048) {
+        nn_plan_pts(Bt, Na, Nb, 4, tiles, chunks, chunk_len);
+        *pts = 4;
+    }
+}
 
 size_t nn_part_bytes(int Bt, int Na, int Nb) {
     if (Bt < 1 || Na < 1 || Nb < 1) return 0;
-    int tiles, chunks, len;
-    nn_plan(Bt, Na, Nb, &tiles, &chunks, &len);
+    int pts, tiles, chunks, len;
+    nn_plan(Bt, Na, Nb, &pts, &tiles, &chunks, &len);
     return chunks > 1 ? (size_t)chunks * Bt * Na * 8 : 0;
 }
 
@@ -185,13 +200,19 @@ hipError_t launch_nn(const float* A, const float* B, int Bt, int Na, int Nb, flo
     p.Bt = Bt;
     p.Na = Na;
     p.Nb = Nb;
-    nn_plan(Bt, Na, Nb, &p.tiles, &p.chunks, &p.chunk_len);
+    int pts;
+    nn_plan(Bt, Na, Nb, &pts, &p.tiles, &p.chunks, &p.chunk_len);
     p.dist = dist;
     p.idx = idx;
     const int64_t n = (int64_t)Bt * Na;
     p.part_d = static_cast<float*>(ws);
     p.part_i = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + (size_t)p.chunks * n * 4);
-    hipLaunchKernelGGL(nn_kernel, dim3((unsigned)((int64_t)Bt * p.tiles * p.chunks)), dim3(kNnThreads), 0, stream, p);
+    const dim3 grid((unsigned)((int64_t)Bt * p.tiles * p.chunks));
+    if (pts == 4) {
+        hipLaunchKernelGGL(nn_kernel<4>, grid, dim3(kNnThreads), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL(nn_kernel<8>, grid, dim3(kNnThreads), 0, stream, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.chunks == 1) return e;
     hipLaunchKernelGGL(nn_merge, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 8192)), dim3(256), 0, stream, p);
