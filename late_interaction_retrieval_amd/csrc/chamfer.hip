@@ -410,8 +410,9 @@ __global__ __launch_bounds__(256) void csr_split(const int32_t* val, const int32
 
 // Destination-owned gradient rows.  Row r of cloud X (b*Nx + i) owns
 //   2 gx[r] (X[r] - Y[b, idx_x[r]])  +  sum over its CSR sources s of 2 gy[s] (X[r] - Y[s]).
-// 16 lanes per row: lane l sums the row's sources l, l+16, ... in ascending
-// order, the lanes are added by a fixed butterfly, then the row's own term.
+// 4 lanes per row (every point selects one point, so a row has one source on
+// average): lane l sums the row's sources l, l+4, ... in ascending order, the
+// lanes are added by a fixed butterfly, then the row's own term.
 struct RowSide {
     const float* X;
     const float* Y;
@@ -426,14 +427,15 @@ struct RowSide {
 };
 
 // A row with more sources than this goes to chamfer_heavy (a whole
-// workgroup), so one 16-lane group never walks a huge bucket alone.
-constexpr int kChHeavy = 1024;
+// workgroup), so one 4-lane group never walks a long bucket alone.
+constexpr int kChLanes = 4;
+constexpr int kChHeavy = 256;
 
 // rows of P first (side 0), then rows of Q (side 1), in one launch; heavy
 // rows are appended to heavy[1 ..] (count in heavy[0]) and left out here
 __global__ __launch_bounds__(256) void chamfer_rows(RowSide s0, RowSide s1, int32_t* heavy, int64_t max_heavy) {
-    const int64_t rg = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
-    const bool second = rg >= s0.nrows;  // uniform per 16-lane group
+    const int64_t rg = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kChLanes;
+    const bool second = rg >= s0.nrows;  // uniform per row group
     const RowSide& sd = second ? s1 : s0;
     const int64_t r = second ? rg - s0.nrows : rg;
     const float* X = sd.X;
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(256) void chamfer_rows(RowSide s0, RowSide s1, int3
     const int32_t* col_idx = sd.col_idx;
     const int Nx = sd.Nx, Ny = sd.Ny;
     float* dX = sd.dX;
-    const int l16 = threadIdx.x & 15;
+    const int lr = threadIdx.x % kChLanes;
     const bool ok = r < sd.nrows;
     const int64_t rr = ok ? r : 0;
     // a group past the last row reads nothing (that cloud may be empty)
@@ -453,14 +455,14 @@ __global__ __launch_bounds__(256) void chamfer_rows(RowSide s0, RowSide s1, int3
     float a0 = 0.f, a1 = 0.f, a2 = 0.f;
     const int beg = ok ? row_ptr[rr] : 0, end = ok ? row_ptr[rr + 1] : 0;
     if (end - beg > kChHeavy) {  // uniform per group
-        if (l16 == 0) {
+        if (lr == 0) {
             const int slot = atomicAdd(&heavy[0], 1);
             if (slot < max_heavy) heavy[1 + slot] = (int32_t)rg;
         }
         return;
     }
     if (ok) {
-        for (int e = beg + l16; e < end; e += 16) {
+        for (int e = beg + lr; e < end; e += kChLanes) {
             const int64_t s = col_idx[e];
             const float w = 2.0f * gy[s];
             a0 = __builtin_fmaf(w, x0 - Y[s * 3], a0);
@@ -469,12 +471,12 @@ __global__ __launch_bounds__(256) void chamfer_rows(RowSide s0, RowSide s1, int3
         }
     }
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-        a0 += __shfl_xor(a0, off, 16);
-        a1 += __shfl_xor(a1, off, 16);
-        a2 += __shfl_xor(a2, off, 16);
+    for (int off = kChLanes / 2; off >= 1; off >>= 1) {
+        a0 += __shfl_xor(a0, off, kChLanes);
+        a1 += __shfl_xor(a1, off, kChLanes);
+        a2 += __shfl_xor(a2, off, kChLanes);
     }
-    if (ok && l16 == 0) {
+    if (ok && lr == 0) {
         const int32_t t = idx_x[rr];
         if (t >= 0 && t < Ny) {
             const int64_t b = rr / Nx;
@@ -613,7 +615,7 @@ hipError_t launch_rows_pair(const ChamferArgs& a, hipStream_t stream) {
     const int64_t nrows = sp.nrows + sq.nrows;
     if (nrows == 0) return hipSuccess;
     const int64_t mh = max_heavy_rows(a);
-    hipLaunchKernelGGL(chamfer_rows, dim3((unsigned)((nrows * 16 + 255) / 256)), dim3(256), 0, stream, sp, sq,
+    hipLaunchKernelGGL(chamfer_rows, dim3((unsigned)((nrows * kChLanes + 255) / 256)), dim3(256), 0, stream, sp, sq,
                        heavy_list(a), mh);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || mh == 0) return e;

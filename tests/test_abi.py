@@ -359,7 +359,7 @@ def test_chamfer_workspace_bytes():
     assert L.maxsim_chamfer_fwd_workspace_bytes(1, 10, 20) == 256  # one chunk: no partials
     assert L.maxsim_chamfer_fwd_workspace_bytes(-1, 10, 20) == 0
     # backward: one sort of both clouds' points (keys and values twice plus 256 counters per
-    # 2048-element tile), then the heavy-row list (a count and n // 1025 rows)
+    # 2048-element tile), then the heavy-row list (a count and n // 257 rows)
     n = 10 + 3000
     assert L.maxsim_chamfer_bwd_workspace_bytes(1, 10, 3000) == 4 * ((n * 4 + 255) // 256 * 256) + 2 * 256 * 4 + 256
 
