@@ -42,14 +42,14 @@ struct NnParams {
     int32_t* part_i;
 };
 
-// grid: Bt * tiles * chunks workgroups; chunk-major inside a batch item so
-// that the workgroups sharing a target chunk are launched together.
+// One direction's workgroup blk of Bt * tiles * chunks; chunk-major inside a
+// batch item so that the workgroups sharing a target chunk run together.
 template <int kPts>  // source points per lane
-__global__ __launch_bounds__(kNnThreads) void nn_kernel(NnParams p) {
+__device__ __forceinline__ void nn_tile(const NnParams& p, int blk) {
     constexpr int kSrcTile = kNnThreads * kPts;
     const int per_item = p.tiles * p.chunks;
-    const int b = blockIdx.x / per_item;
-    const int rem = blockIdx.x - b * per_item;
+    const int b = blk / per_item;
+    const int rem = blk - b * per_item;
     const int c = rem / p.tiles;
     const int tile = rem - c * p.tiles;
     const int s0 = tile * kSrcTile + threadIdx.x;  // this lane's first source; then +kNnThreads
@@ -121,22 +121,49 @@ __global__ __launch_bounds__(kNnThreads) void nn_kernel(NnParams p) {
     }
 }
 
+// Both directions in one launch: workgroups 0 .. g0-1 take p0, the rest p1.
+// (The two are independent; together they give the chip twice the resident
+// work when one direction alone fills it poorly.)
+struct NnPair {
+    NnParams d[2];
+    int g0;  // workgroups of d[0]
+};
+template <int kPts>
+__global__ __launch_bounds__(kNnThreads) void nn_kernel(NnPair pp) {
+    // uniform; indexing the pair loads only the chosen direction's parameters
+    // (selecting field by field kept both in scalar registers and pushed the
+    // scalar-loaded targets into vector registers)
+    const int second = (int)blockIdx.x >= pp.g0 ? 1 : 0;
+    const NnParams p = pp.d[second];
+    nn_tile<kPts>(p, (int)blockIdx.x - (second ? pp.g0 : 0));
+}
+
 // Merge of the chunks' minima in ascending chunk order; a strict compare
 // keeps the first index among equal distances.
-__global__ __launch_bounds__(256) void nn_merge(NnParams p) {
+__device__ __forceinline__ void nn_merge_one(const NnParams& p, int64_t s) {
     const int64_t n = (int64_t)p.Bt * p.Na;
-    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (int64_t)gridDim.x * blockDim.x) {
-        float best = p.part_d[s];
-        int arg = p.part_i[s];
-        for (int c = 1; c < p.chunks; ++c) {
-            const float d = p.part_d[(int64_t)c * n + s];
-            if (d < best) {
-                best = d;
-                arg = p.part_i[(int64_t)c * n + s];
-            }
+    float best = p.part_d[s];
+    int arg = p.part_i[s];
+    for (int c = 1; c < p.chunks; ++c) {
+        const float d = p.part_d[(int64_t)c * n + s];
+        if (d < best) {
+            best = d;
+            arg = p.part_i[(int64_t)c * n + s];
         }
-        p.dist[s] = best;
-        p.idx[s] = arg;
+    }
+    p.dist[s] = best;
+    p.idx[s] = arg;
+}
+// elements 0 .. n0-1 of p0, then n1 of p1 (n = 0 for a direction that needs
+// no merge)
+__global__ __launch_bounds__(256) void nn_merge(NnParams p0, int64_t n0, NnParams p1, int64_t n1) {
+    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n0 + n1;
+         s += (int64_t)gridDim.x * blockDim.x) {
+        if (s < n0) {
+            nn_merge_one(p0, s);
+        } else {
+            nn_merge_one(p1, s - n0);
+        }
     }
 }
 
@@ -185,37 +212,44 @@ size_t nn_part_bytes(int Bt, int Na, int Nb) {
     return chunks > 1 ? (size_t)chunks * Bt * Na * 8 : 0;
 }
 
-hipError_t launch_nn(const float* A, const float* B, int Bt, int Na, int Nb, float* dist, int32_t* idx, void* ws,
-                     hipStream_t stream) {
-    if (Bt == 0 || Na == 0) return hipSuccess;
-    if (Nb == 0) {
-        const int64_t n = (int64_t)Bt * Na;
-        hipLaunchKernelGGL(nn_empty, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
-                           stream, dist, idx, n);
-        return hipGetLastError();
-    }
+// One direction's parameters and plan; its chunk minima (when the targets
+// are split) at ws.
+NnParams nn_params(const float* A, const float* B, int Bt, int Na, int Nb, float* dist, int32_t* idx, void* ws,
+                   int* pts) {
     NnParams p{};
     p.A = A;
     p.B = B;
     p.Bt = Bt;
     p.Na = Na;
     p.Nb = Nb;
-    int pts;
-    nn_plan(Bt, Na, Nb, &pts, &p.tiles, &p.chunks, &p.chunk_len);
+    nn_plan(Bt, Na, Nb, pts, &p.tiles, &p.chunks, &p.chunk_len);
     p.dist = dist;
     p.idx = idx;
     const int64_t n = (int64_t)Bt * Na;
     p.part_d = static_cast<float*>(ws);
     p.part_i = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + (size_t)p.chunks * n * 4);
-    const dim3 grid((unsigned)((int64_t)Bt * p.tiles * p.chunks));
+    return p;
+}
+
+hipError_t launch_nn_pair(const NnParams& p0, const NnParams& p1, int pts, hipStream_t stream) {
+    const int g0 = p0.Bt * p0.tiles * p0.chunks, g1 = p1.Bt * p1.tiles * p1.chunks;
+    const dim3 grid((unsigned)(g0 + g1));
+    NnPair pp;
+    pp.d[0] = p0;
+    pp.d[1] = p1;
+    pp.g0 = g0;
     if (pts == 4) {
-        hipLaunchKernelGGL(nn_kernel<4>, grid, dim3(kNnThreads), 0, stream, p);
+        hipLaunchKernelGGL(nn_kernel<4>, grid, dim3(kNnThreads), 0, stream, pp);
     } else {
-        hipLaunchKernelGGL(nn_kernel<8>, grid, dim3(kNnThreads), 0, stream, p);
+        hipLaunchKernelGGL(nn_kernel<8>, grid, dim3(kNnThreads), 0, stream, pp);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.chunks == 1) return e;
-    hipLaunchKernelGGL(nn_merge, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 8192)), dim3(256), 0, stream, p);
+    if (e != hipSuccess) return e;
+    const int64_t n0 = p0.chunks > 1 ? (int64_t)p0.Bt * p0.Na : 0;
+    const int64_t n1 = p1.chunks > 1 ? (int64_t)p1.Bt * p1.Na : 0;
+    if (n0 + n1 == 0) return hipSuccess;
+    hipLaunchKernelGGL(nn_merge, dim3((unsigned)std::min<int64_t>((n0 + n1 + 255) / 256, 8192)), dim3(256), 0, stream,
+                       p0, n0, p1, n1);
     return hipGetLastError();
 }
 
@@ -626,15 +660,35 @@ hipError_t launch_rows_pair(const ChamferArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// both directions' chunk minima, side by side (the directions run together)
 size_t chamfer_fwd_workspace_bytes(int32_t Bt, int32_t N, int32_t M) {
-    return std::max<size_t>(256, std::max(nn_part_bytes(Bt, N, M), nn_part_bytes(Bt, M, N)));
+    return std::max<size_t>(256, align256(nn_part_bytes(Bt, N, M)) + align256(nn_part_bytes(Bt, M, N)));
 }
 
 hipError_t launch_chamfer_fwd(const ChamferArgs& a, hipStream_t stream) {
-    // the two directions share the workspace: stream order keeps them apart
-    hipError_t e = launch_nn(a.P, a.Q, a.Bt, a.N, a.M, a.dist_p, a.idx_p, a.workspace, stream);
+    if (a.Bt == 0 || (a.N == 0 && a.M == 0)) return hipSuccess;
+    if (a.N == 0 || a.M == 0) {  // one cloud empty: the other's points get +inf and -1
+        const int64_t n = (int64_t)a.Bt * (a.N == 0 ? a.M : a.N);
+        hipLaunchKernelGGL(nn_empty, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, stream,
+                           a.N == 0 ? a.dist_q : a.dist_p, a.N == 0 ? a.idx_q : a.idx_p, n);
+        return hipGetLastError();
+    }
+    char* ws = static_cast<char*>(a.workspace);
+    int pts0, pts1;
+    const NnParams p0 = nn_params(a.P, a.Q, a.Bt, a.N, a.M, a.dist_p, a.idx_p, ws, &pts0);
+    const NnParams p1 = nn_params(a.Q, a.P, a.Bt, a.M, a.N, a.dist_q, a.idx_q,
+                                  ws + align256(nn_part_bytes(a.Bt, a.N, a.M)), &pts1);
+    if (pts0 == pts1) return launch_nn_pair(p0, p1, pts0, stream);
+    // different lane plans: one launch per direction (an empty second half)
+    NnParams none = p0;
+    none.chunks = 1;
+    none.tiles = 0;
+    hipError_t e = launch_nn_pair(p0, none, pts0, stream);
     if (e != hipSuccess) return e;
-    return launch_nn(a.Q, a.P, a.Bt, a.M, a.N, a.dist_q, a.idx_q, a.workspace, stream);
+    NnParams none1 = p1;
+    none1.chunks = 1;
+    none1.tiles = 0;
+    return launch_nn_pair(p1, none1, pts1, stream);
 }
 
 }  // namespace maxsim

@@ -354,8 +354,9 @@ def test_chamfer_validation():
 
 
 def test_chamfer_workspace_bytes():
-    # forward: chunk minima (fp32 + int32) when the targets are split; 100K x 100K splits into 83 chunks
-    assert L.maxsim_chamfer_fwd_workspace_bytes(1, 100000, 100000) == 83 * 100000 * 8
+    # forward: chunk minima (fp32 + int32) of both directions side by side when the targets are
+    # split; 100K x 100K splits each direction into 83 chunks
+    assert L.maxsim_chamfer_fwd_workspace_bytes(1, 100000, 100000) == 2 * 83 * 100000 * 8
     assert L.maxsim_chamfer_fwd_workspace_bytes(1, 10, 20) == 256  # one chunk: no partials
     assert L.maxsim_chamfer_fwd_workspace_bytes(-1, 10, 20) == 0
     # backward: one sort of both clouds' points (keys and values twice plus 256 counters per
