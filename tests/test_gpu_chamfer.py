@@ -58,8 +58,10 @@ def check_direction(A, B, dist, idx, where, sample=None):
     return int(diff.sum())
 
 
+# (16, 100, 20000): the P -> Q direction fills the chip with 8 source points
+# per lane and Q -> P takes 4, so the two run as separate launches
 SHAPES = [(1, 1, 1), (1, 50, 70), (3, 33, 17), (2, 200, 5), (2, 3000, 17), (1, 2049, 513), (1, 5000, 4000),
-          (4, 16, 2100), (2, 10, 0), (2, 0, 10)]
+          (4, 16, 2100), (2, 10, 0), (2, 0, 10), (16, 100, 20000)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
