@@ -53,7 +53,11 @@ SHAPES = [(1, 1, 4, (1, 3)), (2, 7, 9, (0, 40)), (3, 32, 20, (32, 512)), (40, 32
           (1, 300, 5, (10, 600)), (2, 1024, 3, (100, 200)),
           # more queries in a slab than threads in the workgroup (single-token queries:
           # the per-query sums wrap around the workgroup), and two slabs of 512 queries
-          (600, 1, 7, (1, 300)), (520, 2, 3, (5, 90))]
+          (600, 1, 7, (1, 300)), (520, 2, 3, (5, 90)),
+          # the thread-per-query sums: 8-row groups at one address (1, 3, 5 and 7 groups)
+          # and, for a length that is no multiple of 8, the row-by-row read-ahead
+          (5, 8, 9, (0, 50)), (3, 24, 7, (10, 200)), (2, 40, 6, (1, 520)), (2, 56, 5, (30, 300)),
+          (4, 20, 11, (1, 300))]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
