@@ -678,8 +678,10 @@ hipError_t launch_chamfer_fwd(const ChamferArgs& a, hipStream_t stream) {
     const NnParams p0 = nn_params(a.P, a.Q, a.Bt, a.N, a.M, a.dist_p, a.idx_p, ws, &pts0);
     const NnParams p1 = nn_params(a.Q, a.P, a.Bt, a.M, a.N, a.dist_q, a.idx_q,
                                   ws + align256(nn_part_bytes(a.Bt, a.N, a.M)), &pts1);
-    if (pts0 == pts1) return launch_nn_pair(p0, p1, pts0, stream);
-    // different lane plans: one launch per direction (an empty second half)
+    const int64_t g0 = (int64_t)p0.Bt * p0.tiles * p0.chunks, g1 = (int64_t)p1.Bt * p1.tiles * p1.chunks;
+    if (pts0 == pts1 && g0 + g1 <= INT32_MAX) return launch_nn_pair(p0, p1, pts0, stream);
+    // different lane plans (or a grid past int range together): one launch per
+    // direction (an empty second half)
     NnParams none = p0;
     none.chunks = 1;
     none.tiles = 0;
